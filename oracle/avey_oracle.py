@@ -1,0 +1,210 @@
+"""CPU oracle for the Avey-B bidirectional ranker and dynamic contextualizer core.
+
+TEST INFRASTRUCTURE ONLY. This module is the plain, slow, float64 statement of what the GPU
+library computes. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the product path (``attention_free_long_amd``) never does, and this
+module imports nothing from it. Inputs are the exact values the GPU sees (bf16 or fp32 upcast
+to float64); every sum is accumulated in float64. Nothing is blocked, fused or reordered
+beyond what the definitions below state: the all-pairs score matrix is computed one ordered
+pair (i, j) at a time, from scratch.
+
+Sources (the pages' own words are restated, never quoted):
+
+* [notes]   papernotes.org, "Avey-B: 把无注意力架构改造成双向编码器" (ICLR2026 note).
+            Section "方法详解 / 整体框架" (ranker: S-token splits with zero padding, MaxSim
+            relevance, top-k, division by the largest selected score, weighting and
+            concatenation with the current split); "关键设计 2" (dynamic layer mixes Z_t with
+            the cosine matrix N(Z_t)N(Z_t)^T); "关键设计 3", eq. 6 (row normalisation
+            S~_ij = S_ij / (sum_j S_ij + eps)); "关键设计 4", eq. 8 (X^ = P X_cat with
+            P in R^{S x (k+1)S}, plus a residual to the current split's own tokens).
+* [summary] paperlayer.ai summary of Avey-B (arXiv 2602.15814v1), section 3 "Background"
+            (splits, MaxSim, top-k, normalise-weight-concatenate), section 4.3 "Neural
+            compression", appendix H (the compressor residual joins the current split's
+            original tokens).
+* MaxSim itself is taken as: for target split i and candidate split j, the sum over the
+  tokens of i of the largest cosine similarity to any token of j.
+
+Readings where the pages are silent (each is listed, with its reason, in the design notes):
+self is never its own candidate; padded tokens are masked (neither a target nor a candidate);
+ties in top-k go to the lower split index; X_cat = [current, rank 1, ..., rank k]; the
+dynamic layer works within each S-token split on valid tokens only, multiplies the
+un-normalised Z_t, and stops at S~ Z_t (no activation, no bias).
+
+Pinned against closed forms, invariants and brute force in ``tests/test_oracle_pins.py``;
+no function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+# ----------------------------------------------------------------------------- splits
+def n_splits(N: int, S: int) -> int:
+    """[notes] 整体框架: N tokens are cut into S-token splits, the last one zero-padded."""
+    return -(-N // S)
+
+
+def split_rows(N: int, S: int, j: int) -> range:
+    """Token positions of split j that hold real tokens (positions >= N are padding)."""
+    return range(j * S, min((j + 1) * S, N))
+
+
+def padded_split(x_b: np.ndarray, S: int, j: int) -> np.ndarray:
+    """Split j of one sequence as S rows, padding rows set to zero ([notes] 整体框架)."""
+    N, d = x_b.shape
+    out = np.zeros((S, d), dtype=np.float64)
+    r = split_rows(N, S, j)
+    out[: len(r)] = x_b[r.start:r.stop]
+    return out
+
+
+# ----------------------------------------------------------------------------- N(.)
+def unit_rows(a: np.ndarray) -> np.ndarray:
+    """N(.): each row divided by its L2 norm; a zero row stays zero ([notes] 关键设计 2)."""
+    a = np.asarray(a, dtype=np.float64)
+    norm = np.sqrt((a * a).sum(axis=-1, keepdims=True))
+    out = np.zeros_like(a)
+    nz = norm[..., 0] > 0
+    out[nz] = a[nz] / norm[nz]
+    return out
+
+
+# ----------------------------------------------------------------------------- ranker
+def maxsim(x_b: np.ndarray, S: int, i: int, j: int) -> float:
+    """MaxSim relevance of candidate split j to target split i ([summary] 3; [notes] 整体框架).
+
+    Sum over the valid tokens t of split i of max over the valid tokens u of split j of
+    cos(x_t, x_u). Padding tokens take part in neither the sum nor the max.
+    """
+    N = x_b.shape[0]
+    ti, tj = split_rows(N, S, i), split_rows(N, S, j)
+    ui = unit_rows(x_b[ti.start:ti.stop])
+    uj = unit_rows(x_b[tj.start:tj.stop])
+    cos = ui @ uj.T                      # [|i|, |j|] cosine similarities
+    return float(cos.max(axis=1).sum())
+
+
+def score_row(x_b: np.ndarray, S: int, i: int) -> np.ndarray:
+    """Scores of every candidate j for target split i; the target itself gets -inf."""
+    n_s = n_splits(x_b.shape[0], S)
+    row = np.empty(n_s, dtype=np.float64)
+    for j in range(n_s):
+        row[j] = NEG_INF if j == i else maxsim(x_b, S, i, j)
+    return row
+
+
+def score_matrix(x: np.ndarray, S: int) -> np.ndarray:
+    """All ordered split pairs: scores[b, i, j] = MaxSim(i <- j), diagonal -inf."""
+    B, N, _ = x.shape
+    n_s = n_splits(N, S)
+    out = np.empty((B, n_s, n_s), dtype=np.float64)
+    for b in range(B):
+        for i in range(n_s):
+            out[b, i] = score_row(x[b], S, i)
+    return out
+
+
+def top_k(row: np.ndarray, i: int, k: int):
+    """Top-k candidates of one target split and their divide-by-max weights.
+
+    [notes] 整体框架 / [summary] 3: keep the k most relevant splits, then divide each selected
+    score by the largest of them. Order: score descending, ties to the lower index; the
+    target itself is never a candidate. Returns (idx[k], w[k], s[k], gap) where gap is the
+    relative distance between the k-th and (k+1)-th scores (inf when there is no (k+1)-th).
+    """
+    cands = sorted((j for j in range(len(row)) if j != i), key=lambda j: (-row[j], j))
+    idx = cands[:k]
+    s = np.array([row[j] for j in idx], dtype=np.float64)
+    w = s / s[0]
+    if len(cands) > k:
+        sk, sk1 = row[cands[k - 1]], row[cands[k]]
+        gap = (sk - sk1) / abs(sk) if sk != 0 else (0.0 if sk1 == sk else math.inf)
+    else:
+        gap = math.inf
+    return np.array(idx, dtype=np.int64), w, s, gap
+
+
+def split_rank(x: np.ndarray, S: int, k: int, rows=None):
+    """Score rows, top-k indices and weights for the listed (b, i) target splits (default: all).
+
+    Returns dict {(b, i): (score_row, idx, w, gap)}.
+    """
+    B, N, _ = x.shape
+    n_s = n_splits(N, S)
+    if rows is None:
+        rows = [(b, i) for b in range(B) for i in range(n_s)]
+    out = {}
+    for b, i in rows:
+        r = score_row(x[b], S, i)
+        idx, w, _, gap = top_k(r, i, k)
+        out[(b, i)] = (r, idx, w, gap)
+    return out
+
+
+# ----------------------------------------------------------------------------- compression
+def compress_split(x_b: np.ndarray, S: int, idx_i, w_i, P: np.ndarray, i: int, residual: bool = True) -> np.ndarray:
+    """X^_i = P X_cat (+ X_i) for target split i, valid rows only.
+
+    [notes] 关键设计 4, eq. 8 and [summary] 4.3: X_cat stacks the current split and its k
+    retrieved splits, each retrieved split scaled by its normalised score ([notes] 整体框架);
+    P (S x (k+1)S) maps the (k+1)S rows back to S. The residual adds the current split's own
+    tokens ([summary] appendix H). Block order: [current, rank 1, ..., rank k].
+    """
+    N = x_b.shape[0]
+    blocks = [padded_split(x_b, S, i)]
+    for j, wj in zip(idx_i, w_i):
+        blocks.append(float(wj) * padded_split(x_b, S, int(j)))
+    x_cat = np.concatenate(blocks, axis=0)            # [(k+1)S, d]
+    xhat = np.asarray(P, dtype=np.float64) @ x_cat     # [S, d]
+    if residual:
+        xhat = xhat + blocks[0]
+    return xhat[: len(split_rows(N, S, i))]
+
+
+def select_compress(x: np.ndarray, S: int, idx: np.ndarray, w: np.ndarray, P: np.ndarray,
+                    residual: bool = True, splits=None):
+    """compress_split over the listed (b, i) splits (default: all). Returns {(b, i): rows}."""
+    B, N, _ = x.shape
+    n_s = n_splits(N, S)
+    if splits is None:
+        splits = [(b, i) for b in range(B) for i in range(n_s)]
+    return {(b, i): compress_split(x[b], S, idx[b, i], w[b, i], P, i, residual) for b, i in splits}
+
+
+# ----------------------------------------------------------------------------- dynamic layer
+def dyn_context_split(z_b: np.ndarray, S: int, eps: float, i: int) -> np.ndarray:
+    """S~ Z_t for one split, valid rows only.
+
+    [notes] 关键设计 2: the dynamic layer forms the cosine matrix N(Z_t) N(Z_t)^T over the
+    tokens of the split and multiplies Z_t by it; 关键设计 3, eq. 6: each row is divided by
+    its own sum plus eps. Within-split, bidirectional (no mask between valid tokens).
+    """
+    N = z_b.shape[0]
+    r = split_rows(N, S, i)
+    zt = np.asarray(z_b[r.start:r.stop], dtype=np.float64)   # [n_valid, m_t]
+    nz = unit_rows(zt)
+    sim = nz @ nz.T                                            # S = N(Z_t) N(Z_t)^T
+    rowsum = sim.sum(axis=1)
+    s_tilde = sim / (rowsum + eps)[:, None]                    # eq. 6
+    return s_tilde @ zt
+
+
+def dyn_context(z: np.ndarray, S: int, eps: float, splits=None):
+    """dyn_context_split over the listed (b, i) splits (default: all). Returns {(b, i): rows}."""
+    B, N, _ = z.shape
+    n_s = n_splits(N, S)
+    if splits is None:
+        splits = [(b, i) for b in range(B) for i in range(n_s)]
+    return {(b, i): dyn_context_split(z[b], S, eps, i) for b, i in splits}
+
+
+def assemble(parts: dict, B: int, N: int, S: int, width: int) -> np.ndarray:
+    """Stack per-split results {(b, i): rows} into a [B, N, width] array (NaN where absent)."""
+    out = np.full((B, N, width), np.nan)
+    for (b, i), rows in parts.items():
+        out[b, i * S: i * S + rows.shape[0]] = rows
+    return out

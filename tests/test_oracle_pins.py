@@ -1,0 +1,353 @@
+"""Pins of the CPU oracle against facts other than itself (CPU only).
+
+Each test is chosen so that a plausible slip in the oracle fails it: the MaxSim direction
+(target sum vs candidate max), missing normalisation, unmasked padding, the top-k order and
+tie rule, the X_cat block order and weighting, the residual, eq. 6's denominator and the
+within-split scope of the dynamic layer.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import avey_oracle as O
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
+
+
+# ----------------------------------------------------------------------------- hand-worked
+def test_hand_worked_maxsim_and_topk():
+    g = GOLD["maxsim"]
+    x = np.array(g["x"], dtype=np.float64)
+    S, k = g["S"], g["k"]
+    sc = O.score_matrix(x[None], S)[0]
+    for i, row in enumerate(g["scores"]):
+        for j, v in enumerate(row):
+            if v is None:
+                assert sc[i, j] == -math.inf
+            else:
+                assert sc[i, j] == pytest.approx(v, abs=1e-14)
+    ranked = O.split_rank(x[None], S, k)
+    for i in range(3):
+        _, idx, w, _ = ranked[(0, i)]
+        assert list(idx) == g["idx"][i]
+        np.testing.assert_allclose(w, g["w"][i], rtol=1e-14)
+
+
+def test_hand_worked_compress():
+    g = GOLD["compress"]
+    x = np.array(g["x"], dtype=np.float64)[None]
+    S = g["S"]
+    for case in g["cases"]:
+        idx = np.array(case["idx"])[None]
+        w = np.array(case["w"])[None]
+        P = np.array(case["P"], dtype=np.float64)
+        parts = O.select_compress(x, S, idx, w, P, residual=case["residual"])
+        if "xhat" in case:
+            got = O.assemble(parts, 1, x.shape[1], S, 2)[0]
+            np.testing.assert_allclose(got, case["xhat"], atol=1e-14)
+        else:
+            np.testing.assert_allclose(parts[(0, case["only_split"])], case["xhat_split0"], atol=1e-14)
+
+
+def test_hand_worked_dyn():
+    g = GOLD["dyn"]
+    z = np.array(g["z"], dtype=np.float64)[None]
+    out = O.dyn_context(z, g["S"], g["eps"])[(0, 0)]
+    np.testing.assert_allclose(out, g["out"], atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- MaxSim
+def _one_hot(codes, d):
+    x = np.zeros((len(codes), d))
+    x[np.arange(len(codes)), codes] = 1.0
+    return x
+
+
+def test_maxsim_one_hot_counts():
+    """One-hot tokens: cosines are 0/1, so MaxSim(i<-j) counts the tokens of i whose code occurs in j."""
+    rng = np.random.default_rng(1)
+    S, d, n_s = 8, 12, 6
+    codes = rng.integers(0, d, size=S * n_s - 3)          # ragged: last split has 5 tokens
+    x = _one_hot(codes, d)
+    sc = O.score_matrix(x[None], S)[0]
+    N = len(codes)
+    for i in range(n_s):
+        ci = codes[i * S: min((i + 1) * S, N)]
+        for j in range(n_s):
+            if i == j:
+                continue
+            cj = set(codes[j * S: min((j + 1) * S, N)].tolist())
+            assert sc[i, j] == sum(1 for c in ci if c in cj)
+    # direction: a target with repeated codes versus a candidate with distinct codes
+    x2 = _one_hot([0, 0, 0, 1, 0, 2, 3, 4], 5)
+    s2 = O.score_matrix(x2[None], 4)[0]
+    assert s2[0, 1] == 3 and s2[1, 0] == 1
+
+
+def test_maxsim_scale_and_permutation_invariance():
+    rng = np.random.default_rng(2)
+    S, d, N = 7, 5, 31
+    x = rng.standard_normal((N, d))
+    base = O.score_matrix(x[None], S)[0]
+    scaled = x * rng.uniform(0.1, 10.0, size=(N, 1))
+    np.testing.assert_allclose(O.score_matrix(scaled[None], S)[0], base, rtol=1e-12)
+    perm = x.copy()
+    for j in range(O.n_splits(N, S)):
+        r = O.split_rows(N, S, j)
+        perm[r.start:r.stop] = x[r.start:r.stop][rng.permutation(len(r))]
+    np.testing.assert_allclose(O.score_matrix(perm[None], S)[0], base, rtol=1e-12)
+
+
+def test_maxsim_duplicate_split_closed_form():
+    rng = np.random.default_rng(3)
+    S, d, n_s = 6, 4, 5
+    x = rng.standard_normal((S * n_s, d))
+    x[4 * S:5 * S] = x[1 * S:2 * S]                      # split 4 is an exact copy of split 1
+    sc = O.score_matrix(x[None], S)[0]
+    assert sc[1, 4] == pytest.approx(S, abs=1e-12) and sc[4, 1] == pytest.approx(S, abs=1e-12)
+    for i in (0, 2, 3):
+        assert sc[i, 1] == sc[i, 4]                      # identical computation -> identical bits
+    # no other candidate can beat a copy: each term is at most 1
+    assert np.all(sc[1][[0, 2, 3]] <= S + 1e-12)
+
+
+def test_maxsim_padding_is_masked():
+    """A padded candidate whose valid tokens are all anti-parallel gives -(#target tokens).
+
+    Were the zero padding rows candidates (cosine 0), every term would be 0 instead.
+    """
+    d, S = 3, 4
+    tgt = np.tile([1.0, 0.0, 0.0], (S, 1))
+    cand = np.array([[-2.0, 0.0, 0.0]])                  # one valid token, three padding slots
+    x = np.concatenate([tgt, cand])
+    sc = O.score_matrix(x[None], S)[0]
+    assert sc[0, 1] == pytest.approx(-4.0, abs=1e-15)
+    assert sc[1, 0] == pytest.approx(-1.0, abs=1e-15)    # only the one valid target token counts
+    # Appending rows after N changes nothing: they are never part of any split's valid tokens.
+    more = np.concatenate([x, np.full((2, d), 7.0)])
+    sc2 = O.score_matrix(more[None, :5], S)[0]
+    np.testing.assert_array_equal(sc2, sc)
+
+
+def test_maxsim_brute_force_tiny():
+    """Scalar loops with math.sqrt, per token pair, on many random tiny shapes."""
+    rng = np.random.default_rng(4)
+    for trial in range(40):
+        S = int(rng.integers(1, 6))
+        d = int(rng.integers(1, 6))
+        N = int(rng.integers(S + 1, 4 * S + 2))
+        x = rng.standard_normal((N, d))
+        if trial % 5 == 0:
+            x[rng.integers(0, N)] = 0.0                  # a zero token: cosine 0 with everything
+        sc = O.score_matrix(x[None], S)[0]
+        n_s = -(-N // S)
+        for i in range(n_s):
+            for j in range(n_s):
+                if i == j:
+                    continue
+                total = 0.0
+                for t in range(i * S, min(i * S + S, N)):
+                    best = -math.inf
+                    for u in range(j * S, min(j * S + S, N)):
+                        dot = sum(x[t, c] * x[u, c] for c in range(d))
+                        nt = math.sqrt(sum(x[t, c] ** 2 for c in range(d)))
+                        nu = math.sqrt(sum(x[u, c] ** 2 for c in range(d)))
+                        cos = 0.0 if nt == 0 or nu == 0 else dot / (nt * nu)
+                        best = max(best, cos)
+                    total += best
+                assert sc[i, j] == pytest.approx(total, abs=1e-12)
+
+
+# ----------------------------------------------------------------------------- top-k
+def test_topk_worked_ties():
+    row = np.array([5.0, 3.0, 3.0, 9.0, -math.inf])
+    idx, w, s, gap = O.top_k(row, 4, 3)
+    assert list(idx) == [3, 0, 1]                        # tie 3.0 at j=1 and j=2 -> lower index
+    assert w[0] == 1.0 and w[1] == 5.0 / 9.0 and w[2] == 3.0 / 9.0
+    assert gap == 0.0                                    # k-th and (k+1)-th are tied
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_topk_invariants(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 40))
+    i = int(rng.integers(0, n))
+    k = int(rng.integers(1, n))
+    row = rng.integers(1, 6, size=n).astype(np.float64) * rng.choice([1.0, 0.5])  # many ties
+    row[i] = -math.inf
+    idx, w, s, _ = O.top_k(row, i, k)
+    assert len(set(idx.tolist())) == k and i not in idx and all(0 <= j < n for j in idx)
+    assert w[0] == 1.0
+    assert np.all(np.diff(s) <= 0) and np.all((w > 0) & (w <= 1))
+    kth = s[-1]
+    for j in range(n):
+        if j == i or j in idx:
+            continue
+        assert row[j] < kth or (row[j] == kth and j > max(jj for jj in idx if row[jj] == kth))
+    for a, b in zip(idx[:-1], idx[1:]):
+        assert row[a] > row[b] or (row[a] == row[b] and a < b)
+
+
+# ----------------------------------------------------------------------------- compression
+def _rand_setup(rng, S=4, d=3, n_s=5, N=None, k=2):
+    N = N or S * n_s
+    x = rng.standard_normal((1, N, d))
+    n_s = -(-N // S)
+    idx = np.stack([rng.permutation([j for j in range(n_s) if j != i])[:k] for i in range(n_s)])[None]
+    w = rng.uniform(0.2, 1.0, size=(1, n_s, k))
+    w[..., 0] = 1.0
+    return x, idx, w, N, n_s
+
+
+def test_compress_block_order_and_weights():
+    rng = np.random.default_rng(5)
+    S, d, k = 4, 3, 2
+    x, idx, w, N, n_s = _rand_setup(rng, S, d, 6, N=22, k=k)   # last split has 2 valid tokens
+    eye = np.eye(S)
+    for r in range(k + 1):
+        P = np.zeros((S, (k + 1) * S))
+        P[:, r * S:(r + 1) * S] = eye
+        got = O.select_compress(x, S, idx, w, P, residual=False)
+        for i in range(n_s):
+            n_i = len(O.split_rows(N, S, i))
+            src = i if r == 0 else int(idx[0, i, r - 1])
+            scale = 1.0 if r == 0 else w[0, i, r - 1]
+            want = scale * O.padded_split(x[0], S, src)[:n_i]
+            np.testing.assert_allclose(got[(0, i)], want, atol=1e-15)
+    # residual adds exactly the current split's own tokens
+    P = rng.standard_normal((S, (k + 1) * S))
+    a = O.select_compress(x, S, idx, w, P, residual=True)
+    b = O.select_compress(x, S, idx, w, P, residual=False)
+    for i in range(n_s):
+        r_ = O.split_rows(N, S, i)
+        np.testing.assert_allclose(a[(0, i)] - b[(0, i)], x[0, r_.start:r_.stop], atol=1e-12)
+
+
+def test_compress_padding_rows_are_zero_and_linear_in_P():
+    rng = np.random.default_rng(6)
+    S, d, k = 4, 3, 1
+    x, idx, w, N, n_s = _rand_setup(rng, S, d, 5, N=17, k=k)   # split 4 holds one token
+    last = n_s - 1
+    idx[0, 0, 0] = last
+    P = np.zeros((S, 2 * S))
+    P[:, S:] = np.eye(S)                                  # output = w * (retrieved split)
+    out = O.select_compress(x, S, idx, w, P, residual=False)[(0, 0)]
+    np.testing.assert_allclose(out[0], w[0, 0, 0] * x[0, 16], atol=1e-15)
+    assert np.all(out[1:] == 0.0)                         # padding slots of the retrieved split
+    P1, P2 = rng.standard_normal((2, S, 2 * S))
+    o1 = O.select_compress(x, S, idx, w, P1, residual=False)
+    o2 = O.select_compress(x, S, idx, w, P2, residual=False)
+    o3 = O.select_compress(x, S, idx, w, 2.0 * P1 - 3.0 * P2, residual=False)
+    for key in o1:
+        np.testing.assert_allclose(o3[key], 2.0 * o1[key] - 3.0 * o2[key], atol=1e-12)
+
+
+def test_compress_brute_force_tiny():
+    rng = np.random.default_rng(7)
+    S, d, k = 3, 2, 2
+    x, idx, w, N, n_s = _rand_setup(rng, S, d, 4, N=11, k=k)
+    P = rng.standard_normal((S, (k + 1) * S))
+    got = O.select_compress(x, S, idx, w, P, residual=True)
+    for i in range(n_s):
+        for s in range(len(O.split_rows(N, S, i))):
+            for f in range(d):
+                acc = 0.0
+                for blk in range(k + 1):
+                    src = i if blk == 0 else int(idx[0, i, blk - 1])
+                    wt = 1.0 if blk == 0 else w[0, i, blk - 1]
+                    for slot in range(S):
+                        t = src * S + slot
+                        if t < N:
+                            acc += P[s, blk * S + slot] * wt * x[0, t, f]
+                acc += x[0, i * S + s, f]
+                assert got[(0, i)][s, f] == pytest.approx(acc, abs=1e-12)
+
+
+# ----------------------------------------------------------------------------- dynamic layer
+def test_dyn_constant_and_orthogonal_splits():
+    eps = 1e-3                                           # large enough to see in the closed forms
+    S, m = 5, 4
+    z = np.tile(np.array([0.5, 2.0, 0.0, 1.0]), (S, 1))[None]
+    out = O.dyn_context(z, S, eps)[(0, 0)]
+    np.testing.assert_allclose(out, S * z[0] / (S + eps), rtol=1e-14)
+    z2 = (np.eye(4) * np.array([3.0, 1.0, 2.0, 5.0]))[None]   # orthogonal tokens -> S~ = I/(1+eps)
+    out2 = O.dyn_context(z2, 4, eps)[(0, 0)]
+    np.testing.assert_allclose(out2, z2[0] / (1 + eps), rtol=1e-14)
+
+
+def test_dyn_two_token_closed_form_and_padding():
+    eps = 1e-8
+    rng = np.random.default_rng(8)
+    z1, z2 = rng.uniform(0, 1, size=(2, 6))
+    c = z1 @ z2 / (np.linalg.norm(z1) * np.linalg.norm(z2))
+    # split 0 = {z1, z2}; split 1 = {z1} alone (N=3, S=2: one padding slot)
+    z = np.stack([z1, z2, z1])[None]
+    res = O.dyn_context(z, 2, eps)
+    np.testing.assert_allclose(res[(0, 0)][0], (z1 + c * z2) / (1 + c + eps), rtol=1e-13)
+    np.testing.assert_allclose(res[(0, 0)][1], (c * z1 + z2) / (1 + c + eps), rtol=1e-13)
+    assert res[(0, 1)].shape == (1, 6)
+    np.testing.assert_allclose(res[(0, 1)][0], z1 / (1 + eps), rtol=1e-14)
+
+
+def test_dyn_row_stochastic_bounds_scaling_and_scope():
+    rng = np.random.default_rng(9)
+    S, m, N = 8, 5, 29
+    z = np.maximum(rng.standard_normal((1, N, m)), 0) ** 2
+    res = O.dyn_context(z, S, 1e-8)
+    for (b, i), out in res.items():
+        r = O.split_rows(N, S, i)
+        zi = z[0, r.start:r.stop]
+        assert np.all(out >= -1e-15) and np.all(out <= zi.max(axis=0) + 1e-12)   # sub-convex mix
+    res2 = O.dyn_context(3.5 * z, S, 1e-8)
+    for key in res:
+        np.testing.assert_allclose(res2[key], 3.5 * res[key], rtol=1e-9)
+    # only tokens of the same split mix: changing split 2 leaves split 0 unchanged
+    z3 = z.copy()
+    z3[0, 2 * S:3 * S] += 1.0
+    np.testing.assert_array_equal(O.dyn_context(z3, S, 1e-8)[(0, 0)], res[(0, 0)])
+
+
+def test_dyn_monotonic_in_similarity():
+    """[summary] appendix A: raising one token's similarity to the target weakly raises its
+    normalised weight and weakly lowers the others. Moving z_q toward z_p raises G_pq only."""
+    rng = np.random.default_rng(10)
+    m = 6
+    zp = rng.uniform(0.1, 1, m)
+    others = rng.uniform(0.1, 1, (3, m))
+    def weights(zq):
+        zs = np.vstack([zp, zq, others])
+        n = O.unit_rows(zs)
+        g = n @ n.T
+        return g[0] / (g[0].sum() + 1e-8)
+    zq0 = rng.uniform(0.1, 1, m)
+    w0 = weights(zq0)
+    w1 = weights(0.5 * zq0 + 0.5 * zp / np.linalg.norm(zp) * np.linalg.norm(zq0))
+    assert w1[1] > w0[1] and np.all(w1[[0, 2, 3, 4]] <= w0[[0, 2, 3, 4]] + 1e-15)
+    # and the oracle's output equals the explicit weighted sum with these weights
+    zs = np.vstack([zp, zq0, others])
+    out = O.dyn_context(zs[None], 5, 1e-8)[(0, 0)]
+    np.testing.assert_allclose(out[0], w0 @ zs, rtol=1e-13)
+
+
+def test_dyn_brute_force_tiny():
+    rng = np.random.default_rng(11)
+    S, m, N, eps = 3, 4, 8, 1e-8
+    z = np.maximum(rng.standard_normal((1, N, m)), 0)
+    z[0, 4] = 0.0                                         # zero token: no similarity to anything
+    res = O.dyn_context(z, S, eps)
+    for i in range(-(-N // S)):
+        toks = list(range(i * S, min(i * S + S, N)))
+        for a, p in enumerate(toks):
+            np_ = math.sqrt(sum(v * v for v in z[0, p]))
+            g = []
+            for q in toks:
+                nq = math.sqrt(sum(v * v for v in z[0, q]))
+                dot = sum(z[0, p, c] * z[0, q, c] for c in range(m))
+                g.append(0.0 if np_ == 0 or nq == 0 else dot / (np_ * nq))
+            den = sum(g) + eps
+            for c in range(m):
+                want = sum(g[bq] * z[0, q, c] for bq, q in enumerate(toks)) / den
+                assert res[(0, i)][a, c] == pytest.approx(want, abs=1e-12)
