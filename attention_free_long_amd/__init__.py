@@ -1,0 +1,190 @@
+"""Avey-B bidirectional ranker and dynamic contextualizer core on MI355X (gfx950).
+
+Thin ctypes binding over libavey.so (see include/avey.h): argument marshalling only, every step
+runs in the library's HIP kernels. torch supplies device memory and the current stream.
+
+    scores, idx, w = avey_split_rank(x, S, k)
+    xhat = avey_select_compress(x, idx, w, P, S, residual=True)
+    out = avey_dyn_context(z_tail, S, eps)
+
+Tensors are [B, N, width] with unit stride along width and any row stride (ld); bf16 or fp32.
+There is no fallback: if libavey.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libavey.so")
+
+AVEY_F32, AVEY_BF16 = 0, 1
+AVEY_ABI_VERSION = 1
+
+EXPORTS = (
+    "avey_abi_version",
+    "avey_status_str",
+    "avey_maxsim_scores",
+    "avey_topk_norm",
+    "avey_split_rank",
+    "avey_select_compress",
+    "avey_dyn_context",
+)
+
+
+class AveyError(RuntimeError):
+    """A libavey call returned a non-zero status (or the library could not be loaded)."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libavey.so once and declare the C signatures. Raises AveyError if it is missing."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise AveyError("load_library", -100, f"{path} not found; build it with `python -m attention_free_long_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    lib.avey_abi_version.restype = i32
+    lib.avey_abi_version.argtypes = []
+    lib.avey_status_str.restype = ctypes.c_char_p
+    lib.avey_status_str.argtypes = [i32]
+    lib.avey_maxsim_scores.restype = i32
+    lib.avey_maxsim_scores.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp]
+    lib.avey_topk_norm.restype = i32
+    lib.avey_topk_norm.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.avey_split_rank.restype = i32
+    lib.avey_split_rank.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.avey_select_compress.restype = i32
+    lib.avey_select_compress.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, i64, vp]
+    lib.avey_dyn_context.restype = i32
+    lib.avey_dyn_context.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, vp, i64, vp]
+    ver = lib.avey_abi_version()
+    if ver != AVEY_ABI_VERSION:
+        raise AveyError("load_library", -101, f"ABI version {ver}, expected {AVEY_ABI_VERSION}")
+    _lib_handle = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise AveyError(fn, status, load_library().avey_status_str(status).decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return AVEY_BF16
+    if t.dtype == torch.float32:
+        return AVEY_F32
+    raise AveyError("dtype", -3, f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _rows(t, name: str):
+    """(B, N, width, ld) of a [B, N, width] tensor with unit inner stride and batch stride N*ld."""
+    if t.dim() != 3:
+        raise AveyError(name, -2, f"{name} must be [B, N, width], got {tuple(t.shape)}")
+    B, N, w = t.shape
+    if not t.is_cuda:
+        raise AveyError(name, -1, f"{name} must be a device tensor")
+    if w > 0 and t.stride(2) != 1:
+        raise AveyError(name, -2, f"{name} must have unit stride along its last axis")
+    ld = t.stride(1) if N > 1 else max(w, t.stride(1))
+    if B > 1 and N > 0 and t.stride(0) != N * ld:
+        raise AveyError(name, -2, f"{name} batch stride must be N * row stride")
+    return B, N, w, ld
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def n_splits(N: int, S: int) -> int:
+    return -(-N // S)
+
+
+def avey_maxsim_scores(x, S: int, scores=None):
+    """All-pairs MaxSim scores [B, n_s, n_s] (fp32, diagonal -inf) of x [B, N, d]."""
+    import torch
+    B, N, d, ld = _rows(x, "x")
+    n_s = n_splits(N, S)
+    if scores is None:
+        scores = torch.empty((B, n_s, n_s), device=x.device, dtype=torch.float32)
+    _check("avey_maxsim_scores", load_library().avey_maxsim_scores(
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, scores.data_ptr(), _stream(x)))
+    return scores
+
+
+def avey_topk_norm(scores, k: int, idx=None, w=None):
+    """Top-k indices [B, n_s, k] (int32) and divide-by-max weights (fp32) of a score matrix."""
+    import torch
+    B, n_s, _ = scores.shape
+    if idx is None:
+        idx = torch.empty((B, n_s, k), device=scores.device, dtype=torch.int32)
+    if w is None:
+        w = torch.empty((B, n_s, k), device=scores.device, dtype=torch.float32)
+    _check("avey_topk_norm", load_library().avey_topk_norm(
+        scores.data_ptr(), B, n_s, k, idx.data_ptr(), w.data_ptr(), _stream(scores)))
+    return idx, w
+
+
+def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None):
+    """(scores, idx, w) of the bidirectional ranker for x [B, N, d]."""
+    import torch
+    B, N, d, ld = _rows(x, "x")
+    n_s = n_splits(N, S)
+    dev = x.device
+    if scores is None:
+        scores = torch.empty((B, n_s, n_s), device=dev, dtype=torch.float32)
+    if idx is None:
+        idx = torch.empty((B, n_s, k), device=dev, dtype=torch.int32)
+    if w is None:
+        w = torch.empty((B, n_s, k), device=dev, dtype=torch.float32)
+    _check("avey_split_rank", load_library().avey_split_rank(
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, scores.data_ptr(), idx.data_ptr(), w.data_ptr(),
+        _stream(x)))
+    return scores, idx, w
+
+
+def avey_select_compress(x, idx, w, P, S: int, residual: bool = True, out=None):
+    """Xhat [B, N, d] = P X_cat (+ X_i) per split, X_cat gathered through idx and weighted by w."""
+    import torch
+    B, N, d, ld = _rows(x, "x")
+    k = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, N, d), device=x.device, dtype=x.dtype)
+    _, _, _, ld_out = _rows(out, "out")
+    if P.dtype != x.dtype or out.dtype != x.dtype:
+        raise AveyError("avey_select_compress", -3, "x, P and out must share one dtype")
+    if idx.dtype != torch.int32 or w.dtype != torch.float32:
+        raise AveyError("avey_select_compress", -3, "idx must be int32 and w float32")
+    if not (idx.is_contiguous() and w.is_contiguous() and P.is_contiguous()):
+        raise AveyError("avey_select_compress", -2, "idx, w and P must be contiguous")
+    if tuple(P.shape) != (S, (k + 1) * S):
+        raise AveyError("avey_select_compress", -2, f"P must be [S, (k+1)S] = [{S}, {(k + 1) * S}]")
+    _check("avey_select_compress", load_library().avey_select_compress(
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, idx.data_ptr(), w.data_ptr(), P.data_ptr(),
+        1 if residual else 0, out.data_ptr(), ld_out, _stream(x)))
+    return out
+
+
+def avey_dyn_context(z_tail, S: int, eps: float, out=None):
+    """S~ Z_t per split for z_tail [B, N, m_t] (may be a column slice of Z with row stride m)."""
+    import torch
+    B, N, m_t, ld = _rows(z_tail, "z_tail")
+    if out is None:
+        out = torch.empty((B, N, m_t), device=z_tail.device, dtype=z_tail.dtype)
+    if out.dtype != z_tail.dtype:
+        raise AveyError("avey_dyn_context", -3, "out must have the dtype of z_tail")
+    _, _, _, ld_out = _rows(out, "out")
+    _check("avey_dyn_context", load_library().avey_dyn_context(
+        z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, float(eps), out.data_ptr(), ld_out,
+        _stream(z_tail)))
+    return out

@@ -1,0 +1,165 @@
+// C ABI of libavey.so: argument checks and kernel launches. See include/avey.h for the contract.
+#include "avey.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+using namespace avey;
+
+namespace {
+
+constexpr int64_t kMaxS = 512;
+constexpr int64_t kI32 = 0x7fffffffLL;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t splits(int64_t N, int64_t S) { return (N + S - 1) / S; }
+
+avey_status hip_status(hipError_t e) { return e == hipSuccess ? AVEY_OK : AVEY_ERR_HIP; }
+
+// Checks common to the three tensor entry points. Returns AVEY_OK with *empty set when there is
+// nothing to do.
+avey_status check_common(avey_dtype dt, int64_t B, int64_t N, int32_t S, bool* empty) {
+  if (dt != AVEY_F32 && dt != AVEY_BF16) return AVEY_ERR_DTYPE;
+  if (B < 0 || N < 0 || S < 1 || S > kMaxS) return AVEY_ERR_SHAPE;
+  *empty = (B == 0 || N == 0);
+  return AVEY_OK;
+}
+
+// A [B, N, width] operand with row stride ld.
+avey_status check_tensor(const void* p, avey_dtype dt, int64_t N, int64_t width, int64_t ld) {
+  if (!p) return AVEY_ERR_NULL;
+  if (width < 1 || ld < width) return AVEY_ERR_SHAPE;
+  if (dt == AVEY_BF16) {
+    if (width % 64) return AVEY_ERR_UNSUPPORTED;
+    if (ld % 8 || !aligned(p, 16)) return AVEY_ERR_ALIGN;
+    if (N * ld >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // byte offsets within a sequence stay < 2^31
+  } else {
+    if (!aligned(p, 4)) return AVEY_ERR_ALIGN;
+  }
+  return AVEY_OK;
+}
+
+avey_status check_split_bf16(avey_dtype dt, int32_t S) {
+  return (dt == AVEY_BF16 && S % 64) ? AVEY_ERR_UNSUPPORTED : AVEY_OK;
+}
+
+#define AVEY_TRY(expr)                      \
+  do {                                      \
+    const avey_status s_ = (expr);          \
+    if (s_ != AVEY_OK) return s_;           \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t avey_abi_version(void) { return AVEY_ABI_VERSION; }
+
+const char* avey_status_str(int32_t s) {
+  switch (s) {
+    case AVEY_OK: return "AVEY_OK: success";
+    case AVEY_ERR_NULL: return "AVEY_ERR_NULL: a required pointer is NULL";
+    case AVEY_ERR_SHAPE: return "AVEY_ERR_SHAPE: a size or leading dimension is out of range";
+    case AVEY_ERR_DTYPE: return "AVEY_ERR_DTYPE: unknown dtype";
+    case AVEY_ERR_ALIGN: return "AVEY_ERR_ALIGN: a pointer or leading dimension is misaligned";
+    case AVEY_ERR_UNSUPPORTED: return "AVEY_ERR_UNSUPPORTED: shape not implemented for this dtype";
+    case AVEY_ERR_HIP: return "AVEY_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown avey status";
+  }
+}
+
+avey_status avey_maxsim_scores(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
+                               int32_t S, float* scores, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_common(dt, B, N, S, &empty));
+  if (empty) return AVEY_OK;
+  if (!scores) return AVEY_ERR_NULL;
+  AVEY_TRY(check_tensor(x, dt, N, d, ld_x));
+  const int64_t n_s = splits(N, S);
+  if (n_s < 2) return AVEY_ERR_SHAPE;
+  if (!aligned(scores, 4)) return AVEY_ERR_ALIGN;
+  AVEY_TRY(check_split_bf16(dt, S));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dt == AVEY_BF16) {
+    if (B * (n_s * (n_s - 1) / 2) > kI32) return AVEY_ERR_UNSUPPORTED;
+    return hip_status(launch_maxsim_bf16(static_cast<const uint16_t*>(x), B, N, (int)d, ld_x, S, scores, st));
+  }
+  if (B * n_s * n_s > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_maxsim_f32(static_cast<const float*>(x), B, N, (int)d, ld_x, S, scores, st));
+}
+
+avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t k, int32_t* idx, float* w,
+                           void* stream) {
+  if (B < 0 || n_s < 0) return AVEY_ERR_SHAPE;
+  if (B == 0 || n_s == 0) return AVEY_OK;
+  if (!scores || !idx || !w) return AVEY_ERR_NULL;
+  if (n_s < 2 || k < 1 || k > n_s - 1 || n_s > kI32) return AVEY_ERR_SHAPE;
+  if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
+  if ((B * n_s + 3) / 4 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_topk_norm(scores, B, n_s, k, idx, w, reinterpret_cast<hipStream_t>(stream)));
+}
+
+avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
+                            int32_t k, float* scores, int32_t* idx, float* w, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_common(dt, B, N, S, &empty));
+  if (empty) return AVEY_OK;
+  if (!idx || !w) return AVEY_ERR_NULL;
+  const int64_t n_s = splits(N, S);
+  if (k < 1 || k > n_s - 1) return AVEY_ERR_SHAPE;
+  if (!aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
+  AVEY_TRY(avey_maxsim_scores(x, dt, B, N, d, ld_x, S, scores, stream));
+  return avey_topk_norm(scores, B, n_s, k, idx, w, stream);
+}
+
+avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
+                                 int32_t S, int32_t k, const int32_t* idx, const float* w, const void* P,
+                                 int32_t residual, void* xhat, int64_t ld_out, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_common(dt, B, N, S, &empty));
+  if (empty) return AVEY_OK;
+  if (!idx || !w || !P) return AVEY_ERR_NULL;
+  AVEY_TRY(check_tensor(x, dt, N, d, ld_x));
+  AVEY_TRY(check_tensor(xhat, dt, N, d, ld_out));
+  if (k < 1 || (residual != 0 && residual != 1)) return AVEY_ERR_SHAPE;
+  if (!aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
+  if ((int64_t)S * (k + 1) * S >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // P byte offsets < 2^31
+  AVEY_TRY(check_split_bf16(dt, S));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dt == AVEY_BF16) {
+    if (!aligned(P, 16)) return AVEY_ERR_ALIGN;
+    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * ((d + 255) / 256);
+    if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
+    return hip_status(launch_compress_bf16(static_cast<const uint16_t*>(x), B, N, (int)d, ld_x, S, k, idx, w,
+                                           static_cast<const uint16_t*>(P), residual, static_cast<uint16_t*>(xhat),
+                                           ld_out, st));
+  }
+  if (!aligned(P, 4)) return AVEY_ERR_ALIGN;
+  if ((B * N * d + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_compress_f32(static_cast<const float*>(x), B, N, (int)d, ld_x, S, k, idx, w,
+                                        static_cast<const float*>(P), residual, static_cast<float*>(xhat), ld_out, st));
+}
+
+avey_status avey_dyn_context(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t, int64_t ld_z,
+                             int32_t S, float eps, void* out, int64_t ld_out, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_common(dt, B, N, S, &empty));
+  if (empty) return AVEY_OK;
+  AVEY_TRY(check_tensor(z_tail, dt, N, m_t, ld_z));
+  AVEY_TRY(check_tensor(out, dt, N, m_t, ld_out));
+  AVEY_TRY(check_split_bf16(dt, S));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dt == AVEY_BF16) {
+    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * (S > 256 ? 2 : 1);
+    if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
+    return hip_status(launch_dyn_bf16(static_cast<const uint16_t*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
+                                      static_cast<uint16_t*>(out), ld_out, st));
+  }
+  if (B * N > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_dyn_f32(static_cast<const float*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
+                                   static_cast<float*>(out), ld_out, st));
+}
+
+}  // extern "C"

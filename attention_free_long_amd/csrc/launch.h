@@ -1,0 +1,27 @@
+// Internal launchers (not exported). Argument checks happen in abi.hip before any of these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace avey {
+
+hipError_t launch_maxsim_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, float* scores,
+                              hipStream_t stream);
+hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, int32_t* idx, float* w,
+                            hipStream_t stream);
+hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
+                                const int32_t* idx, const float* w, const uint16_t* P, int residual, uint16_t* xhat,
+                                int64_t ld_out, hipStream_t stream);
+hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps,
+                           uint16_t* out, int64_t ld_out, hipStream_t stream);
+
+hipError_t launch_maxsim_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, float* scores,
+                             hipStream_t stream);
+hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
+                               const int32_t* idx, const float* w, const float* P, int residual, float* xhat,
+                               int64_t ld_out, hipStream_t stream);
+hipError_t launch_dyn_f32(const float* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps, float* out,
+                          int64_t ld_out, hipStream_t stream);
+
+}  // namespace avey

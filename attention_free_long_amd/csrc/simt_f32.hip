@@ -1,0 +1,153 @@
+// fp32 path: plain SIMT kernels with fp32 arithmetic for all three steps.
+//
+// These serve fp32 inputs (the 1000-token, d = 64 parity workload); they favour a direct
+// reading of the definitions over speed. Same definitions as the bf16 kernels: MaxSim over
+// valid tokens (paperlayer.ai "Avey-B" summary, section 3), X^ = P X_cat + X_i
+// (papernotes.org Avey-B note, 关键设计 4, eq. 8), S~ Z_t with eq. 6 (关键设计 2 and 3).
+#include "avey_common.h"
+#include "launch.h"
+
+namespace avey {
+
+namespace {
+
+__device__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__device__ float norm_f32(const float* __restrict__ v, int n) {
+  float s = 0.f;
+  for (int c = 0; c < n; ++c) s = fmaf(v[c], v[c], s);
+  return sqrtf(s);
+}
+
+// One workgroup per ordered pair (b, i, j).
+__global__ void __launch_bounds__(256) maxsim_f32_kernel(const float* __restrict__ x, int64_t N, int d,
+                                                          int64_t ld_x, int S, int n_s, float* __restrict__ scores) {
+  __shared__ float red[4];
+  const int64_t pr = blockIdx.x;
+  const int j = (int)(pr % n_s);
+  const int i = (int)((pr / n_s) % n_s);
+  const int64_t b = pr / ((int64_t)n_s * n_s);
+  float* out = scores + pr;
+  if (i == j) {
+    if (threadIdx.x == 0) *out = -INFINITY;
+    return;
+  }
+  const float* xb = x + b * N * ld_x;
+  const int64_t ti0 = (int64_t)i * S, tj0 = (int64_t)j * S;
+  const int ni = (int)min((int64_t)S, N - ti0), nj = (int)min((int64_t)S, N - tj0);
+  float part = 0.f;
+  for (int t = threadIdx.x; t < ni; t += 256) {
+    const float* xt = xb + (ti0 + t) * ld_x;
+    const float nt = norm_f32(xt, d);
+    float best = -INFINITY;
+    for (int u = 0; u < nj; ++u) {
+      const float* xu = xb + (tj0 + u) * ld_x;
+      const float nu = norm_f32(xu, d);
+      float dot = 0.f;
+      for (int c = 0; c < d; ++c) dot = fmaf(xt[c], xu[c], dot);
+      const float cs = (nt > 0.f && nu > 0.f) ? dot / (nt * nu) : 0.f;
+      best = fmaxf(best, cs);
+    }
+    part += best;
+  }
+  const float tot = block_sum(part, red);
+  if (threadIdx.x == 0) *out = tot;
+}
+
+// One thread per output element (b, token, feature).
+__global__ void __launch_bounds__(256) compress_f32_kernel(const float* __restrict__ x, int64_t B, int64_t N, int d,
+                                                            int64_t ld_x, int S, int k, int n_s,
+                                                            const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                            const float* __restrict__ P, int residual,
+                                                            float* __restrict__ xhat, int64_t ld_out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= B * N * d) return;
+  const int f = (int)(e % d);
+  const int64_t bt = e / d;
+  const int64_t t = bt % N, b = bt / N;
+  const int i = (int)(t / S), s = (int)(t % S);
+  const float* xb = x + b * N * ld_x;
+  const int KP = (k + 1) * S;
+  const float* prow = P + (int64_t)s * KP;
+  float acc = 0.f;
+  for (int blk = 0; blk <= k; ++blk) {
+    int src = blk ? idx[(b * n_s + i) * k + blk - 1] : i;
+    src = min(max(src, 0), n_s - 1);
+    const float wt = blk ? w[(b * n_s + i) * k + blk - 1] : 1.f;
+    for (int slot = 0; slot < S; ++slot) {
+      const int64_t tok = (int64_t)src * S + slot;
+      if (tok >= N) break;
+      acc = fmaf(prow[blk * S + slot], wt * xb[tok * ld_x + f], acc);
+    }
+  }
+  if (residual) acc += xb[t * ld_x + f];
+  xhat[(b * N + t) * ld_out + f] = acc;
+}
+
+// One workgroup per (b, token p): cosine row G_p., its sum, then the mixed output row.
+__global__ void __launch_bounds__(256) dyn_f32_kernel(const float* __restrict__ z, int64_t N, int m_t, int64_t ld_z,
+                                                       int S, float eps, float* __restrict__ out, int64_t ld_out) {
+  __shared__ float g[512];
+  __shared__ float red[4];
+  const int64_t bt = blockIdx.x;
+  const int64_t t = bt % N, b = bt / N;
+  const int64_t base = (t / S) * S;
+  const int nv = (int)min((int64_t)S, N - base);
+  const float* zb = z + b * N * ld_z;
+  const float* zp = zb + t * ld_z;
+  const float np_ = norm_f32(zp, m_t);
+  float part = 0.f;
+  for (int q = threadIdx.x; q < nv; q += 256) {
+    const float* zq = zb + (base + q) * ld_z;
+    const float nq = norm_f32(zq, m_t);
+    float dot = 0.f;
+    for (int c = 0; c < m_t; ++c) dot = fmaf(zp[c], zq[c], dot);
+    const float gq = (np_ > 0.f && nq > 0.f) ? dot / (np_ * nq) : 0.f;
+    g[q] = gq;
+    part += gq;
+  }
+  const float r = block_sum(part, red);   // contains a barrier: g[] is complete afterwards
+  const float den = r + eps;
+  for (int f = threadIdx.x; f < m_t; f += 256) {
+    float acc = 0.f;
+    for (int q = 0; q < nv; ++q) acc = fmaf(g[q], zb[(base + q) * ld_z + f], acc);
+    out[(b * N + t) * ld_out + f] = acc / den;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_maxsim_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, float* scores,
+                             hipStream_t stream) {
+  const int n_s = (int)((N + S - 1) / S);
+  const int64_t grid = B * n_s * n_s;
+  hipLaunchKernelGGL(maxsim_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, N, d, ld_x, S, n_s, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
+                               const int32_t* idx, const float* w, const float* P, int residual, float* xhat,
+                               int64_t ld_out, hipStream_t stream) {
+  const int n_s = (int)((N + S - 1) / S);
+  const int64_t total = B * N * d;
+  hipLaunchKernelGGL(compress_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, x, B, N, d,
+                     ld_x, S, k, n_s, idx, w, P, residual, xhat, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dyn_f32(const float* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps, float* out,
+                          int64_t ld_out, hipStream_t stream) {
+  hipLaunchKernelGGL(dyn_f32_kernel, dim3((unsigned)(B * N)), dim3(256), 0, stream, z, N, m_t, ld_z, S, eps, out,
+                     ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace avey

@@ -1,0 +1,156 @@
+/*
+ * avey.h -- C ABI of libavey.so: the Avey-B bidirectional ranker and dynamic contextualizer
+ * core on AMD Instinct MI355X (gfx950).
+ *
+ * Sources cited below:
+ *   [notes]   papernotes.org, ICLR2026 note "Avey-B: 把无注意力架构改造成双向编码器",
+ *             sections 方法详解/整体框架, 关键设计 2, 关键设计 3 (eq. 6), 关键设计 4 (eq. 8).
+ *   [summary] paperlayer.ai summary "Avey-B" (arXiv 2602.15814v1), sections 3 (Background),
+ *             4.2, 4.3 (Neural compression) and appendix H (Ablation study).
+ *
+ * General conventions (all entry points)
+ *   - Every pointer argument except the status string is DEVICE memory owned by the caller.
+ *     The library allocates nothing, keeps no state between calls, never synchronises and is
+ *     safe to call from several host threads at once.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream). The call
+ *     returns once the kernels are enqueued.
+ *   - Return value: AVEY_OK, or an AVEY_ERR_* code. Argument checks run on the host before
+ *     any HIP call, so a call that fails them enqueues nothing. AVEY_ERR_HIP reports a launch
+ *     error (hipGetLastError right after the launches). A fault while a kernel runs is only
+ *     seen at the caller's next synchronisation.
+ *   - Tensors are row-major. A [B, N, w] tensor with row stride `ld` (elements, ld >= w) has
+ *     element (b, t, c) at offset (b * N + t) * ld + c. Rows t >= N are never read or written.
+ *   - dtype AVEY_BF16: x, P, z and the outputs xhat/out are bf16 bit patterns (uint16),
+ *     accumulation is fp32. dtype AVEY_F32: the same tensors are float32, arithmetic is fp32.
+ *     scores and w are always float32; idx is always int32.
+ *   - Splits: n_s = ceil(N / S). Split j holds tokens [j*S, min((j+1)*S, N)); the missing
+ *     tokens of the last split are zero padding ([notes] 整体框架). Padding tokens take part
+ *     neither as targets nor as candidates in MaxSim, are zero rows in X_cat, and are not
+ *     mixed in the dynamic layer.
+ *   - Outputs must not overlap inputs.
+ *   - Empty work (B == 0 or N == 0) returns AVEY_OK and enqueues nothing; pointers may then
+ *     be NULL.
+ *   - Shape limits: 1 <= S <= 512. For AVEY_BF16 additionally S % 64 == 0, every feature
+ *     width (d, m_t) is a multiple of 64, every ld is a multiple of 8 and every tensor pointer
+ *     is 16-byte aligned; for AVEY_F32 every tensor pointer is 4-byte aligned.
+ *     Violations return AVEY_ERR_SHAPE, AVEY_ERR_ALIGN or AVEY_ERR_UNSUPPORTED.
+ */
+#ifndef AVEY_H
+#define AVEY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AVEY_ABI_VERSION 1
+
+typedef enum { AVEY_F32 = 0, AVEY_BF16 = 1 } avey_dtype;
+
+typedef enum {
+  AVEY_OK = 0,
+  AVEY_ERR_NULL = -1,        /* a required pointer is NULL                              */
+  AVEY_ERR_SHAPE = -2,       /* a size or leading dimension is out of range            */
+  AVEY_ERR_DTYPE = -3,       /* unknown dtype                                          */
+  AVEY_ERR_ALIGN = -4,       /* a pointer or leading dimension is misaligned           */
+  AVEY_ERR_UNSUPPORTED = -5, /* valid request that this build does not implement       */
+  AVEY_ERR_HIP = -6          /* the HIP runtime reported an error at launch            */
+} avey_status;
+
+/* ABI version implemented by the loaded library (AVEY_ABI_VERSION). */
+int32_t avey_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* avey_status_str(int32_t status);
+
+/*
+ * avey_maxsim_scores -- all-pairs split relevance ([summary] section 3: the ranker scores
+ * every split against the target split with MaxSim; [notes] 整体框架).
+ *
+ *   scores[b, i, j] = sum over valid tokens t of split i of
+ *                     max over valid tokens u of split j of cos(x_t, x_u),   for i != j
+ *   scores[b, i, i] = -INFINITY
+ * cos(a, b) = a.b / (|a| |b|), and 0 when either vector is zero (N(0) = 0).
+ *
+ *   x       [B, N, d] row stride ld_x, dtype dt (input)
+ *   scores  [B, n_s, n_s] float32, contiguous (output)
+ * Requires n_s >= 2. MaxSim is not symmetric; both directions of each split pair come from
+ * one pass over the pair.
+ */
+avey_status avey_maxsim_scores(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
+                               int64_t ld_x, int32_t S, float* scores, void* stream);
+
+/*
+ * avey_topk_norm -- top-k selection and divide-by-max weighting ([notes] 整体框架: the ranker
+ * keeps the k best candidate splits and divides their scores by the largest of them;
+ * [summary] section 3).
+ *
+ * For each row (b, i) of scores, the candidates j != i are ordered by (score descending,
+ * j ascending); NaN scores order as -INFINITY. The first k are written:
+ *   idx[b, i, r] = j_r                  (int32, rank order)
+ *   w[b, i, r]   = scores[b,i,j_r] / scores[b,i,j_0]   (IEEE fp32 division; w[..., 0] == 1
+ *                                                       exactly when the top score is finite
+ *                                                       and non-zero)
+ *   scores  [B, n_s, n_s] float32 (input; the diagonal is ignored)
+ *   idx, w  [B, n_s, k] int32 / float32 contiguous (outputs)
+ * Requires 1 <= k <= n_s - 1.
+ */
+avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t k,
+                           int32_t* idx, float* w, void* stream);
+
+/*
+ * avey_split_rank -- avey_maxsim_scores followed by avey_topk_norm on the same stream.
+ *   outputs scores [B, n_s, n_s], idx [B, n_s, k], w [B, n_s, k] as described above.
+ */
+avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
+                            int64_t ld_x, int32_t S, int32_t k, float* scores, int32_t* idx,
+                            float* w, void* stream);
+
+/*
+ * avey_select_compress -- weighted gather and neural compression ([notes] 关键设计 4, eq. 8;
+ * [summary] 4.3 and appendix H).
+ *
+ * For each split (b, i):
+ *   X_cat = [ X_i ; w[b,i,0] * X_{idx[b,i,0]} ; ... ; w[b,i,k-1] * X_{idx[b,i,k-1]} ]
+ *           ((k+1)S x d; each X_j is split j as S rows with zero padding)
+ *   Xhat_i = P X_cat + (residual ? X_i : 0)
+ * and the valid rows of Xhat_i are written to xhat.
+ *
+ *   x        [B, N, d] row stride ld_x (input)
+ *   idx, w   [B, n_s, k] int32 / float32 (inputs; every idx must lie in [0, n_s))
+ *   P        [S, (k+1)S] contiguous, dtype dt (input)
+ *   residual 0 or 1
+ *   xhat     [B, N, d] row stride ld_out, dtype dt (output)
+ * Requires k >= 1. For AVEY_BF16 each retrieved row w * x is rounded to bf16 before the
+ * product (the current split's rows are used as they are); the result is rounded to bf16.
+ */
+avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
+                                 int64_t ld_x, int32_t S, int32_t k, const int32_t* idx,
+                                 const float* w, const void* P, int32_t residual, void* xhat,
+                                 int64_t ld_out, void* stream);
+
+/*
+ * avey_dyn_context -- core of the dynamic contextualizer ([notes] 关键设计 2: mix Z_t with the
+ * cosine matrix N(Z_t) N(Z_t)^T; 关键设计 3, eq. 6: divide each row by its sum plus eps).
+ *
+ * For each split (b, i), over its valid tokens p, q (no mask between them: bidirectional):
+ *   n_p = z_p / |z_p|  (0 for a zero row)
+ *   G_pq = n_p . n_q,   r_p = sum_q G_pq
+ *   out_p = sum_q G_pq z_q / (r_p + eps)
+ * The activation and bias that follow in the full layer are not applied.
+ *
+ *   z_tail  [B, N, m_t] row stride ld_z (input; point it at the first tail column of Z)
+ *   out     [B, N, m_t] row stride ld_out, dtype dt (output)
+ * For AVEY_BF16, G is rounded to bf16 for the product with z and r is summed from those
+ * rounded values; the result is rounded to bf16.
+ */
+avey_status avey_dyn_context(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t,
+                             int64_t ld_z, int32_t S, float eps, void* out, int64_t ld_out,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AVEY_H */

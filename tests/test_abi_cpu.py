@@ -1,0 +1,105 @@
+"""libavey.so loads on the host, exports every function include/avey.h declares, and rejects bad
+arguments before any HIP call (CPU only: every call here fails validation or is empty work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_free_long_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "avey.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP = 0, -1, -2, -3, -4, -5
+P16 = 0x10000          # fake, 16-byte aligned device address: never dereferenced by these calls
+P4 = 0x10004           # 4-byte aligned, not 16-byte aligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(avey_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return A.load_library()
+
+
+def test_exports_match_header(lib):
+    decl = declared_functions()
+    assert set(decl) == set(A.EXPORTS)
+    so = ctypes.CDLL(A.LIB_PATH)
+    for name in decl:
+        assert hasattr(so, name), name
+    assert lib.avey_abi_version() == A.AVEY_ABI_VERSION == 1
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, -6):
+        assert lib.avey_status_str(code).decode().startswith("AVEY_")
+    assert lib.avey_status_str(12345) == b"unknown avey status"
+
+
+def test_split_rank_validation(lib):
+    f = lib.avey_split_rank
+    # (x, dt, B, N, d, ld, S, k, scores, idx, w, stream)
+    assert f(P16, 7, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == DTYPE
+    assert f(P16, 1, -1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 0, 3, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 1024, 3, P16, P16, P16, None) == SHAPE      # S > 512
+    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None) == OK       # B == 0: no work
+    assert f(None, 1, 1, 0, 64, 64, 64, 3, None, None, None, None) == OK          # N == 0: no work
+    assert f(None, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, None) == SHAPE        # k > n_s - 1
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 64, 64, 64, 64, 1, P16, P16, P16, None) == SHAPE           # a single split
+    assert f(P16, 1, 1, 1024, 64, 32, 64, 3, P16, P16, P16, None) == SHAPE         # ld < d
+    assert f(P16, 1, 1, 1024, 96, 96, 64, 3, P16, P16, P16, None) == UNSUP         # bf16 d % 64
+    assert f(P16, 1, 1, 1024, 64, 68, 64, 3, P16, P16, P16, None) == ALIGN         # bf16 ld % 8
+    assert f(P4, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == ALIGN          # bf16 x alignment
+    assert f(P16, 1, 1, 1000, 64, 64, 100, 3, P16, P16, P16, None) == UNSUP        # bf16 S % 64
+    assert f(P16, 0, 1, 1000, 64, 64, 64, 3, P16, P16 + 2, P16, None) == ALIGN     # idx alignment
+    assert f(P16, 1, 1, 1 << 25, 64, 64, 256, 3, P16, P16, P16, None) == UNSUP     # > 2^30 elements
+
+
+def test_topk_validation(lib):
+    f = lib.avey_topk_norm
+    assert f(P16, 0, 16, 3, P16, P16, None) == OK
+    assert f(None, 1, 16, 3, P16, P16, None) == NULL
+    assert f(P16, 1, 16, 16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1, P16, P16, None) == SHAPE
+    assert f(P16 + 1, 1, 16, 3, P16, P16, None) == ALIGN
+
+
+def test_select_compress_validation(lib):
+    f = lib.avey_select_compress
+    # (x, dt, B, N, d, ld_x, S, k, idx, w, P, residual, xhat, ld_out, stream)
+    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, 1, None, 64, None) == OK
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, 1, P16, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, 1, None, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, 2, P16, 64, None) == SHAPE   # residual flag
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, 1, P16, 64, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, 1, P16, 60, None) == SHAPE   # ld_out < d
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P4, 1, P16, 64, None) == ALIGN    # P alignment
+    assert f(P16, 1, 1, 1024, 64, 64, 32, 3, P16, P16, P16, 1, P16, 64, None) == UNSUP   # bf16 S % 64
+
+
+def test_dyn_context_validation(lib):
+    f = lib.avey_dyn_context
+    # (z_tail, dt, B, N, m_t, ld_z, S, eps, out, ld_out, stream)
+    assert f(None, 1, 0, 1024, 64, 64, 64, 1e-8, None, 64, None) == OK
+    assert f(None, 1, 1, 1024, 64, 64, 64, 1e-8, P16, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, None, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 100, 104, 64, 1e-8, P16, 104, None) == UNSUP    # bf16 m_t % 64
+    assert f(P16, 1, 1, 1024, 64, 64, 600, 1e-8, P16, 64, None) == SHAPE      # S > 512
+    assert f(P16 + 8, 1, 1, 1024, 64, 64, 64, 1e-8, P16, 64, None) == ALIGN
+    assert f(P16, 9, 1, 1024, 64, 64, 64, 1e-8, P16, 64, None) == DTYPE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(A.AveyError):
+        A.avey_split_rank(torch.zeros(1, 1024, 64, dtype=torch.bfloat16), 64, 3)

@@ -1,0 +1,170 @@
+"""GPU parity: libavey (through the C ABI) against the float64 CPU oracle on identical inputs.
+
+Small workloads (several tiles, ragged last split) are compared output by output; the full-size
+workloads are compared on sampled score rows and sampled splits, in the launch configuration
+the bench times.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_free_long_amd as A
+from oracle import avey_oracle as O
+from synth import CONFIGS, Config, make_inputs
+
+from helpers import (TOL, check_score_row, check_topk_row, dev_tensor, host_f64, row_rel_err,
+                     split_rows_of, upload)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # 8 splits of 256, last one 208 tokens; 2 sequences
+    "small_bf16": Config("small_bf16", B=2, N=2000, d=256, S=256, k=3, m_t=256, m=384, dtype="bf16",
+                         x_dist="mixture", n_centroids=16),
+    # S = 512: 2 x 2 quadrants per split pair, last split 40 tokens
+    "s512_bf16": Config("s512_bf16", B=2, N=2600, d=128, S=512, k=2, m_t=128, m=256, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+    # S = 64 < tile: heavy masking inside every tile
+    "s64_bf16": Config("s64_bf16", B=1, N=700, d=64, S=64, k=2, m_t=64, m=128, dtype="bf16",
+                       x_dist="mixture", n_centroids=8),
+    "tiny": CONFIGS["tiny"],
+}
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_all(inp, residual=True):
+    cfg = inp.cfg
+    x, P, z, z_tail = upload(inp)
+    scores, idx, w = A.avey_split_rank(x, cfg.S, cfg.k)
+    xhat = A.avey_select_compress(x, idx, w, P, cfg.S, residual=residual)
+    out = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
+    torch.cuda.synchronize()
+    return {
+        "scores": scores.cpu().numpy().astype(np.float64),
+        "idx": idx.cpu().numpy(),
+        "w": w.cpu().numpy(),
+        "xhat": host_f64(xhat),
+        "out": host_f64(out),
+    }
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_parity(gpu_ok, name):
+    cfg = SMALL[name]
+    tol = TOL[cfg.dtype]
+    inp = make_inputs(cfg)
+    say(f"{name}: split_rank + select_compress + dyn_context B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S} k={cfg.k}")
+    g = run_all(inp)
+    x64 = inp.x_f64()
+    n_s = cfg.n_s
+    ranked = O.split_rank(x64, cfg.S, cfg.k)
+    for (b, i), (o_row, o_idx, o_w, gap) in ranked.items():
+        check_score_row(g["scores"][b, i], o_row, i, tol["scores"])
+        check_topk_row(g["idx"][b, i], g["w"][b, i], o_row, o_idx, gap, i, cfg.k, tol["w"])
+    # compression on the GPU's own idx / w (independent of tie effects)
+    comp = O.select_compress(x64, cfg.S, g["idx"], g["w"].astype(np.float64), inp.P_f64(), residual=True)
+    for (b, i), rows in comp.items():
+        err = row_rel_err(g["xhat"][b, split_rows_of(cfg.N, cfg.S, i)], rows)
+        assert err <= tol["out"], f"xhat split {(b, i)}: {err:.3e}"
+    dyn = O.dyn_context(inp.z_tail_f64(), cfg.S, cfg.eps)
+    for (b, i), rows in dyn.items():
+        err = row_rel_err(g["out"][b, split_rows_of(cfg.N, cfg.S, i)], rows)
+        assert err <= tol["out"], f"dyn split {(b, i)}: {err:.3e}"
+    assert n_s == g["scores"].shape[1]
+
+
+def test_residual_off_and_k_max(gpu_ok):
+    cfg = SMALL["small_bf16"].with_(k=7, B=1)        # k = n_s - 1: every other split is retrieved
+    inp = make_inputs(cfg)
+    say("residual off, k = n_s - 1")
+    g = run_all(inp, residual=False)
+    x64 = inp.x_f64()
+    ranked = O.split_rank(x64, cfg.S, cfg.k)
+    for (b, i), (o_row, o_idx, o_w, gap) in ranked.items():
+        assert sorted(g["idx"][b, i].tolist()) == [j for j in range(cfg.n_s) if j != i]
+        check_topk_row(g["idx"][b, i], g["w"][b, i], o_row, o_idx, gap, i, cfg.k, TOL["bf16"]["w"])
+    comp = O.select_compress(x64, cfg.S, g["idx"], g["w"].astype(np.float64), inp.P_f64(), residual=False)
+    for (b, i), rows in comp.items():
+        assert row_rel_err(g["xhat"][b, split_rows_of(cfg.N, cfg.S, i)], rows) <= TOL["bf16"]["out"]
+
+
+def test_padding_rows_never_read_and_determinism(gpu_ok):
+    """NaN rows after N must not change any output (they are never loaded); two runs are bitwise equal."""
+    cfg = SMALL["small_bf16"].with_(B=1)
+    inp = make_inputs(cfg)
+    say("NaN sentinels after N, determinism")
+    x, P, z, z_tail = upload(inp)
+    N, d = cfg.N, cfg.d
+    xb = torch.full((1, N + 64, d), float("nan"), device="cuda", dtype=torch.bfloat16)
+    xb[:, :N] = x
+    zb = torch.full((1, N + 64, cfg.m), float("nan"), device="cuda", dtype=torch.bfloat16)
+    zb[:, :N] = z
+    outs = []
+    for xx, zz in ((x, z), (xb[:, :N], zb[:, :N]), (x, z)):
+        s, i_, w_ = A.avey_split_rank(xx, cfg.S, cfg.k)
+        xh = A.avey_select_compress(xx, i_, w_, P, cfg.S)
+        o = A.avey_dyn_context(zz[..., inp.tail_col:], cfg.S, cfg.eps)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (s, i_, w_, xh, o)])
+    for a_, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_,
+                           b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_)
+    for a_, b_ in zip(outs[0], outs[2]):
+        assert torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_,
+                           b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_)
+    assert torch.isfinite(outs[0][3].float()).all() and torch.isfinite(outs[0][4].float()).all()
+
+
+def test_empty_inputs(gpu_ok):
+    x = torch.empty((0, 1024, 64), device="cuda", dtype=torch.bfloat16)
+    s, i_, w_ = A.avey_split_rank(x, 64, 3)
+    assert s.numel() == 0
+    z = torch.empty((2, 0, 64), device="cuda", dtype=torch.bfloat16)
+    assert A.avey_dyn_context(z, 64, 1e-8).numel() == 0
+
+
+# ------------------------------------------------------------------ full-size workloads
+FULL_SAMPLES = {
+    "base": [(0, 0), (3, 17), (7, 31)],
+    "long": [(0, 0), (0, 77), (1, 127)],
+    "extreme": [(0, 0), (0, 200), (0, 383)],
+    "wide": [(0, 0), (1, 9), (3, 31)],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_full_size_sampled(gpu_ok, name):
+    cfg = CONFIGS[name]
+    tol = TOL[cfg.dtype]
+    inp = make_inputs(cfg)
+    say(f"{name}: full size B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S} k={cfg.k} m_t={cfg.m_t}")
+    g = run_all(inp)
+    rows = FULL_SAMPLES[name]
+    x64_b = {b: inp.x_f64(b) for b in {b for b, _ in rows}}
+    for b, i in rows:
+        o_row = O.score_row(x64_b[b], cfg.S, i)
+        o_idx, _, _, gap = O.top_k(o_row, i, cfg.k)
+        check_score_row(g["scores"][b, i], o_row, i, tol["scores"])
+        check_topk_row(g["idx"][b, i], g["w"][b, i], o_row, o_idx, gap, i, cfg.k, tol["w"])
+        ref = O.compress_split(x64_b[b], cfg.S, g["idx"][b, i], g["w"][b, i].astype(np.float64), inp.P_f64(), i)
+        err = row_rel_err(g["xhat"][b, split_rows_of(cfg.N, cfg.S, i)], ref)
+        assert err <= tol["out"], f"xhat {(b, i)}: {err:.3e}"
+        zt = inp.z_tail_f64(b, split_rows_of(cfg.N, cfg.S, i))
+        ref = O.dyn_context_split(zt, cfg.S, cfg.eps, 0)
+        err = row_rel_err(g["out"][b, split_rows_of(cfg.N, cfg.S, i)], ref)
+        assert err <= tol["out"], f"dyn {(b, i)}: {err:.3e}"
+    # properties that hold everywhere: w0 == 1, weights in (0, 1], indices valid and not self
+    w = g["w"]
+    assert (w[..., 0] == 1.0).all() and (w > 0).all() and (w <= 1).all()
+    n_s = cfg.n_s
+    idx = g["idx"]
+    assert (idx >= 0).all() and (idx < n_s).all()
+    assert not (idx == np.arange(n_s)[None, :, None]).any()
+    assert np.isfinite(g["xhat"]).all() and np.isfinite(g["out"]).all()
