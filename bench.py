@@ -1,0 +1,214 @@
+"""Throughput of the Avey-B ranker + dynamic contextualizer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long] [--no-cpu-baseline]
+
+One step is one pass of the whole path over one batch of synthetic input already resident in
+HBM: all-pairs MaxSim, top-k with divide-by-max, weighted gather + (k+1)S -> S compression,
+and the dynamic layer's row-normalised cosine mixing. The default workload is the 32K-token
+one (batch 2, N = 32768, d = 768, S = 256, k = 3, tail width 1536).
+
+Prints one JSON line: tokens/s over the timed steps, per-kernel times from HIP events on the
+launch stream, the MaxSim kernel against the bf16 MFMA roofline, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "tokens/sec for ranker+dynamic layer at N=32K; MaxSim MFMA util %"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic(cfg):
+    """Algorithmic work per launch of each kernel (FLOPs, bytes)."""
+    B, N, d, S, k, m_t = cfg.B, cfg.N, cfg.d, cfg.S, cfg.k, cfg.m_t
+    n_s = cfg.n_s
+    eb = 2 if cfg.dtype == "bf16" else 4
+    pairs = B * n_s * (n_s - 1) // 2
+    return {
+        # one S x S x d tile per unordered split pair serves both directions
+        "maxsim": {"flop": 2.0 * S * S * d * pairs, "bytes": B * N * d * eb},
+        "topk": {"flop": 0.0, "bytes": B * n_s * n_s * 4 + 2 * B * n_s * k * 4},
+        # read X_i and k retrieved splits, write Xhat_i; P once
+        "compress": {"flop": 2.0 * B * n_s * S * d * (k + 1) * S,
+                     "bytes": (k + 2) * B * N * d * eb + S * (k + 1) * S * eb},
+        # read the tail once, write the output once
+        "dyn": {"flop": 4.0 * B * n_s * S * S * m_t, "bytes": 2 * B * N * m_t * eb},
+    }
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """The float64 oracle, as it stands, on whole target splits of the same workload until the
+    time budget is spent: score row + top-k, compression and dynamic layer of each split."""
+    import numpy as np
+    from oracle import avey_oracle as O
+    cfg = inp.cfg
+    n_s = cfg.n_s
+    stride = max(1, n_s // 16)
+    order = [(b, i) for r in range(stride) for i in range(r, n_s, stride) for b in range(cfg.B)]
+    xs, Ps = {}, inp.P_f64()
+    done, tok = 0, 0
+    t0 = time.perf_counter()
+    for b, i in order:
+        if b not in xs:
+            xs[b] = inp.x_f64(b)
+        row = O.score_row(xs[b], cfg.S, i)
+        idx, w, _, _ = O.top_k(row, i, cfg.k)
+        O.compress_split(xs[b], cfg.S, idx, w, Ps, i)
+        rows = slice(i * cfg.S, min((i + 1) * cfg.S, cfg.N))
+        O.dyn_context_split(inp.z_tail_f64(b, rows), cfg.S, cfg.eps, 0)
+        done += 1
+        tok += rows.stop - rows.start
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": tok / el,
+        "unit": "tokens/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of {cfg.B * n_s} target splits of the {cfg.name} workload (full score row, "
+                  f"top-k, compression and dynamic layer per split), {el:.1f} s, float64 numpy",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path here is the single-GPU kernel set; "
+              "run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import attention_free_long_amd as A
+    from synth import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    cfg = CONFIGS[args.config]
+    inp = make_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    x, P, z = dev(inp.x), dev(inp.P), dev(inp.z)
+    z_tail = z[..., inp.tail_col:]
+    B, N, n_s, S, k = cfg.B, cfg.N, cfg.n_s, cfg.S, cfg.k
+    scores = torch.empty((B, n_s, n_s), device="cuda", dtype=torch.float32)
+    idx = torch.empty((B, n_s, k), device="cuda", dtype=torch.int32)
+    w = torch.empty((B, n_s, k), device="cuda", dtype=torch.float32)
+    xhat = torch.empty((B, N, cfg.d), device="cuda", dtype=dt)
+    out = torch.empty((B, N, cfg.m_t), device="cuda", dtype=dt)
+    names = ("maxsim", "topk", "compress", "dyn")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        A.avey_maxsim_scores(x, S, scores)
+        if ev is not None:
+            ev[1].record()
+        A.avey_topk_norm(scores, k, idx, w)
+        if ev is not None:
+            ev[2].record()
+        A.avey_select_compress(x, idx, w, P, S, residual=True, out=xhat)
+        if ev is not None:
+            ev[3].record()
+        A.avey_dyn_context(z_tail, S, cfg.eps, out=out)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    work = algorithmic(cfg)
+    kern = {}
+    for n in names:
+        t = float(np.mean(per[n]))
+        entry = {"avg_us": t * 1e6, "min_us": float(np.min(per[n])) * 1e6}
+        if work[n]["flop"]:
+            entry["tflops"] = work[n]["flop"] / t / 1e12
+        entry["gbs"] = work[n]["bytes"] / t / 1e9
+        kern[n] = entry
+    ms_per_step = wall / args.steps * 1e3
+    value = B * N / (wall / args.steps)
+
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    ms_t = kern["maxsim"]["avg_us"] * 1e-6
+    achieved = work["maxsim"]["flop"] / ms_t / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
+    comp_t = kern["compress"]["avg_us"] * 1e-6
+    dyn_t = kern["dyn"]["avg_us"] * 1e-6
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} N={N} d={cfg.d} S={S} k={k} m_t={cfg.m_t} eps={cfg.eps}",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "maxsim_mfma_util_pct": round(100 * achieved / peak, 2),
+        "compress_hbm_frac": round(work["compress"]["bytes"] / comp_t / 1e9 / PEAK_HBM_GBS, 4),
+        "dyn_hbm_frac": round(work["dyn"]["bytes"] / dyn_t / 1e9 / PEAK_HBM_GBS, 4),
+        "dyn_mfma_frac": round(work["dyn"]["flop"] / dyn_t / 1e12 / peak, 4),
+        "kernels": {n: {kk: round(v, 3) for kk, v in e.items()} for n, e in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 2)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
