@@ -56,11 +56,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_status_str.restype = ctypes.c_char_p
     lib.avey_status_str.argtypes = [i32]
     lib.avey_maxsim_scores.restype = i32
-    lib.avey_maxsim_scores.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp]
+    lib.avey_maxsim_scores.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, vp]
     lib.avey_topk_norm.restype = i32
     lib.avey_topk_norm.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.avey_split_rank.restype = i32
-    lib.avey_split_rank.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.avey_split_rank.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.avey_select_compress.restype = i32
     lib.avey_select_compress.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, i64, vp]
     lib.avey_dyn_context.restype = i32
@@ -110,15 +110,19 @@ def n_splits(N: int, S: int) -> int:
     return -(-N // S)
 
 
-def avey_maxsim_scores(x, S: int, scores=None):
-    """All-pairs MaxSim scores [B, n_s, n_s] (fp32, diagonal -inf) of x [B, N, d]."""
+def avey_maxsim_scores(x, S: int, scores=None, rnorm=None):
+    """All-pairs MaxSim scores [B, n_s, n_s] (fp32, diagonal -inf) of x [B, N, d].
+
+    rnorm [B, N] (fp32) receives the inverse token norms; allocated when not given."""
     import torch
     B, N, d, ld = _rows(x, "x")
     n_s = n_splits(N, S)
     if scores is None:
         scores = torch.empty((B, n_s, n_s), device=x.device, dtype=torch.float32)
+    if rnorm is None:
+        rnorm = torch.empty((B, N), device=x.device, dtype=torch.float32)
     _check("avey_maxsim_scores", load_library().avey_maxsim_scores(
-        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, scores.data_ptr(), _stream(x)))
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, scores.data_ptr(), rnorm.data_ptr(), _stream(x)))
     return scores
 
 
@@ -135,8 +139,8 @@ def avey_topk_norm(scores, k: int, idx=None, w=None):
     return idx, w
 
 
-def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None):
-    """(scores, idx, w) of the bidirectional ranker for x [B, N, d]."""
+def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, rnorm=None):
+    """(scores, idx, w) of the bidirectional ranker for x [B, N, d] (rnorm as in avey_maxsim_scores)."""
     import torch
     B, N, d, ld = _rows(x, "x")
     n_s = n_splits(N, S)
@@ -147,9 +151,11 @@ def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None):
         idx = torch.empty((B, n_s, k), device=dev, dtype=torch.int32)
     if w is None:
         w = torch.empty((B, n_s, k), device=dev, dtype=torch.float32)
+    if rnorm is None:
+        rnorm = torch.empty((B, N), device=dev, dtype=torch.float32)
     _check("avey_split_rank", load_library().avey_split_rank(
         x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, scores.data_ptr(), idx.data_ptr(), w.data_ptr(),
-        _stream(x)))
+        rnorm.data_ptr(), _stream(x)))
     return scores, idx, w
 
 

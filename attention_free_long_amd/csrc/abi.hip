@@ -71,22 +71,25 @@ const char* avey_status_str(int32_t s) {
 }
 
 avey_status avey_maxsim_scores(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
-                               int32_t S, float* scores, void* stream) {
+                               int32_t S, float* scores, float* rnorm, void* stream) {
   bool empty = false;
   AVEY_TRY(check_common(dt, B, N, S, &empty));
   if (empty) return AVEY_OK;
-  if (!scores) return AVEY_ERR_NULL;
+  if (!scores || !rnorm) return AVEY_ERR_NULL;
   AVEY_TRY(check_tensor(x, dt, N, d, ld_x));
   const int64_t n_s = splits(N, S);
   if (n_s < 2) return AVEY_ERR_SHAPE;
-  if (!aligned(scores, 4)) return AVEY_ERR_ALIGN;
+  if (!aligned(scores, 4) || !aligned(rnorm, 4)) return AVEY_ERR_ALIGN;
   AVEY_TRY(check_split_bf16(dt, S));
+  if ((B * N + 15) / 16 > kI32) return AVEY_ERR_UNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dt == AVEY_BF16) {
-    if (B * (n_s * (n_s - 1) / 2) > kI32) return AVEY_ERR_UNSUPPORTED;
-    return hip_status(launch_maxsim_bf16(static_cast<const uint16_t*>(x), B, N, (int)d, ld_x, S, scores, st));
+    if (n_s * (n_s - 1) / 2 > kI32) return AVEY_ERR_UNSUPPORTED;
+    AVEY_TRY(hip_status(launch_rnorm(x, true, B, N, (int)d, ld_x, rnorm, st)));
+    return hip_status(launch_maxsim_bf16(static_cast<const uint16_t*>(x), rnorm, B, N, (int)d, ld_x, S, scores, st));
   }
   if (B * n_s * n_s > kI32) return AVEY_ERR_UNSUPPORTED;
+  AVEY_TRY(hip_status(launch_rnorm(x, false, B, N, (int)d, ld_x, rnorm, st)));
   return hip_status(launch_maxsim_f32(static_cast<const float*>(x), B, N, (int)d, ld_x, S, scores, st));
 }
 
@@ -102,7 +105,7 @@ avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t 
 }
 
 avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
-                            int32_t k, float* scores, int32_t* idx, float* w, void* stream) {
+                            int32_t k, float* scores, int32_t* idx, float* w, float* rnorm, void* stream) {
   bool empty = false;
   AVEY_TRY(check_common(dt, B, N, S, &empty));
   if (empty) return AVEY_OK;
@@ -110,7 +113,7 @@ avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, 
   const int64_t n_s = splits(N, S);
   if (k < 1 || k > n_s - 1) return AVEY_ERR_SHAPE;
   if (!aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
-  AVEY_TRY(avey_maxsim_scores(x, dt, B, N, d, ld_x, S, scores, stream));
+  AVEY_TRY(avey_maxsim_scores(x, dt, B, N, d, ld_x, S, scores, rnorm, stream));
   return avey_topk_norm(scores, B, n_s, k, idx, w, stream);
 }
 

@@ -2,12 +2,14 @@
 //
 // Operand tiles live in LDS as [rows][64] bf16 (128-byte rows). The sixteen-byte chunk c of
 // row r is stored at chunk position c ^ swz(r), with one of two swizzles:
-//   * SWZ_ROW  swz(r) = r & 7               for tiles filled by direct global -> LDS copies
+//   * SWZ_ROW  swz(r) = (r >> 1) & 7        for tiles filled by direct global -> LDS copies
 //     (one copy instruction writes 8 whole rows);
 //   * SWZ_DIAG swz(r) = (r ^ (r >> 3)) & 7  for tiles written by register transposes (one
 //     write instruction covers rows 8 apart).
-// Either way an MFMA fragment read (32 consecutive rows, one chunk each) and the tile's own
-// write pattern touch eight distinct chunk positions per eight lanes, i.e. all 32 banks. Both
+// The LDS has 64 four-byte banks and serves a 16-byte-per-lane access for 16 lanes per cycle, so
+// an MFMA fragment read (16 consecutive rows, one chunk each) must hit 16 distinct 16-byte slots
+// of a 256-byte window: rows 2m and 2m+1 differ by 128 bytes, and the swizzle spreads the eight
+// row pairs over the eight chunk positions. Both
 // keep the fragment address of row block mb (32 rows) a fixed offset from block 0 (SWZ_DIAG
 // also swaps k-steps 0<->2 and 1<->3 on odd blocks), so a wave needs only 4 address registers
 // per operand.
@@ -32,7 +34,7 @@ enum Swizzle { SWZ_ROW = 0, SWZ_DIAG = 1 };
 
 template <Swizzle W>
 __device__ __forceinline__ uint32_t swz(int r) {
-  return W == SWZ_ROW ? (uint32_t)(r & 7) : (uint32_t)((r ^ (r >> 3)) & 7);
+  return W == SWZ_ROW ? (uint32_t)((r >> 1) & 7) : (uint32_t)((r ^ (r >> 3)) & 7);
 }
 
 // Byte offset of logical 16-byte chunk c of row r.
@@ -122,6 +124,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_bas
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS traffic only. __syncthreads() also drains every outstanding global
+// load, including direct-to-LDS copies of a stage that is not read yet; this one waits for the
+// wave's own LDS operations and leaves global loads in flight. The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Barrier after which every wave's direct-to-LDS copies (and LDS writes) are complete.
+__device__ __forceinline__ void copy_sync() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

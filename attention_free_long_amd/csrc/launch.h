@@ -6,8 +6,10 @@
 
 namespace avey {
 
-hipError_t launch_maxsim_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, float* scores,
-                              hipStream_t stream);
+hipError_t launch_rnorm(const void* x, bool bf16, int64_t B, int64_t N, int d, int64_t ld, float* rn,
+                        hipStream_t stream);
+hipError_t launch_maxsim_bf16(const uint16_t* x, const float* rn, int64_t B, int64_t N, int d, int64_t ld_x, int S,
+                              float* scores, hipStream_t stream);
 hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, int32_t* idx, float* w,
                             hipStream_t stream);
 hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,

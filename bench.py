@@ -128,6 +128,7 @@ def main(argv=None):
     scores = torch.empty((B, n_s, n_s), device="cuda", dtype=torch.float32)
     idx = torch.empty((B, n_s, k), device="cuda", dtype=torch.int32)
     w = torch.empty((B, n_s, k), device="cuda", dtype=torch.float32)
+    rnorm = torch.empty((B, N), device="cuda", dtype=torch.float32)
     xhat = torch.empty((B, N, cfg.d), device="cuda", dtype=dt)
     out = torch.empty((B, N, cfg.m_t), device="cuda", dtype=dt)
     names = ("maxsim", "topk", "compress", "dyn")
@@ -135,7 +136,7 @@ def main(argv=None):
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        A.avey_maxsim_scores(x, S, scores)
+        A.avey_maxsim_scores(x, S, scores, rnorm)
         if ev is not None:
             ev[1].record()
         A.avey_topk_norm(scores, k, idx, w)

@@ -75,11 +75,13 @@ const char* avey_status_str(int32_t status);
  *
  *   x       [B, N, d] row stride ld_x, dtype dt (input)
  *   scores  [B, n_s, n_s] float32, contiguous (output)
+ *   rnorm   [B, N] float32, contiguous (output): rnorm[b, t] = 1 / |x_t|, 0 for a zero token --
+ *           the scale of N(.) ([notes] 关键设计 2). Written first, then read by the scoring pass.
  * Requires n_s >= 2. MaxSim is not symmetric; both directions of each split pair come from
  * one pass over the pair.
  */
 avey_status avey_maxsim_scores(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
-                               int64_t ld_x, int32_t S, float* scores, void* stream);
+                               int64_t ld_x, int32_t S, float* scores, float* rnorm, void* stream);
 
 /*
  * avey_topk_norm -- top-k selection and divide-by-max weighting ([notes] 整体框架: the ranker
@@ -101,11 +103,12 @@ avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t 
 
 /*
  * avey_split_rank -- avey_maxsim_scores followed by avey_topk_norm on the same stream.
- *   outputs scores [B, n_s, n_s], idx [B, n_s, k], w [B, n_s, k] as described above.
+ *   outputs scores [B, n_s, n_s], idx [B, n_s, k], w [B, n_s, k], rnorm [B, N] as described
+ *   above.
  */
 avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
                             int64_t ld_x, int32_t S, int32_t k, float* scores, int32_t* idx,
-                            float* w, void* stream);
+                            float* w, float* rnorm, void* stream);
 
 /*
  * avey_select_compress -- weighted gather and neural compression ([notes] 关键设计 4, eq. 8;

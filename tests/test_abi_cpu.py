@@ -44,25 +44,25 @@ def test_status_strings(lib):
 
 def test_split_rank_validation(lib):
     f = lib.avey_split_rank
-    # (x, dt, B, N, d, ld, S, k, scores, idx, w, stream)
-    assert f(P16, 7, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == DTYPE
-    assert f(P16, 1, -1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == SHAPE
-    assert f(P16, 1, 1, 1024, 64, 64, 0, 3, P16, P16, P16, None) == SHAPE
-    assert f(P16, 1, 1, 1024, 64, 64, 1024, 3, P16, P16, P16, None) == SHAPE      # S > 512
-    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None) == OK       # B == 0: no work
-    assert f(None, 1, 1, 0, 64, 64, 64, 3, None, None, None, None) == OK          # N == 0: no work
-    assert f(None, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == NULL
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, None) == NULL
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, None) == SHAPE        # k > n_s - 1
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, None) == SHAPE
-    assert f(P16, 1, 1, 64, 64, 64, 64, 1, P16, P16, P16, None) == SHAPE           # a single split
-    assert f(P16, 1, 1, 1024, 64, 32, 64, 3, P16, P16, P16, None) == SHAPE         # ld < d
-    assert f(P16, 1, 1, 1024, 96, 96, 64, 3, P16, P16, P16, None) == UNSUP         # bf16 d % 64
-    assert f(P16, 1, 1, 1024, 64, 68, 64, 3, P16, P16, P16, None) == ALIGN         # bf16 ld % 8
-    assert f(P4, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == ALIGN          # bf16 x alignment
-    assert f(P16, 1, 1, 1000, 64, 64, 100, 3, P16, P16, P16, None) == UNSUP        # bf16 S % 64
-    assert f(P16, 0, 1, 1000, 64, 64, 64, 3, P16, P16 + 2, P16, None) == ALIGN     # idx alignment
-    assert f(P16, 1, 1, 1 << 25, 64, 64, 256, 3, P16, P16, P16, None) == UNSUP     # > 2^30 elements
+    # (x, dt, B, N, d, ld, S, k, scores, idx, w, rnorm, stream)
+    assert f(P16, 7, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == DTYPE
+    assert f(P16, 1, -1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 0, 3, P16, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 1024, 3, P16, P16, P16, P16, None) == SHAPE      # S > 512
+    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None, None) == OK       # B == 0: no work
+    assert f(None, 1, 1, 0, 64, 64, 64, 3, None, None, None, None, None) == OK          # N == 0: no work
+    assert f(None, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, P16, None) == SHAPE        # k > n_s - 1
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 64, 64, 64, 64, 1, P16, P16, P16, P16, None) == SHAPE           # a single split
+    assert f(P16, 1, 1, 1024, 64, 32, 64, 3, P16, P16, P16, P16, None) == SHAPE         # ld < d
+    assert f(P16, 1, 1, 1024, 96, 96, 64, 3, P16, P16, P16, P16, None) == UNSUP         # bf16 d % 64
+    assert f(P16, 1, 1, 1024, 64, 68, 64, 3, P16, P16, P16, P16, None) == ALIGN         # bf16 ld % 8
+    assert f(P4, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == ALIGN          # bf16 x alignment
+    assert f(P16, 1, 1, 1000, 64, 64, 100, 3, P16, P16, P16, P16, None) == UNSUP        # bf16 S % 64
+    assert f(P16, 0, 1, 1000, 64, 64, 64, 3, P16, P16 + 2, P16, P16, None) == ALIGN     # idx alignment
+    assert f(P16, 1, 1, 1 << 25, 64, 64, 256, 3, P16, P16, P16, P16, None) == UNSUP     # > 2^30 elements
 
 
 def test_topk_validation(lib):
