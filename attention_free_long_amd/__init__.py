@@ -3,7 +3,7 @@
 Thin ctypes binding over libavey.so (see include/avey.h): argument marshalling only, every step
 runs in the library's HIP kernels. torch supplies device memory and the current stream.
 
-    scores, idx, w = avey_split_rank(x, S, k)
+    scores, idx, w = avey_split_rank(x, S, k)        # allocates the ranker workspace if not given
     xhat = avey_select_compress(x, idx, w, P, S, residual=True)
     out = avey_dyn_context(z_tail, S, eps)
 
@@ -23,6 +23,8 @@ AVEY_ABI_VERSION = 1
 EXPORTS = (
     "avey_abi_version",
     "avey_status_str",
+    "avey_rank_workspace_bytes",
+    "avey_maxsim_prepare",
     "avey_maxsim_scores",
     "avey_topk_norm",
     "avey_split_rank",
@@ -55,8 +57,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_abi_version.argtypes = []
     lib.avey_status_str.restype = ctypes.c_char_p
     lib.avey_status_str.argtypes = [i32]
+    lib.avey_rank_workspace_bytes.restype = i64
+    lib.avey_rank_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    lib.avey_maxsim_prepare.restype = i32
+    lib.avey_maxsim_prepare.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp]
     lib.avey_maxsim_scores.restype = i32
-    lib.avey_maxsim_scores.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, vp]
+    lib.avey_maxsim_scores.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp]
     lib.avey_topk_norm.restype = i32
     lib.avey_topk_norm.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.avey_split_rank.restype = i32
@@ -110,19 +116,42 @@ def n_splits(N: int, S: int) -> int:
     return -(-N // S)
 
 
-def avey_maxsim_scores(x, S: int, scores=None, rnorm=None):
-    """All-pairs MaxSim scores [B, n_s, n_s] (fp32, diagonal -inf) of x [B, N, d].
+def avey_rank_workspace_bytes(dtype_code: int, B: int, N: int, d: int, S: int) -> int:
+    """Bytes of the ranker workspace for this shape; raises AveyError if the shape is rejected."""
+    n = load_library().avey_rank_workspace_bytes(dtype_code, B, N, d, S)
+    if n < 0:
+        _check("avey_rank_workspace_bytes", int(n))
+    return int(n)
 
-    rnorm [B, N] (fp32) receives the inverse token norms; allocated when not given."""
+
+def rank_workspace(x, S: int):
+    """A device byte buffer large enough to be the ranker workspace for x [B, N, d]."""
     import torch
+    B, N, d, _ = _rows(x, "x")
+    n = avey_rank_workspace_bytes(_dtype_code(x), B, N, d, S)
+    return torch.empty((max(n, 16),), device=x.device, dtype=torch.uint8)
+
+
+def avey_maxsim_prepare(x, S: int, workspace=None):
+    """Fill (and return) the ranker workspace from x [B, N, d]."""
     B, N, d, ld = _rows(x, "x")
+    if workspace is None:
+        workspace = rank_workspace(x, S)
+    _check("avey_maxsim_prepare", load_library().avey_maxsim_prepare(
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, workspace.data_ptr(), _stream(x)))
+    return workspace
+
+
+def avey_maxsim_scores(workspace, x, S: int, scores=None):
+    """All-pairs MaxSim scores [B, n_s, n_s] (fp32, diagonal -inf) from a workspace that
+    avey_maxsim_prepare filled for x (x supplies the shape and dtype only)."""
+    import torch
+    B, N, d, _ = _rows(x, "x")
     n_s = n_splits(N, S)
     if scores is None:
         scores = torch.empty((B, n_s, n_s), device=x.device, dtype=torch.float32)
-    if rnorm is None:
-        rnorm = torch.empty((B, N), device=x.device, dtype=torch.float32)
     _check("avey_maxsim_scores", load_library().avey_maxsim_scores(
-        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, scores.data_ptr(), rnorm.data_ptr(), _stream(x)))
+        workspace.data_ptr(), _dtype_code(x), B, N, d, S, scores.data_ptr(), _stream(x)))
     return scores
 
 
@@ -139,23 +168,23 @@ def avey_topk_norm(scores, k: int, idx=None, w=None):
     return idx, w
 
 
-def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, rnorm=None):
-    """(scores, idx, w) of the bidirectional ranker for x [B, N, d] (rnorm as in avey_maxsim_scores)."""
+def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, workspace=None):
+    """(scores, idx, w) of the bidirectional ranker for x [B, N, d]."""
     import torch
     B, N, d, ld = _rows(x, "x")
     n_s = n_splits(N, S)
     dev = x.device
+    if workspace is None:
+        workspace = rank_workspace(x, S)
     if scores is None:
         scores = torch.empty((B, n_s, n_s), device=dev, dtype=torch.float32)
     if idx is None:
         idx = torch.empty((B, n_s, k), device=dev, dtype=torch.int32)
     if w is None:
         w = torch.empty((B, n_s, k), device=dev, dtype=torch.float32)
-    if rnorm is None:
-        rnorm = torch.empty((B, N), device=dev, dtype=torch.float32)
     _check("avey_split_rank", load_library().avey_split_rank(
-        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, scores.data_ptr(), idx.data_ptr(), w.data_ptr(),
-        rnorm.data_ptr(), _stream(x)))
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, workspace.data_ptr(), scores.data_ptr(), idx.data_ptr(),
+        w.data_ptr(), _stream(x)))
     return scores, idx, w
 
 

@@ -51,6 +51,62 @@ avey_status check_split_bf16(avey_dtype dt, int32_t S) {
     if (s_ != AVEY_OK) return s_;           \
   } while (0)
 
+// Bytes of the ranker workspace (normalised, padded copy of X), or a negative status.
+int64_t workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S) {
+  const int64_t eb = dt == AVEY_BF16 ? 2 : 4;
+  return B * splits(N, S) * S * d * eb;
+}
+
+// Checks of the ranker's first two stages (preparation and scoring) on the shape alone.
+avey_status check_rank_shape(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S, bool* empty) {
+  AVEY_TRY(check_common(dt, B, N, S, empty));
+  if (*empty) return AVEY_OK;
+  if (d < 1) return AVEY_ERR_SHAPE;
+  const int64_t n_s = splits(N, S);
+  if (n_s < 2) return AVEY_ERR_SHAPE;
+  AVEY_TRY(check_split_bf16(dt, S));
+  if (dt == AVEY_BF16) {
+    if (d % 64) return AVEY_ERR_UNSUPPORTED;
+    if (n_s * S * d >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // workspace byte offsets per sequence < 2^31
+    if (n_s * (n_s - 1) / 2 > kI32) return AVEY_ERR_UNSUPPORTED;
+  } else {
+    if (B * n_s * n_s > kI32) return AVEY_ERR_UNSUPPORTED;
+  }
+  if ((B * n_s * S + 15) / 16 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return AVEY_OK;
+}
+
+avey_status check_prepare(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
+                          const void* ws, bool* empty) {
+  AVEY_TRY(check_rank_shape(dt, B, N, d, S, empty));
+  if (*empty) return AVEY_OK;
+  if (!ws) return AVEY_ERR_NULL;
+  AVEY_TRY(check_tensor(x, dt, N, d, ld_x));
+  if (!aligned(ws, 16)) return AVEY_ERR_ALIGN;
+  return AVEY_OK;
+}
+
+avey_status check_scores(const void* ws, avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S,
+                         const float* scores, bool* empty) {
+  AVEY_TRY(check_rank_shape(dt, B, N, d, S, empty));
+  if (*empty) return AVEY_OK;
+  if (!ws || !scores) return AVEY_ERR_NULL;
+  if (!aligned(ws, 16) || !aligned(scores, 4)) return AVEY_ERR_ALIGN;
+  return AVEY_OK;
+}
+
+avey_status check_topk(const float* scores, int64_t B, int64_t n_s, int32_t k, const int32_t* idx, const float* w,
+                       bool* empty) {
+  if (B < 0 || n_s < 0) return AVEY_ERR_SHAPE;
+  *empty = (B == 0 || n_s == 0);
+  if (*empty) return AVEY_OK;
+  if (!scores || !idx || !w) return AVEY_ERR_NULL;
+  if (n_s < 2 || k < 1 || k > n_s - 1 || n_s > kI32) return AVEY_ERR_SHAPE;
+  if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
+  if ((B * n_s + 3) / 4 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return AVEY_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -70,50 +126,52 @@ const char* avey_status_str(int32_t s) {
   }
 }
 
-avey_status avey_maxsim_scores(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
-                               int32_t S, float* scores, float* rnorm, void* stream) {
+int64_t avey_rank_workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S) {
   bool empty = false;
-  AVEY_TRY(check_common(dt, B, N, S, &empty));
+  const avey_status st = check_rank_shape(dt, B, N, d, S, &empty);
+  if (st != AVEY_OK) return st;
+  return empty ? 0 : workspace_bytes(dt, B, N, d, S);
+}
+
+avey_status avey_maxsim_prepare(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
+                                int32_t S, void* workspace, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_prepare(x, dt, B, N, d, ld_x, S, workspace, &empty));
   if (empty) return AVEY_OK;
-  if (!scores || !rnorm) return AVEY_ERR_NULL;
-  AVEY_TRY(check_tensor(x, dt, N, d, ld_x));
-  const int64_t n_s = splits(N, S);
-  if (n_s < 2) return AVEY_ERR_SHAPE;
-  if (!aligned(scores, 4) || !aligned(rnorm, 4)) return AVEY_ERR_ALIGN;
-  AVEY_TRY(check_split_bf16(dt, S));
-  if ((B * N + 15) / 16 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_prepare(x, dt == AVEY_BF16, B, N, (int)d, ld_x, S, workspace,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+avey_status avey_maxsim_scores(const void* workspace, avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S,
+                               float* scores, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_scores(workspace, dt, B, N, d, S, scores, &empty));
+  if (empty) return AVEY_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (dt == AVEY_BF16) {
-    if (n_s * (n_s - 1) / 2 > kI32) return AVEY_ERR_UNSUPPORTED;
-    AVEY_TRY(hip_status(launch_rnorm(x, true, B, N, (int)d, ld_x, rnorm, st)));
-    return hip_status(launch_maxsim_bf16(static_cast<const uint16_t*>(x), rnorm, B, N, (int)d, ld_x, S, scores, st));
-  }
-  if (B * n_s * n_s > kI32) return AVEY_ERR_UNSUPPORTED;
-  AVEY_TRY(hip_status(launch_rnorm(x, false, B, N, (int)d, ld_x, rnorm, st)));
-  return hip_status(launch_maxsim_f32(static_cast<const float*>(x), B, N, (int)d, ld_x, S, scores, st));
+  if (dt == AVEY_BF16)
+    return hip_status(launch_maxsim_bf16(static_cast<const uint16_t*>(workspace), B, N, (int)d, S, scores, st));
+  return hip_status(launch_maxsim_f32(static_cast<const float*>(workspace), B, N, (int)d, S, scores, st));
 }
 
 avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t k, int32_t* idx, float* w,
                            void* stream) {
-  if (B < 0 || n_s < 0) return AVEY_ERR_SHAPE;
-  if (B == 0 || n_s == 0) return AVEY_OK;
-  if (!scores || !idx || !w) return AVEY_ERR_NULL;
-  if (n_s < 2 || k < 1 || k > n_s - 1 || n_s > kI32) return AVEY_ERR_SHAPE;
-  if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
-  if ((B * n_s + 3) / 4 > kI32) return AVEY_ERR_UNSUPPORTED;
+  bool empty = false;
+  AVEY_TRY(check_topk(scores, B, n_s, k, idx, w, &empty));
+  if (empty) return AVEY_OK;
   return hip_status(launch_topk_norm(scores, B, n_s, k, idx, w, reinterpret_cast<hipStream_t>(stream)));
 }
 
 avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
-                            int32_t k, float* scores, int32_t* idx, float* w, float* rnorm, void* stream) {
+                            int32_t k, void* workspace, float* scores, int32_t* idx, float* w, void* stream) {
+  // Every check of the three stages runs before the first launch.
   bool empty = false;
-  AVEY_TRY(check_common(dt, B, N, S, &empty));
+  AVEY_TRY(check_prepare(x, dt, B, N, d, ld_x, S, workspace, &empty));
   if (empty) return AVEY_OK;
-  if (!idx || !w) return AVEY_ERR_NULL;
+  AVEY_TRY(check_scores(workspace, dt, B, N, d, S, scores, &empty));
   const int64_t n_s = splits(N, S);
-  if (k < 1 || k > n_s - 1) return AVEY_ERR_SHAPE;
-  if (!aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
-  AVEY_TRY(avey_maxsim_scores(x, dt, B, N, d, ld_x, S, scores, rnorm, stream));
+  AVEY_TRY(check_topk(scores, B, n_s, k, idx, w, &empty));
+  AVEY_TRY(avey_maxsim_prepare(x, dt, B, N, d, ld_x, S, workspace, stream));
+  AVEY_TRY(avey_maxsim_scores(workspace, dt, B, N, d, S, scores, stream));
   return avey_topk_norm(scores, B, n_s, k, idx, w, stream);
 }
 

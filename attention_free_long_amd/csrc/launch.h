@@ -6,10 +6,10 @@
 
 namespace avey {
 
-hipError_t launch_rnorm(const void* x, bool bf16, int64_t B, int64_t N, int d, int64_t ld, float* rn,
-                        hipStream_t stream);
-hipError_t launch_maxsim_bf16(const uint16_t* x, const float* rn, int64_t B, int64_t N, int d, int64_t ld_x, int S,
-                              float* scores, hipStream_t stream);
+hipError_t launch_prepare(const void* x, bool bf16, int64_t B, int64_t N, int d, int64_t ld, int S, void* ws,
+                          hipStream_t stream);
+hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
+                              hipStream_t stream);
 hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, int32_t* idx, float* w,
                             hipStream_t stream);
 hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
@@ -18,8 +18,7 @@ hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, 
 hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps,
                            uint16_t* out, int64_t ld_out, hipStream_t stream);
 
-hipError_t launch_maxsim_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, float* scores,
-                             hipStream_t stream);
+hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S, float* scores, hipStream_t stream);
 hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                const int32_t* idx, const float* w, const float* P, int residual, float* xhat,
                                int64_t ld_out, hipStream_t stream);

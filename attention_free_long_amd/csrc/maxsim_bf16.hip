@@ -2,25 +2,24 @@
 //
 // MaxSim relevance of candidate split j to target split i is the sum over the tokens t of i of
 // the largest cosine between x_t and any token u of j (paperlayer.ai "Avey-B" summary,
-// section 3; papernotes.org Avey-B note, 方法详解/整体框架). Both directions of a split pair
-// come from the same dot-product tile C = X_i X_j^T:
-//   score(i <- j) = sum_t rn_t * max_u (C_tu * rn_u)      (row direction)
-//   score(j <- i) = sum_u rn_u * max_t (C_tu * rn_t)      (column direction)
-// with rn = 1 / |x| (0 for a zero vector; precomputed once per token), because rn_t >= 0
-// factors out of the max. So each unordered pair i < j is computed once for both directions,
-// and no token-by-token similarity ever leaves the chip.
+// section 3; papernotes.org Avey-B note, 方法详解/整体框架). The operands are the L2-normalised
+// tokens n_t = N(x_t) (papernotes.org Avey-B note, 关键设计 2), prepared once per call in a
+// split-packed bf16 copy (prepare.hip), so that an MFMA tile C = N(X_i) N(X_j)^T holds the
+// cosines themselves and both directions of the pair come from it:
+//   score(i <- j) = sum_t max_u C_tu          (row direction)
+//   score(j <- i) = sum_u max_t C_tu          (column direction)
+// Each unordered pair i < j is computed once, and no token-by-token similarity leaves the chip.
 //
-// Persistent grid, one workgroup per CU. Workgroups are dealt to the 8 XCDs round-robin; each
-// XCD owns one contiguous range of pair tiles, and its 32 workgroups walk that range 32 tiles at
-// a time, so concurrently resident tiles span about 4 target x 8 candidate splits and share
-// operands in the XCD's L2.
+// Units are 256 target rows x 256 candidate rows (one per pair at S = 256, four at S = 512).
+// One workgroup of 8 waves per CU (2 per SIMD), in a 2 x 4 grid: each wave owns 128 x 64 of the
+// fp32 accumulator (8 MFMA 32x32x16 blocks). Features stream through a 4-stage LDS ring in
+// chunks of 32 by direct global -> LDS copies, three chunks in flight while one is multiplied;
+// the next unit's first three chunks are copied while the current one finishes and during its
+// epilogue. The packed layout makes every copy instruction read 1 KiB of contiguous memory.
 //
-// A pair is processed in units of 256 target rows x 128 candidate rows (2 units per pair at
-// S = 256, 8 at S = 512); row maxima run across the units of a pair, column maxima across its
-// target blocks. Workgroup: 256 threads = 4 waves in a 2 x 2 grid, each wave owning 128 x 64 of
-// the fp32 accumulator (8 MFMA 32x32x16 blocks, 128 accumulator registers). Features stream
-// through LDS in chunks of 64 by direct global -> LDS copies, double-buffered; the next unit's
-// first chunk is copied during the current unit's last chunk.
+// Persistent grid: workgroups are dealt to the 8 XCDs round-robin; each XCD owns one contiguous
+// range of pair tiles, walked in bands of 4 target splits, so that the target operands of the
+// concurrently resident tiles stay in the XCD's L2 while candidates stream past.
 #include "avey_common.h"
 #include "launch.h"
 
@@ -28,17 +27,21 @@ namespace avey {
 
 namespace {
 
-constexpr int TA = 256;   // target rows per unit
-constexpr int TB = 128;   // candidate rows per unit
+constexpr int T = 256;    // rows per unit block (target and candidate)
+constexpr int KH = 32;    // K elements per chunk
+constexpr int RB = 64;    // bytes per LDS row (one chunk of one token)
+
+// 16-byte piece c of LDS row r sits at position c ^ ((r >> 2) & 3): an MFMA fragment read (16
+// consecutive rows, one piece each) then covers the 16 slots of a 256-byte bank window once.
+__device__ __forceinline__ uint32_t sw4(int r) { return (uint32_t)((r >> 2) & 3); }
 
 struct MaxsimParams {
-  const uint16_t* x;
-  const float* rn;
-  int64_t N, ld_x;
+  const uint16_t* xp;   // packed N(x): [B][n_s][d / 32][S][32] bf16, padding tokens zero
+  int64_t N;
   int d, S, n_s;
-  int qa, qb;      // 256-row target blocks and 128-row candidate blocks per split
-  int pairs;       // unordered pairs per sequence
-  int64_t tiles;   // B * pairs
+  int q;                // 256-row blocks per split
+  int pairs;            // unordered pairs per sequence
+  int64_t tiles;        // B * pairs
   float* scores;
 };
 
@@ -86,18 +89,23 @@ struct Unit {
   int i, j, ua, ub;   // pair and the unit's target / candidate block
 };
 
-__global__ void __launch_bounds__(256, 1) maxsim_bf16_kernel(MaxsimParams a) {
-  // Named stage buffers: separate LDS objects let the compiler see that reads of one stage do not
-  // depend on copies in flight into the other. sA1 doubles as the epilogue's row-max scratch.
-  __shared__ __align__(16) uint8_t sA0[TA * ROWB], sB0[TB * ROWB], sA1[TA * ROWB], sB1[TB * ROWB];
-  __shared__ __align__(16) float2 s_sbA[TA];   // per target row: (rn, 0), or (0, -inf) for padding
-  __shared__ __align__(16) float2 s_sbB[TB];   // per candidate row
-  __shared__ float s_cm[2][TB];                // column maxima of the two row halves
-  __shared__ float s_colmax[4 * TB];           // running column maxima over target blocks
+// This wave's copies except the newest n are complete, then a workgroup barrier: afterwards
+// every wave's older copies have landed in LDS and every wave is done with the previous stage.
+#define WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+__global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
+  // One LDS object per stage (target block, then candidate block): the compiler tracks copies
+  // per object, so reads of one stage do not wait for copies into another. Stage 3 doubles as
+  // the epilogue's row-max scratch.
+  __shared__ __align__(16) uint8_t st0[2 * T * RB], st1[2 * T * RB], st2[2 * T * RB], st3[2 * T * RB];
+  __shared__ __align__(16) float s_biA[T];   // per target row: 0, or -inf for a padding token
+  __shared__ float s_biB[T];                 // per candidate row
+  __shared__ float s_cm[2][T];               // column maxima of the two row halves
+  __shared__ float s_colmax[2 * T];          // running column maxima over target blocks (S = 512)
   __shared__ float s_red[8];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uniform(tid >> 6), wm = wave >> 1, wn = wave & 1;
+  const int wave = uniform(tid >> 6), wm = wave >> 2, wn = wave & 3;
 
   // ---- persistent work split: XCD x owns tiles [xs, xs + cnt); its workgroup l takes every
   // Gx-th of them starting at l.
@@ -108,10 +116,14 @@ __global__ void __launch_bounds__(256, 1) maxsim_bf16_kernel(MaxsimParams a) {
   int64_t t = l;
   if (t >= cnt) return;
 
-  const int nk = a.d / KC;
-  uint32_t fa[4], fb[4];
-  frag_offsets<SWZ_ROW>(fa, wm * 128, lane);
-  frag_offsets<SWZ_ROW>(fb, wn * 64, lane);
+  const int nk = a.d / KH;
+  uint32_t fa[2], fb[2];   // fragment offsets of the two k-steps of a chunk
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int ra = wm * 128 + (lane & 31), rb = wn * 64 + (lane & 31);
+    fa[ks] = (uint32_t)ra * RB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(ra)) << 4);
+    fb[ks] = (uint32_t)rb * RB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(rb)) << 4);
+  }
 
   auto tile_unit = [&](int64_t tl) {
     Unit u;
@@ -123,92 +135,84 @@ __global__ void __launch_bounds__(256, 1) maxsim_bf16_kernel(MaxsimParams a) {
     return u;
   };
 
-  // Copy addressing: scalar state per unit plus lane terms recomputed at every copy (laundered
-  // through an empty asm so they are not hoisted into long-lived registers). Wave w copies target
-  // rows [64w, 64w + 64) and candidate rows [32w, 32w + 32), 8 rows per instruction; lane l lands
-  // in chunk position (l & 7) of row (l >> 3) of the group, i.e. fetches the logical chunk
-  // (l & 7) ^ swz(row) with swz(row) = (row >> 1) & 7.
+  // Copy addressing: a descriptor over the unit's sequence and the byte offsets of its two
+  // blocks in chunk 0; chunk kc is kc * S * 64 bytes further.
   __amdgpu_buffer_rsrc_t xr;
-  int64_t rowA0 = 0, rowB0 = 0;   // first token of the unit's target / candidate block
-  int limA = 0, limB = 0;         // valid rows of those blocks
+  int limA = 0, limB = 0;      // valid (non-padding) rows of the unit's blocks
+  uint32_t pbA = 0, pbB = 0;
   auto set_unit = [&](const Unit& u) {
-    xr = make_rsrc(a.x + u.b * a.N * a.ld_x, (uint32_t)(a.N * a.ld_x * 2));
-    rowA0 = (int64_t)u.i * a.S + u.ua * TA;
-    rowB0 = (int64_t)u.j * a.S + u.ub * TB;
-    limA = (int)min((int64_t)min(a.S - u.ua * TA, TA), a.N - rowA0);
-    limB = (int)min((int64_t)min(a.S - u.ub * TB, TB), a.N - rowB0);
+    const int64_t seq = (int64_t)a.n_s * a.S * a.d;
+    xr = make_rsrc(a.xp + u.b * seq, (uint32_t)(seq * 2));
+    limA = (int)min((int64_t)min(a.S - u.ua * T, T), a.N - ((int64_t)u.i * a.S + u.ua * T));
+    limB = (int)min((int64_t)min(a.S - u.ub * T, T), a.N - ((int64_t)u.j * a.S + u.ub * T));
+    pbA = (uint32_t)((int64_t)u.i * a.S * a.d * 2 + u.ua * T * RB);
+    pbB = (uint32_t)((int64_t)u.j * a.S * a.d * 2 + u.ub * T * RB);
   };
-  // Copy chunk kc of the current copy unit; with valid == false every lane loads zeros.
-  auto dma = [&](int kc, uint8_t* dA, uint8_t* dB, bool valid) {
-    int sub = lane >> 3;
+  // Chunk kc of the current copy unit into stage st: wave w copies rows [32w, 32w + 32) of both
+  // blocks, 16 rows (1 KiB) per instruction, 4 instructions. Lane l lands at LDS row l >> 2,
+  // position l & 3, so it fetches the logical piece (l & 3) ^ sw4(row). Lane terms are
+  // recomputed per copy (laundered through an empty asm so they are not hoisted into long-lived
+  // registers). With valid == false every lane loads zeros.
+  auto dma = [&](int kc, uint8_t* st, bool valid) {
+    int sub = lane >> 2;
     asm volatile("" : "+v"(sub));
-    const uint32_t kb = (uint32_t)kc * KC * 2;
-    const uint32_t ldb = (uint32_t)a.ld_x * 2;
-    const uint32_t c0 = 16u * (uint32_t)((lane & 7) ^ (sub >> 1));
-    const uint32_t laneA = (uint32_t)sub * ldb + (uint32_t)(rowA0 * ldb);
-    const uint32_t laneB = (uint32_t)sub * ldb + (uint32_t)(rowB0 * ldb);
-    const int la = valid ? limA : 0, lb = valid ? limB : 0;
+    const uint32_t kb = (uint32_t)kc * (uint32_t)a.S * RB;
+    const uint32_t c = (uint32_t)sub * RB + 16u * (uint32_t)((lane & 3) ^ ((sub >> 2) & 3));
+    const uint32_t laneA = pbA + c, laneB = pbB + c;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int r0 = wave * 64 + n * 8;
-      const uint32_t c = (n & 1) ? (c0 ^ 64u) : c0;
-      dma16(xr, dA + r0 * ROWB, r0 + sub < la ? laneA + (uint32_t)r0 * ldb + c : OOB, kb);
-    }
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int r0 = wave * 32 + n * 8;
-      const uint32_t c = (n & 1) ? (c0 ^ 64u) : c0;
-      dma16(xr, dB + r0 * ROWB, r0 + sub < lb ? laneB + (uint32_t)r0 * ldb + c : OOB, kb);
+    for (int n = 0; n < 2; ++n) {
+      const int r0 = wave * 32 + n * 16;
+      dma16(xr, st + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
+      dma16(xr, st + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
     }
   };
 
   f32x16 acc[4][2];
-  // Fragments of k-step ks + 1 are read while the MFMAs of k-step ks run; scheduling barriers
-  // keep the compiler from hoisting more reads (and registers) than that.
-  auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+  // Both k-steps' fragments are read first, then the 16 MFMAs; the other wave on the SIMD
+  // covers the read latency.
+  auto compute = [&](const uint8_t* st) {
+    const uint8_t* sa = st;
+    const uint8_t* sb = st + T * RB;
     uint4 ra[2][4], rb[2][2];
-    auto fetch = [&](int ks, int slot) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) ra[slot][mb] = lds_read16(sa, fa[ks] + mb * 32 * ROWB);
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) rb[slot][nb] = lds_read16(sb, fb[ks] + nb * 32 * ROWB);
-    };
-    fetch(0, 0);
+      for (int mb = 0; mb < 4; ++mb) ra[ks][mb] = lds_read16(sa, fa[ks] + mb * 32 * RB);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int cur = ks & 1;
-      if (ks < 3) fetch(ks + 1, cur ^ 1);
+      for (int nb = 0; nb < 2; ++nb) rb[ks][nb] = lds_read16(sb, fb[ks] + nb * 32 * RB);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = mfma32(as_bf16x8(ra[cur][mb]), as_bf16x8(rb[cur][nb]), acc[mb][nb]);
+          acc[mb][nb] = mfma32(as_bf16x8(ra[ks][mb]), as_bf16x8(rb[ks][nb]), acc[mb][nb]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Row-max scratch in sA1: wave w owns [128 rows][16 lane pairs] fp32 (8 KB). After a pair-max
-  // across lanes 2p and 2p+1, the even lane stores the rows with (v & 1) == 0, the odd one the rest.
-  float* const scr = reinterpret_cast<float*>(sA1);
-
-  // Per-thread partial scores of the current pair: thread tid owns target row tid of the target
-  // block and (tid < 128) candidate column tid of the candidate block.
-  float rmax = 0.f, sr = 0.f, sc = 0.f;
+  // Thread tid < 256 owns target row tid of the unit, thread tid >= 256 candidate column
+  // tid - 256; part accumulates its share of the pair's score.
+  const bool is_row = tid < T;
+  const int own = tid & (T - 1);
+  float rmax = 0.f, part = 0.f;
 
   Unit cur = tile_unit(t);
   set_unit(cur);
-  dma(0, sA0, sB0, true);
-  copy_sync();
-  // An odd chunk count gets one zero chunk so that every unit starts on stage 0.
-  const int nk2 = (nk + 1) & ~1;
+  dma(0, st0, true);
+  dma(1, st1, 1 < nk);
+  dma(2, st2, 2 < nk);
+  // Chunk count padded to a multiple of 4 with zero chunks so that every unit starts on stage 0.
+  const int nk4 = (nk + 3) / 4 * 4;
 
   for (;;) {
     // ---- what comes after this unit: candidate blocks inner, target blocks outer, then tiles
     Unit nx = cur;
     bool has_next = true;
-    if (cur.ub + 1 < a.qb) {
+    if (cur.ub + 1 < a.q) {
       nx.ub = cur.ub + 1;
-    } else if (cur.ua + 1 < a.qa) {
+    } else if (cur.ua + 1 < a.q) {
       nx.ua = cur.ua + 1;
       nx.ub = 0;
     } else if (t + Gx < cnt) {
@@ -216,82 +220,122 @@ __global__ void __launch_bounds__(256, 1) maxsim_bf16_kernel(MaxsimParams a) {
     } else {
       has_next = false;
     }
-    const int64_t cb = cur.b, cA0 = rowA0, cB0 = rowB0;
     const int cLimA = limA, cLimB = limB;
+    const bool valid = own < (is_row ? cLimA : cLimB);
 
-    // ---- K loop over the features, two stages. The last copy of the loop is the next unit's
-    // first chunk, so no copy is in flight during the epilogue, and every copy is issued
-    // unconditionally (control-flow joins would make the compiler wait for all copies before
-    // the next LDS read).
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    for (int kc = 0; kc < nk2; kc += 2) {
-      dma(kc + 1, sA1, sB1, kc + 1 < nk);
-      compute(sA0, sB0);
-      copy_sync();
-      const bool last = kc + 2 >= nk2;
-      if (last && has_next) set_unit(nx);
-      dma(last ? 0 : kc + 2, sA0, sB0, !last || has_next);
-      compute(sA1, sB1);
-      copy_sync();
+    // ---- K loop. Every copy is issued unconditionally (a control-flow join around a copy
+    // makes the compiler drain all copies before the next LDS read) and every dma() issues
+    // exactly 4 copies per wave, so WAIT_KEEP(8) leaves exactly the two newer chunks in flight.
+    for (int kc = 0; kc + 4 < nk4; kc += 4) {
+      WAIT_KEEP(8);
+      dma(kc + 3, st3, kc + 3 < nk);
+      compute(st0);
+      WAIT_KEEP(8);
+      dma(kc + 4, st0, kc + 4 < nk);
+      compute(st1);
+      WAIT_KEEP(8);
+      dma(kc + 5, st1, kc + 5 < nk);
+      compute(st2);
+      WAIT_KEEP(8);
+      dma(kc + 6, st2, kc + 6 < nk);
+      compute(st3);
+    }
+    {
+      // last four chunks; the next unit's first three are copied meanwhile
+      const int kc = nk4 - 4;
+      WAIT_KEEP(8);
+      dma(kc + 3, st3, kc + 3 < nk);
+      compute(st0);
+      WAIT_KEEP(8);
+      if (has_next) set_unit(nx);
+      dma(0, st0, has_next);
+      compute(st1);
+      WAIT_KEEP(8);
+      dma(1, st1, has_next && 1 < nk);
+      compute(st2);
+      WAIT_KEEP(8);
+      dma(2, st2, has_next && 2 < nk);
+      compute(st3);
     }
 
-    // ---- epilogue (no copies in flight)
-    const bool vA = tid < cLimA;
-    const bool vB = tid < cLimB;            // false for tid >= TB
-    const float* rnb = a.rn + cb * a.N;
-    const float rA = vA ? rnb[cA0 + tid] : 0.f;
-    const float rB = vB ? rnb[cB0 + tid] : 0.f;
-    const bool first_ub = cur.ub == 0, last_ub = cur.ub == a.qb - 1;
-    const bool first_ua = cur.ua == 0, last_ua = cur.ua == a.qa - 1;
-    const int ubc = cur.ub;
-    s_sbA[tid] = make_float2(rA, vA ? 0.f : -INFINITY);
-    if (tid < TB) s_sbB[tid] = make_float2(rB, vB ? 0.f : -INFINITY);
-    lds_sync();
+    // ---- epilogue (the next unit's first three chunks are in flight into stages 0-2)
+    const bool first_ub = cur.ub == 0, last_ub = cur.ub == a.q - 1;
+    const bool first_ua = cur.ua == 0, last_ua = cur.ua == a.q - 1;
+    const bool full = cLimA == T && cLimB == T;   // no padding token in this unit
+    // (two stores to named arrays: a store through a selected pointer would make the compiler
+    // wait for the copies in flight)
+    if (is_row) s_biA[own] = valid ? 0.f : -INFINITY;
+    else s_biB[own] = valid ? 0.f : -INFINITY;
+    lds_sync();   // also: every wave is done reading stage 3
 
     // One pass over the accumulators, both directions:
-    //   column u: max over this wave's rows t of C_tu * rn_t (padding rows -> -inf)
-    //   row t:    max over this wave's 64 columns u of C_tu * rn_u -> scratch
-    float csc[2], cbi[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float2 s = s_sbB[wn * 64 + nb * 32 + (lane & 31)];
-      csc[nb] = s.x;
-      cbi[nb] = s.y;
-    }
-    const float2* sbA_lane = s_sbA + wm * 128 + (lane >> 5) * 4;
-    float* const wscr = scr + wave * (128 * 16) + ((lane & 31) >> 1);
-    const int par = lane & 1;
+    //   column u: max over this wave's 128 rows -> cm, then across the two row halves
+    //   row t:    max over this wave's 64 columns -> scratch [128 rows][8 lane quads] per wave
+    // A two-step transposing max across the 4 lanes of a quad leaves lane q with row e = q of
+    // each group of 4 rows, so each lane stores one value per group.
+    const int q = lane & 3, par = lane & 1, hi2 = (lane >> 1) & 1;
+    float* const wscr = reinterpret_cast<float*>(st3) + wave * (128 * 8) + ((lane & 31) >> 2);
     float cm[2] = {-INFINITY, -INFINITY};
+    auto reduce_store = [&](int mb, int g, const float (&m)[4]) {
+      // step 1, lanes l and l ^ 1: the even lane keeps rows e = 0, 2, the odd lane e = 1, 3
+      const float s0 = par ? m[0] : m[1], k0 = par ? m[1] : m[0];
+      const float s1 = par ? m[2] : m[3], k1 = par ? m[3] : m[2];
+      const float t0 = fmaxf(k0, __builtin_amdgcn_update_dpp(0.f, s0, 0xB1, 0xF, 0xF, false));
+      const float t1 = fmaxf(k1, __builtin_amdgcn_update_dpp(0.f, s1, 0xB1, 0xF, 0xF, false));
+      // step 2, lanes l and l ^ 2: keep row e = par (hi2 == 0) or e = par + 2 (hi2 == 1)
+      const float s2 = hi2 ? t0 : t1, k2 = hi2 ? t1 : t0;
+      const float f = fmaxf(k2, __builtin_amdgcn_update_dpp(0.f, s2, 0x4E, 0xF, 0xF, false));
+      wscr[(mb * 32 + g * 8 + (lane >> 5) * 4 + q) * 8] = f;
+    };
+    // Accumulator element v of block (mb, nb) in lane l: row mb*32 + 8(v >> 2) + 4(l >> 5) + (v & 3)
+    // of the wave's rows, column nb*32 + (l & 31) of its columns.
+    if (full) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 p01 = *reinterpret_cast<const float4*>(sbA_lane + mb * 32 + g * 8);
-        const float4 p23 = *reinterpret_cast<const float4*>(sbA_lane + mb * 32 + g * 8 + 2);
-        const float rsc[4] = {p01.x, p01.z, p23.x, p23.z};
-        const float rbi[4] = {p01.y, p01.w, p23.y, p23.w};
-        float m[4];
+        for (int g = 0; g < 4; ++g) {
+          float m[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float c0 = acc[mb][0][g * 4 + e], c1 = acc[mb][1][g * 4 + e];
-          m[e] = fmaxf(fmaf(c0, csc[0], cbi[0]), fmaf(c1, csc[1], cbi[1]));
-          cm[0] = fmaxf(cm[0], fmaf(c0, rsc[e], rbi[e]));
-          cm[1] = fmaxf(cm[1], fmaf(c1, rsc[e], rbi[e]));
-          // pair-max with the neighbouring lane (DPP quad_perm [1, 0, 3, 2])
-          m[e] = fmaxf(m[e], __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                 0, __builtin_bit_cast(int, m[e]), 0xB1, 0xF, 0xF, false)));
+          for (int e = 0; e < 4; ++e) {
+            const float c0 = acc[mb][0][g * 4 + e], c1 = acc[mb][1][g * 4 + e];
+            m[e] = fmaxf(c0, c1);
+            cm[0] = fmaxf(cm[0], c0);
+            cm[1] = fmaxf(cm[1], c1);
+          }
+          reduce_store(mb, g, m);
         }
-        // rows of this g-group: mb*32 + 8g + 4h + e; even lane stores e = 0, 2, odd lane e = 1, 3
-        const int rbase = mb * 32 + g * 8 + (lane >> 5) * 4;
-        wscr[(rbase + par) * 16] = par ? m[1] : m[0];
-        wscr[(rbase + 2 + par) * 16] = par ? m[3] : m[2];
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // padding tokens take part in neither the max nor the sum: bias them to -inf
+      float cbi[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) cbi[nb] = s_biB[wn * 64 + nb * 32 + (lane & 31)];
+      const float* biA_lane = s_biA + wm * 128 + (lane >> 5) * 4;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 rbi = *reinterpret_cast<const float4*>(biA_lane + mb * 32 + g * 8);
+          const float rb4[4] = {rbi.x, rbi.y, rbi.z, rbi.w};
+          float m[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float c0 = acc[mb][0][g * 4 + e], c1 = acc[mb][1][g * 4 + e];
+            m[e] = fmaxf(c0 + cbi[0], c1 + cbi[1]);
+            cm[0] = fmaxf(cm[0], c0 + rb4[e]);
+            cm[1] = fmaxf(cm[1], c1 + rb4[e]);
+          }
+          reduce_store(mb, g, m);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -299,42 +343,35 @@ __global__ void __launch_bounds__(256, 1) maxsim_bf16_kernel(MaxsimParams a) {
       if (lane < 32) s_cm[wm][wn * 64 + nb * 32 + lane] = m;
     }
     lds_sync();
-    {
-      // target row tid: the 16 + 16 pair maxima of waves (wr, 0) and (wr, 1)
-      const int wr = tid >> 7, rl = tid & 127;
-      const float* p0 = scr + (wr * 2 + 0) * (128 * 16) + rl * 16;
-      const float* p1 = scr + (wr * 2 + 1) * (128 * 16) + rl * 16;
+    if (is_row) {
+      // target row own: 8 quad maxima from each of the 4 waves that hold its columns
+      const int wr = own >> 7, rl = own & 127;
+      const float* p = reinterpret_cast<const float*>(st3) + wr * (4 * 128 * 8) + rl * 8;
       float m = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int cc = ((c + rl) & 3) * 4;
-        const float4 u = *reinterpret_cast<const float4*>(p0 + cc);
-        const float4 w = *reinterpret_cast<const float4*>(p1 + cc);
-        m = fmaxf(m, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
-        m = fmaxf(m, fmaxf(fmaxf(w.x, w.y), fmaxf(w.z, w.w)));
+      for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int cc = ((c + (rl >> 3)) & 1) * 4;   // rotation: no bank conflicts
+          const float4 u = *reinterpret_cast<const float4*>(p + w * (128 * 8) + cc);
+          m = fmaxf(m, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
+        }
       }
       rmax = first_ub ? m : fmaxf(rmax, m);
-      if (last_ub && vA) sr += rA * rmax;
-      if (tid < TB) {
-        float cmv = fmaxf(s_cm[0][tid], s_cm[1][tid]);
-        if (!first_ua) cmv = fmaxf(cmv, s_colmax[ubc * TB + tid]);
-        if (!last_ua) s_colmax[ubc * TB + tid] = cmv;
-        else if (vB) sc += rB * cmv;
-      }
+      if (last_ub && valid) part += rmax;
+    } else {
+      float cmv = fmaxf(s_cm[0][own], s_cm[1][own]);
+      if (!first_ua) cmv = fmaxf(cmv, s_colmax[cur.ub * T + own]);
+      if (!last_ua) s_colmax[cur.ub * T + own] = cmv;
+      else if (valid) part += cmv;
     }
 
     if (last_ua && last_ub) {
       // ---- scores of the pair; fixed reduction order (bitwise reproducible)
-      float r = sr, c = sc;
+      float r = part;
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        r += __shfl_xor(r, o);
-        c += __shfl_xor(c, o);
-      }
-      if (lane == 0) {
-        s_red[wave] = r;
-        s_red[4 + wave] = c;
-      }
+      for (int o = 32; o >= 1; o >>= 1) r += __shfl_xor(r, o);
+      if (lane == 0) s_red[wave] = r;
       lds_sync();
       if (tid == 0) {
         const float tr = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
@@ -347,39 +384,37 @@ __global__ void __launch_bounds__(256, 1) maxsim_bf16_kernel(MaxsimParams a) {
           if (cur.j == a.n_s - 1) sb[(int64_t)cur.j * a.n_s + cur.j] = -INFINITY;
         }
       }
-      sr = 0.f;
-      sc = 0.f;
+      part = 0.f;
     }
 
     if (!has_next) break;
     if (nx.ua == 0 && nx.ub == 0) t += Gx;
     cur = nx;
-    lds_sync();   // this epilogue's LDS reads are done before stage 1 is refilled
+    lds_sync();   // this epilogue's LDS reads are done before stage 3 is refilled
   }
+  wait_vmem();    // the zero-filled copies issued past the last unit land before the exit
 }
 
 }  // namespace
 
-hipError_t launch_maxsim_bf16(const uint16_t* x, const float* rn, int64_t B, int64_t N, int d, int64_t ld_x, int S,
-                              float* scores, hipStream_t stream) {
+hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
+                              hipStream_t stream) {
   MaxsimParams p;
-  p.x = x;
-  p.rn = rn;
+  p.xp = xp;
   p.N = N;
-  p.ld_x = ld_x;
   p.d = d;
   p.S = S;
   p.n_s = (int)((N + S - 1) / S);
-  p.qa = (S + TA - 1) / TA;
-  p.qb = (S + TB - 1) / TB;
+  p.q = (S + T - 1) / T;
   p.pairs = (int)((int64_t)p.n_s * (p.n_s - 1) / 2);
   p.tiles = B * (int64_t)p.pairs;
   p.scores = scores;
   int dev = 0, cus = 0;
-  hipGetDevice(&dev);
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
   const int64_t grid = p.tiles < cus ? p.tiles : cus;
-  hipLaunchKernelGGL(maxsim_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(maxsim_bf16_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

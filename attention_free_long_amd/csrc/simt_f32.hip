@@ -27,9 +27,10 @@ __device__ float norm_f32(const float* __restrict__ v, int n) {
   return sqrtf(s);
 }
 
-// One workgroup per ordered pair (b, i, j).
-__global__ void __launch_bounds__(256) maxsim_f32_kernel(const float* __restrict__ x, int64_t N, int d,
-                                                          int64_t ld_x, int S, int n_s, float* __restrict__ scores) {
+// One workgroup per ordered pair (b, i, j), over the normalised rows N(x) written by the
+// preparation pass ([B][n_s * S][d], padding rows zero): the cosine is a plain dot product.
+__global__ void __launch_bounds__(256) maxsim_f32_kernel(const float* __restrict__ xn, int64_t N, int d, int S,
+                                                          int n_s, float* __restrict__ scores) {
   __shared__ float red[4];
   const int64_t pr = blockIdx.x;
   const int j = (int)(pr % n_s);
@@ -40,21 +41,18 @@ __global__ void __launch_bounds__(256) maxsim_f32_kernel(const float* __restrict
     if (threadIdx.x == 0) *out = -INFINITY;
     return;
   }
-  const float* xb = x + b * N * ld_x;
+  const float* xb = xn + b * (int64_t)n_s * S * d;
   const int64_t ti0 = (int64_t)i * S, tj0 = (int64_t)j * S;
   const int ni = (int)min((int64_t)S, N - ti0), nj = (int)min((int64_t)S, N - tj0);
   float part = 0.f;
   for (int t = threadIdx.x; t < ni; t += 256) {
-    const float* xt = xb + (ti0 + t) * ld_x;
-    const float nt = norm_f32(xt, d);
+    const float* xt = xb + (ti0 + t) * d;
     float best = -INFINITY;
     for (int u = 0; u < nj; ++u) {
-      const float* xu = xb + (tj0 + u) * ld_x;
-      const float nu = norm_f32(xu, d);
+      const float* xu = xb + (tj0 + u) * d;
       float dot = 0.f;
       for (int c = 0; c < d; ++c) dot = fmaf(xt[c], xu[c], dot);
-      const float cs = (nt > 0.f && nu > 0.f) ? dot / (nt * nu) : 0.f;
-      best = fmaxf(best, cs);
+      best = fmaxf(best, dot);
     }
     part += best;
   }
@@ -125,11 +123,10 @@ __global__ void __launch_bounds__(256) dyn_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_maxsim_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, float* scores,
-                             hipStream_t stream) {
+hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S, float* scores, hipStream_t stream) {
   const int n_s = (int)((N + S - 1) / S);
   const int64_t grid = B * n_s * n_s;
-  hipLaunchKernelGGL(maxsim_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, N, d, ld_x, S, n_s, scores);
+  hipLaunchKernelGGL(maxsim_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, xn, N, d, S, n_s, scores);
   return hipGetLastError();
 }
 

@@ -23,6 +23,40 @@ METRIC = "tokens/sec for ranker+dynamic layer at N=32K; MaxSim MFMA util %"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attention_free_long_amd", "csrc")
+
+# HBM traffic of one launch of the dominant kernel, from two rocprofv3 --pmc passes (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch, averaged over the dispatches of the run) over this bench on
+# the named workload, each scaled by what the same counter reads for a plain 1 GiB device copy
+# (FETCH_SIZE read 524300 KiB for 1048576 KiB moved: x2.0; WRITE_SIZE read 1048576 KiB: x1.0).
+# Keyed by the digest of the kernel's sources: once they change the figures no longer apply and
+# traffic is reported as null until the counters are taken again.
+TRAFFIC = {
+    "maxsim": {
+        "sources": ("maxsim_bf16.hip", "avey_common.h"),
+        "measured": {
+            ("44c0357b8b3e9af7", "long"): {"fetch_kib": 1221973.3, "fetch_scale": 1.99995,
+                                           "write_kib": 252.5, "write_scale": 1.0},
+        },
+    },
+}
+
+
+def sources_digest(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(kernel: str, workload: str):
+    entry = TRAFFIC[kernel]
+    m = entry["measured"].get((sources_digest(entry["sources"]), workload))
+    if m is None:
+        return None
+    return int(round((m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]) * 1024))
 
 
 def algorithmic(cfg):
@@ -32,8 +66,11 @@ def algorithmic(cfg):
     eb = 2 if cfg.dtype == "bf16" else 4
     pairs = B * n_s * (n_s - 1) // 2
     return {
-        # one S x S x d tile per unordered split pair serves both directions
-        "maxsim": {"flop": 2.0 * S * S * d * pairs, "bytes": B * N * d * eb},
+        # read x once, write its normalised, padded copy once
+        "prepare": {"flop": 3.0 * B * N * d, "bytes": B * N * d * eb + B * n_s * S * d * eb},
+        # one S x S x d tile per unordered split pair serves both directions; reads the
+        # normalised copy once
+        "maxsim": {"flop": 2.0 * S * S * d * pairs, "bytes": B * n_s * S * d * eb},
         "topk": {"flop": 0.0, "bytes": B * n_s * n_s * 4 + 2 * B * n_s * k * 4},
         # read X_i and k retrieved splits, write Xhat_i; P once
         "compress": {"flop": 2.0 * B * n_s * S * d * (k + 1) * S,
@@ -93,10 +130,13 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times (the "
+                         "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +153,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return 0
     cfg = CONFIGS[args.config]
     inp = make_inputs(cfg)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -128,31 +177,32 @@ def main(argv=None):
     scores = torch.empty((B, n_s, n_s), device="cuda", dtype=torch.float32)
     idx = torch.empty((B, n_s, k), device="cuda", dtype=torch.int32)
     w = torch.empty((B, n_s, k), device="cuda", dtype=torch.float32)
-    rnorm = torch.empty((B, N), device="cuda", dtype=torch.float32)
+    ws = A.rank_workspace(x, S)
     xhat = torch.empty((B, N, cfg.d), device="cuda", dtype=dt)
     out = torch.empty((B, N, cfg.m_t), device="cuda", dtype=dt)
-    names = ("maxsim", "topk", "compress", "dyn")
+    names = ("prepare", "maxsim", "topk", "compress", "dyn")
+    calls = (
+        lambda: A.avey_maxsim_prepare(x, S, ws),
+        lambda: A.avey_maxsim_scores(ws, x, S, scores),
+        lambda: A.avey_topk_norm(scores, k, idx, w),
+        lambda: A.avey_select_compress(x, idx, w, P, S, residual=True, out=xhat),
+        lambda: A.avey_dyn_context(z_tail, S, cfg.eps, out=out),
+    )
 
     def step(ev=None):
+        # The events are recorded on torch's current stream, which is the stream every call
+        # enqueues its kernels on; each interval brackets exactly one library call.
+        for j, call in enumerate(calls):
+            if ev is not None:
+                ev[j].record()
+            call()
         if ev is not None:
-            ev[0].record()
-        A.avey_maxsim_scores(x, S, scores, rnorm)
-        if ev is not None:
-            ev[1].record()
-        A.avey_topk_norm(scores, k, idx, w)
-        if ev is not None:
-            ev[2].record()
-        A.avey_select_compress(x, idx, w, P, S, residual=True, out=xhat)
-        if ev is not None:
-            ev[3].record()
-        A.avey_dyn_context(z_tail, S, cfg.eps, out=out)
-        if ev is not None:
-            ev[4].record()
+            ev[len(calls)].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -179,7 +229,8 @@ def main(argv=None):
     ms_t = kern["maxsim"]["avg_us"] * 1e-6
     achieved = work["maxsim"]["flop"] / ms_t / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None}
+                "frac": round(achieved / peak, 4), "traffic": traffic_bytes("maxsim", cfg.name),
+                "traffic_unit": "bytes per launch"}
     comp_t = kern["compress"]["avg_us"] * 1e-6
     dyn_t = kern["dyn"]["avg_us"] * 1e-6
     result = {

@@ -11,7 +11,8 @@
  * General conventions (all entry points)
  *   - Every pointer argument except the status string is DEVICE memory owned by the caller.
  *     The library allocates nothing, keeps no state between calls, never synchronises and is
- *     safe to call from several host threads at once.
+ *     safe to call from several host threads at once (calls that share a workspace or an
+ *     output buffer must be ordered by the caller, e.g. by using one stream).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream). The call
  *     returns once the kernels are enqueued.
  *   - Return value: AVEY_OK, or an AVEY_ERR_* code. Argument checks run on the host before
@@ -65,23 +66,45 @@ int32_t avey_abi_version(void);
 const char* avey_status_str(int32_t status);
 
 /*
+ * Ranker workspace. The ranker first writes a normalised, zero-padded copy of X -- the
+ * "L2-normalised tiles" its MaxSim contraction reads -- into caller-provided device memory:
+ * n_t = N(x_t) = x_t / |x_t| (sum of squares in fp32; N(0) = 0) for t < N, zero rows for the
+ * padding tokens of the last split ([notes] 关键设计 2; 整体框架). Its layout is internal to
+ * the library (bf16: split-packed chunk planes of 32 features; fp32: row-major n_s * S rows).
+ *
+ * avey_rank_workspace_bytes -- size in bytes of that workspace for (dt, B, N, d, S):
+ * B * n_s * S * d * (2 for AVEY_BF16, 4 for AVEY_F32), 0 for empty work, or a negative
+ * avey_status if the shape is rejected (the same checks as avey_maxsim_prepare).
+ */
+int64_t avey_rank_workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S);
+
+/*
+ * avey_maxsim_prepare -- fill the workspace from x.
+ *   x          [B, N, d] row stride ld_x, dtype dt (input)
+ *   workspace  avey_rank_workspace_bytes(...) bytes, 16-byte aligned (output)
+ * For AVEY_BF16, n_t is rounded to bf16 (round to nearest even); for AVEY_F32 it stays fp32.
+ * Requires n_s >= 2.
+ */
+avey_status avey_maxsim_prepare(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
+                                int64_t ld_x, int32_t S, void* workspace, void* stream);
+
+/*
  * avey_maxsim_scores -- all-pairs split relevance ([summary] section 3: the ranker scores
- * every split against the target split with MaxSim; [notes] 整体框架).
+ * every split against the target split with MaxSim; [notes] 整体框架), from a workspace that
+ * avey_maxsim_prepare filled (enqueued earlier) for the same (dt, B, N, d, S).
  *
  *   scores[b, i, j] = sum over valid tokens t of split i of
- *                     max over valid tokens u of split j of cos(x_t, x_u),   for i != j
+ *                     max over valid tokens u of split j of n_t . n_u,     for i != j
  *   scores[b, i, i] = -INFINITY
- * cos(a, b) = a.b / (|a| |b|), and 0 when either vector is zero (N(0) = 0).
+ * n_t . n_u is the cosine of x_t and x_u (0 when either is zero). Padding tokens take part
+ * neither in the sum nor in the max. Dot products accumulate in fp32.
  *
- *   x       [B, N, d] row stride ld_x, dtype dt (input)
- *   scores  [B, n_s, n_s] float32, contiguous (output)
- *   rnorm   [B, N] float32, contiguous (output): rnorm[b, t] = 1 / |x_t|, 0 for a zero token --
- *           the scale of N(.) ([notes] 关键设计 2). Written first, then read by the scoring pass.
- * Requires n_s >= 2. MaxSim is not symmetric; both directions of each split pair come from
- * one pass over the pair.
+ *   workspace  (input, not modified)
+ *   scores     [B, n_s, n_s] float32, contiguous (output)
+ * MaxSim is not symmetric; both directions of each split pair come from one pass over the pair.
  */
-avey_status avey_maxsim_scores(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
-                               int64_t ld_x, int32_t S, float* scores, float* rnorm, void* stream);
+avey_status avey_maxsim_scores(const void* workspace, avey_dtype dt, int64_t B, int64_t N,
+                               int64_t d, int32_t S, float* scores, void* stream);
 
 /*
  * avey_topk_norm -- top-k selection and divide-by-max weighting ([notes] 整体框架: the ranker
@@ -102,13 +125,14 @@ avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t 
                            int32_t* idx, float* w, void* stream);
 
 /*
- * avey_split_rank -- avey_maxsim_scores followed by avey_topk_norm on the same stream.
- *   outputs scores [B, n_s, n_s], idx [B, n_s, k], w [B, n_s, k], rnorm [B, N] as described
- *   above.
+ * avey_split_rank -- avey_maxsim_prepare, avey_maxsim_scores and avey_topk_norm on the same
+ * stream. Every argument check of the three runs before the first launch.
+ *   workspace  avey_rank_workspace_bytes(...) bytes, 16-byte aligned (scratch; overwritten)
+ *   outputs scores [B, n_s, n_s], idx [B, n_s, k], w [B, n_s, k] as described above.
  */
 avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
-                            int64_t ld_x, int32_t S, int32_t k, float* scores, int32_t* idx,
-                            float* w, float* rnorm, void* stream);
+                            int64_t ld_x, int32_t S, int32_t k, void* workspace, float* scores,
+                            int32_t* idx, float* w, void* stream);
 
 /*
  * avey_select_compress -- weighted gather and neural compression ([notes] 关键设计 4, eq. 8;

@@ -44,7 +44,7 @@ def test_status_strings(lib):
 
 def test_split_rank_validation(lib):
     f = lib.avey_split_rank
-    # (x, dt, B, N, d, ld, S, k, scores, idx, w, rnorm, stream)
+    # (x, dt, B, N, d, ld, S, k, workspace, scores, idx, w, stream)
     assert f(P16, 7, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == DTYPE
     assert f(P16, 1, -1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == SHAPE
     assert f(P16, 1, 1, 1024, 64, 64, 0, 3, P16, P16, P16, P16, None) == SHAPE
@@ -52,7 +52,8 @@ def test_split_rank_validation(lib):
     assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None, None) == OK       # B == 0: no work
     assert f(None, 1, 1, 0, 64, 64, 64, 3, None, None, None, None, None) == OK          # N == 0: no work
     assert f(None, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == NULL
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, P16, None) == NULL         # no workspace
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, None, P16, P16, None) == NULL
     assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, P16, None) == SHAPE        # k > n_s - 1
     assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, P16, None) == SHAPE
     assert f(P16, 1, 1, 64, 64, 64, 64, 1, P16, P16, P16, P16, None) == SHAPE           # a single split
@@ -60,9 +61,37 @@ def test_split_rank_validation(lib):
     assert f(P16, 1, 1, 1024, 96, 96, 64, 3, P16, P16, P16, P16, None) == UNSUP         # bf16 d % 64
     assert f(P16, 1, 1, 1024, 64, 68, 64, 3, P16, P16, P16, P16, None) == ALIGN         # bf16 ld % 8
     assert f(P4, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == ALIGN          # bf16 x alignment
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P4, P16, P16, P16, None) == ALIGN          # workspace alignment
     assert f(P16, 1, 1, 1000, 64, 64, 100, 3, P16, P16, P16, P16, None) == UNSUP        # bf16 S % 64
-    assert f(P16, 0, 1, 1000, 64, 64, 64, 3, P16, P16 + 2, P16, P16, None) == ALIGN     # idx alignment
+    assert f(P16, 0, 1, 1000, 64, 64, 64, 3, P16, P16, P16 + 2, P16, None) == ALIGN     # idx alignment
     assert f(P16, 1, 1, 1 << 25, 64, 64, 256, 3, P16, P16, P16, P16, None) == UNSUP     # > 2^30 elements
+
+
+def test_workspace_prepare_and_scores_validation(lib):
+    n = lib.avey_rank_workspace_bytes
+    assert n(1, 2, 32768, 768, 256) == 2 * 128 * 256 * 768 * 2
+    assert n(0, 1, 1000, 64, 64) == 1 * 16 * 64 * 64 * 4                # padded to whole splits
+    assert n(1, 0, 1000, 64, 64) == 0
+    assert n(1, 1, 1000, 64, 100) == UNSUP
+    assert n(9, 1, 1000, 64, 64) == DTYPE
+    assert n(1, 1, 64, 64, 64) == SHAPE                                  # a single split
+    p = lib.avey_maxsim_prepare
+    # (x, dt, B, N, d, ld, S, workspace, stream)
+    assert p(None, 1, 0, 1024, 64, 64, 64, None, None) == OK
+    assert p(P16, 1, 1, 1024, 64, 64, 64, None, None) == NULL
+    assert p(None, 1, 1, 1024, 64, 64, 64, P16, None) == NULL
+    assert p(P16, 1, 1, 1024, 64, 32, 64, P16, None) == SHAPE
+    assert p(P16, 1, 1, 1024, 64, 64, 64, P4, None) == ALIGN
+    assert p(P16, 1, 1, 1024, 96, 96, 64, P16, None) == UNSUP
+    m = lib.avey_maxsim_scores
+    # (workspace, dt, B, N, d, S, scores, stream)
+    assert m(None, 1, 1, 0, 64, 64, None, None) == OK
+    assert m(None, 1, 1, 1024, 64, 64, P16, None) == NULL
+    assert m(P16, 1, 1, 1024, 64, 64, None, None) == NULL
+    assert m(P16, 1, 1, 64, 64, 64, P16, None) == SHAPE                  # a single split
+    assert m(P16, 1, 1, 1024, 64, 96, P16, None) == UNSUP                # bf16 S % 64
+    assert m(P16, 1, 1, 1024, 96, 64, P16, None) == UNSUP                # bf16 d % 64
+    assert m(P16, 0, 1, 1024, 64, 64, P16 + 1, None) == ALIGN
 
 
 def test_topk_validation(lib):

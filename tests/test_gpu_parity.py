@@ -168,3 +168,31 @@ def test_full_size_sampled(gpu_ok, name):
     assert (idx >= 0).all() and (idx < n_s).all()
     assert not (idx == np.arange(n_s)[None, :, None]).any()
     assert np.isfinite(g["xhat"]).all() and np.isfinite(g["out"]).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prepare_normalises_and_pads(gpu_ok, dtype):
+    """The ranker workspace holds the oracle's N(x) (bf16: rounded, in split-packed chunk
+    planes; fp32: row-major) and zero rows for the padding tokens of the last split."""
+    cfg = Config("prep_" + dtype, B=2, N=1000, d=128, S=64, k=2, m_t=64, m=128, dtype=dtype,
+                 x_dist="mixture", n_centroids=8)
+    inp = make_inputs(cfg)
+    say(f"maxsim_prepare {dtype} B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S}")
+    x, _, _, _ = upload(inp)
+    x[1, 17].zero_()
+    ws = A.avey_maxsim_prepare(x, cfg.S)
+    torch.cuda.synchronize()
+    n_s, S, d = cfg.n_s, cfg.S, cfg.d
+    if dtype == "bf16":
+        got = ws[: cfg.B * n_s * S * d * 2].view(torch.bfloat16).float()
+        got = got.reshape(cfg.B, n_s, d // 32, S, 32).permute(0, 1, 3, 2, 4).reshape(cfg.B, n_s * S, d)
+    else:
+        got = ws[: cfg.B * n_s * S * d * 4].view(torch.float32).reshape(cfg.B, n_s * S, d)
+    got = got.cpu().numpy().astype(np.float64)
+    xs = host_f64(x)
+    assert np.all(got[:, cfg.N:] == 0.0)
+    assert np.all(got[1, 17] == 0.0)
+    rel = 2.0 ** -8 if dtype == "bf16" else 1e-6
+    for b in range(cfg.B):
+        ref = O.unit_rows(xs[b])
+        assert np.all(np.abs(got[b, : cfg.N] - ref) <= rel * np.abs(ref) + 1e-7)
