@@ -15,7 +15,9 @@ namespace avey {
 
 namespace {
 
-// 16 lanes per token row; rows t >= N of the last split are written as zeros.
+// 16 lanes per token row; rows t >= N of the last split are written as zeros. Rows of up to
+// 16 * 8 * RP features are read once and kept in registers between the norm and the scaling.
+template <int RP>
 __global__ void __launch_bounds__(256) prepare_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows_p, int64_t N,
                                                             int d, int64_t ld, int S, int n_s,
                                                             uint16_t* __restrict__ xp) {
@@ -26,9 +28,16 @@ __global__ void __launch_bounds__(256) prepare_bf16_kernel(const uint16_t* __res
   const bool live = r < rows_p;
   const bool valid = live && tp < N;
   const uint16_t* row = x + (b * N + (valid ? tp : 0)) * ld;
+  uint4 v[RP];
   float s = 0.f;
-  if (valid)
-    for (int c = lane16 * 8; c < d; c += 128) s = sumsq8(*reinterpret_cast<const uint4*>(row + c), s);
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int c = lane16 * 8 + p * 128;
+    v[p] = (valid && c < d) ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0);
+    s = sumsq8(v[p], s);
+  }
+  for (int c = lane16 * 8 + RP * 128; c < d; c += 128)   // rows wider than the register tile
+    if (valid) s = sumsq8(*reinterpret_cast<const uint4*>(row + c), s);
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
   const float rn = s > 0.f ? 1.0f / sqrtf(s) : 0.f;
@@ -36,18 +45,22 @@ __global__ void __launch_bounds__(256) prepare_bf16_kernel(const uint16_t* __res
   const int j = (int)(tp / S), slot = (int)(tp % S);
   const int nkc = d / 32;
   uint16_t* dst = xp + ((b * n_s + j) * (int64_t)nkc * S + slot) * 32;
-  for (int c = lane16 * 8; c < d; c += 128) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (valid) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + c);
-      v.x = pack_bf16(bf16lo(u.x) * rn, bf16hi(u.x) * rn);
-      v.y = pack_bf16(bf16lo(u.y) * rn, bf16hi(u.y) * rn);
-      v.z = pack_bf16(bf16lo(u.z) * rn, bf16hi(u.z) * rn);
-      v.w = pack_bf16(bf16lo(u.w) * rn, bf16hi(u.w) * rn);
-    }
+  auto put = [&](int c, uint4 u) {
+    uint4 o;
+    o.x = pack_bf16(bf16lo(u.x) * rn, bf16hi(u.x) * rn);
+    o.y = pack_bf16(bf16lo(u.y) * rn, bf16hi(u.y) * rn);
+    o.z = pack_bf16(bf16lo(u.z) * rn, bf16hi(u.z) * rn);
+    o.w = pack_bf16(bf16lo(u.w) * rn, bf16hi(u.w) * rn);
     // feature c lives in chunk c / 32 at position c % 32 of the token's 32-element row
-    *reinterpret_cast<uint4*>(dst + (int64_t)(c >> 5) * S * 32 + (c & 31)) = v;
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c >> 5) * S * 32 + (c & 31)) = o;
+  };
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int c = lane16 * 8 + p * 128;
+    if (c < d) put(c, v[p]);
   }
+  for (int c = lane16 * 8 + RP * 128; c < d; c += 128)
+    put(c, valid ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0));
 }
 
 __global__ void __launch_bounds__(256) prepare_f32_kernel(const float* __restrict__ x, int64_t rows_p, int64_t N,
@@ -79,7 +92,7 @@ hipError_t launch_prepare(const void* x, bool bf16, int64_t B, int64_t N, int d,
   const int64_t rows_p = B * n_s * (int64_t)S;
   const unsigned blocks = (unsigned)((rows_p + 15) / 16);
   if (bf16)
-    hipLaunchKernelGGL(prepare_bf16_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+    hipLaunchKernelGGL(prepare_bf16_kernel<8>, dim3(blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(x),
                        rows_p, N, d, ld, S, n_s, static_cast<uint16_t*>(ws));
   else
     hipLaunchKernelGGL(prepare_f32_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const float*>(x), rows_p,

@@ -5,7 +5,7 @@
 // One wave per score row. Candidates are ordered by (score descending, index ascending), NaN
 // ordering as -inf. Round r picks the best candidate strictly after the round r-1 winner in
 // that total order, so no "taken" set is needed: every lane scans its strided share of the
-// row, then a 6-step butterfly (ds_swizzle-free shuffles) finds the wave's best.
+// row, then a 6-step butterfly of cross-lane shuffles finds the wave's best.
 #include "avey_common.h"
 #include "launch.h"
 

@@ -54,6 +54,7 @@ def check_score_row(g_row: np.ndarray, o_row: np.ndarray, i: int, tol: float):
     mask = np.arange(len(o_row)) != i
     rel = np.abs(g_row[mask] - o_row[mask]) / np.abs(o_row[mask])
     assert rel.max() <= tol, f"score rel err {rel.max():.3e} > {tol}"
+    return float(rel.max())
 
 
 def check_topk_row(g_idx, g_w, o_row, o_idx, gap, i, k, tol_w):

@@ -65,19 +65,23 @@ def test_small_full_parity(gpu_ok, name):
     x64 = inp.x_f64()
     n_s = cfg.n_s
     ranked = O.split_rank(x64, cfg.S, cfg.k)
+    worst = {"scores": 0.0, "xhat": 0.0, "out": 0.0}
     for (b, i), (o_row, o_idx, o_w, gap) in ranked.items():
-        check_score_row(g["scores"][b, i], o_row, i, tol["scores"])
+        worst["scores"] = max(worst["scores"], check_score_row(g["scores"][b, i], o_row, i, tol["scores"]))
         check_topk_row(g["idx"][b, i], g["w"][b, i], o_row, o_idx, gap, i, cfg.k, tol["w"])
     # compression on the GPU's own idx / w (independent of tie effects)
     comp = O.select_compress(x64, cfg.S, g["idx"], g["w"].astype(np.float64), inp.P_f64(), residual=True)
     for (b, i), rows in comp.items():
         err = row_rel_err(g["xhat"][b, split_rows_of(cfg.N, cfg.S, i)], rows)
         assert err <= tol["out"], f"xhat split {(b, i)}: {err:.3e}"
+        worst["xhat"] = max(worst["xhat"], err)
     dyn = O.dyn_context(inp.z_tail_f64(), cfg.S, cfg.eps)
     for (b, i), rows in dyn.items():
         err = row_rel_err(g["out"][b, split_rows_of(cfg.N, cfg.S, i)], rows)
         assert err <= tol["out"], f"dyn split {(b, i)}: {err:.3e}"
+        worst["out"] = max(worst["out"], err)
     assert n_s == g["scores"].shape[1]
+    say(f"{name}: worst relative errors " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
 
 
 def test_residual_off_and_k_max(gpu_ok):
@@ -148,10 +152,11 @@ def test_full_size_sampled(gpu_ok, name):
     g = run_all(inp)
     rows = FULL_SAMPLES[name]
     x64_b = {b: inp.x_f64(b) for b in {b for b, _ in rows}}
+    worst = 0.0
     for b, i in rows:
         o_row = O.score_row(x64_b[b], cfg.S, i)
         o_idx, _, _, gap = O.top_k(o_row, i, cfg.k)
-        check_score_row(g["scores"][b, i], o_row, i, tol["scores"])
+        worst = max(worst, check_score_row(g["scores"][b, i], o_row, i, tol["scores"]))
         check_topk_row(g["idx"][b, i], g["w"][b, i], o_row, o_idx, gap, i, cfg.k, tol["w"])
         ref = O.compress_split(x64_b[b], cfg.S, g["idx"][b, i], g["w"][b, i].astype(np.float64), inp.P_f64(), i)
         err = row_rel_err(g["xhat"][b, split_rows_of(cfg.N, cfg.S, i)], ref)
@@ -160,6 +165,7 @@ def test_full_size_sampled(gpu_ok, name):
         ref = O.dyn_context_split(zt, cfg.S, cfg.eps, 0)
         err = row_rel_err(g["out"][b, split_rows_of(cfg.N, cfg.S, i)], ref)
         assert err <= tol["out"], f"dyn {(b, i)}: {err:.3e}"
+    say(f"{name}: worst score relative error on the sampled rows {worst:.2e}")
     # properties that hold everywhere: w0 == 1, weights in (0, 1], indices valid and not self
     w = g["w"]
     assert (w[..., 0] == 1.0).all() and (w > 0).all() and (w <= 1).all()
