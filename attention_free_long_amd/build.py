@@ -31,6 +31,14 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# Per-source additions. The MaxSim epilogue is a long chain of maxima over finite values: with
+# the IEEE mode bit off (which needs relaxed NaN handling) v_max_f32 takes its operands as they
+# are, so the compiler neither inserts a canonicalising v_max before each one nor splits the
+# DPP-fed maxima into a move plus a max. NaN inputs give unspecified scores.
+SOURCE_FLAGS = {
+    "maxsim_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -61,7 +69,7 @@ def build(jobs: int | None = None, verbose: bool = False, extra_flags=()) -> str
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *flags, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:

@@ -13,7 +13,8 @@
 // Units are 256 target rows x 256 candidate rows (one per pair at S = 256, four at S = 512).
 // One workgroup of 8 waves per CU (2 per SIMD), in a 2 x 4 grid: each wave owns 128 x 64 of the
 // fp32 accumulator (8 MFMA 32x32x16 blocks). Features stream through a 4-stage LDS ring in
-// chunks of 32 by direct global -> LDS copies, three chunks in flight while one is multiplied;
+// chunks of 32 by direct global -> LDS copies, three chunks in flight while one is multiplied
+// (the copies of a chunk are issued between the MFMA groups of the chunk being multiplied);
 // the next unit's first three chunks are copied while the current one finishes and during its
 // epilogue. The packed layout makes every copy instruction read 1 KiB of contiguous memory.
 //
@@ -168,27 +169,42 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   };
 
   f32x16 acc[4][2];
-  // Both k-steps' fragments are read first, then the 16 MFMAs; the other wave on the SIMD
-  // covers the read latency.
-  auto compute = [&](const uint8_t* st) {
+  // One chunk of MFMAs from stage st, with the 4 copies of chunk kc into stage dst spread
+  // between its four MFMA groups, and the second k-step's fragments read behind the first
+  // group: copies landing in LDS then compete less with the fragment reads, which measured
+  // 6-7 % faster than issuing all reads and copies up front.
+  auto compute_copy = [&](const uint8_t* st, int kc, uint8_t* dst, bool valid) {
     const uint8_t* sa = st;
     const uint8_t* sb = st + T * RB;
     uint4 ra[2][4], rb[2][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    auto fetch = [&](int ks) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) ra[ks][mb] = lds_read16(sa, fa[ks] + mb * 32 * RB);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) rb[ks][nb] = lds_read16(sb, fb[ks] + nb * 32 * RB);
-    }
+    };
+    fetch(0);
+    int sub = lane >> 2;
+    asm volatile("" : "+v"(sub));
+    const uint32_t kb = (uint32_t)kc * (uint32_t)a.S * RB;
+    const uint32_t c = (uint32_t)sub * RB + 16u * (uint32_t)((lane & 3) ^ ((sub >> 2) & 3));
+    const uint32_t laneA = pbA + c, laneB = pbB + c;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = mfma32(as_bf16x8(ra[ks][mb]), as_bf16x8(rb[ks][nb]), acc[mb][nb]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = mfma32(as_bf16x8(ra[ks][mb]), as_bf16x8(rb[ks][nb]), acc[mb][nb]);
+        if (ks == 0 && h == 0) fetch(1);
+        // copy (block h, 16-row group ks) of this wave's rows, as dma() orders them
+        const int r0 = wave * 32 + ks * 16;
+        if (h == 0) dma16(xr, dst + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
+        else dma16(xr, dst + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -230,38 +246,30 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
     // ---- K loop. Every copy is issued unconditionally (a control-flow join around a copy
-    // makes the compiler drain all copies before the next LDS read) and every dma() issues
-    // exactly 4 copies per wave, so WAIT_KEEP(8) leaves exactly the two newer chunks in flight.
+    // makes the compiler drain all copies before the next LDS read) and every chunk is exactly
+    // 4 copies per wave, so WAIT_KEEP(8) leaves exactly the two newer chunks in flight.
     for (int kc = 0; kc + 4 < nk4; kc += 4) {
       WAIT_KEEP(8);
-      dma(kc + 3, st3, kc + 3 < nk);
-      compute(st0);
+      compute_copy(st0, kc + 3, st3, kc + 3 < nk);
       WAIT_KEEP(8);
-      dma(kc + 4, st0, kc + 4 < nk);
-      compute(st1);
+      compute_copy(st1, kc + 4, st0, kc + 4 < nk);
       WAIT_KEEP(8);
-      dma(kc + 5, st1, kc + 5 < nk);
-      compute(st2);
+      compute_copy(st2, kc + 5, st1, kc + 5 < nk);
       WAIT_KEEP(8);
-      dma(kc + 6, st2, kc + 6 < nk);
-      compute(st3);
+      compute_copy(st3, kc + 6, st2, kc + 6 < nk);
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
       WAIT_KEEP(8);
-      dma(kc + 3, st3, kc + 3 < nk);
-      compute(st0);
+      compute_copy(st0, kc + 3, st3, kc + 3 < nk);
       WAIT_KEEP(8);
       if (has_next) set_unit(nx);
-      dma(0, st0, has_next);
-      compute(st1);
+      compute_copy(st1, 0, st0, has_next);
       WAIT_KEEP(8);
-      dma(1, st1, has_next && 1 < nk);
-      compute(st2);
+      compute_copy(st2, 1, st1, has_next && 1 < nk);
       WAIT_KEEP(8);
-      dma(2, st2, has_next && 2 < nk);
-      compute(st3);
+      compute_copy(st3, 2, st2, has_next && 2 < nk);
     }
 
     // ---- epilogue (the next unit's first three chunks are in flight into stages 0-2)

@@ -33,10 +33,10 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attention_free_
 # traffic is reported as null until the counters are taken again.
 TRAFFIC = {
     "maxsim": {
-        "sources": ("maxsim_bf16.hip", "avey_common.h"),
+        "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("44c0357b8b3e9af7", "long"): {"fetch_kib": 1221973.3, "fetch_scale": 1.99995,
-                                           "write_kib": 252.5, "write_scale": 1.0},
+            ("42c3f7e77f57cebd", "long"): {"fetch_kib": 1221263.6, "fetch_scale": 1.99995,
+                                           "write_kib": 253.8, "write_scale": 1.0},
         },
     },
 }

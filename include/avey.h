@@ -97,7 +97,8 @@ avey_status avey_maxsim_prepare(const void* x, avey_dtype dt, int64_t B, int64_t
  *                     max over valid tokens u of split j of n_t . n_u,     for i != j
  *   scores[b, i, i] = -INFINITY
  * n_t . n_u is the cosine of x_t and x_u (0 when either is zero). Padding tokens take part
- * neither in the sum nor in the max. Dot products accumulate in fp32.
+ * neither in the sum nor in the max. Dot products accumulate in fp32. x must be finite: with a
+ * NaN or infinite token the scores are unspecified.
  *
  *   workspace  (input, not modified)
  *   scores     [B, n_s, n_s] float32, contiguous (output)
