@@ -191,6 +191,7 @@ avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dt == AVEY_BF16) {
     if (!aligned(P, 16)) return AVEY_ERR_ALIGN;
+    if (k + 1 > kCompressMaxBlocks) return AVEY_ERR_UNSUPPORTED;
     const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * ((d + 255) / 256);
     if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
     return hip_status(launch_compress_bf16(static_cast<const uint16_t*>(x), B, N, (int)d, ld_x, S, k, idx, w,

@@ -202,3 +202,30 @@ def test_prepare_normalises_and_pads(gpu_ok, dtype):
     for b in range(cfg.B):
         ref = O.unit_rows(xs[b])
         assert np.all(np.abs(got[b, : cfg.N] - ref) <= rel * np.abs(ref) + 1e-7)
+
+
+@pytest.mark.parametrize("weights", ["positive", "zero_and_negative"])
+def test_compress_given_weights(gpu_ok, weights):
+    """select_compress on caller-given idx / w, including a zero and a negative weight (divide-
+    by-max of non-positive scores, read as written) and weights above 1."""
+    cfg = SMALL["small_bf16"]
+    inp = make_inputs(cfg)
+    say(f"select_compress given weights ({weights})")
+    x, P, _, _ = upload(inp)
+    rng = np.random.default_rng(7)
+    B, n_s, k = cfg.B, cfg.n_s, cfg.k
+    idx = np.stack([rng.permutation(n_s)[:k] for _ in range(B * n_s)]).reshape(B, n_s, k).astype(np.int32)
+    w = rng.uniform(0.05, 3.0, size=(B, n_s, k)).astype(np.float32)
+    if weights == "zero_and_negative":
+        w[0, 1, 1] = 0.0
+        w[1, 2, 0] = -0.75
+    g = A.avey_select_compress(x, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), P, cfg.S)
+    torch.cuda.synchronize()
+    got = host_f64(g)
+    ref = O.select_compress(inp.x_f64(), cfg.S, idx, w.astype(np.float64), inp.P_f64(), residual=True)
+    worst = 0.0
+    for (b, i), rows in ref.items():
+        err = row_rel_err(got[b, split_rows_of(cfg.N, cfg.S, i)], rows)
+        assert err <= TOL["bf16"]["out"], f"xhat split {(b, i)}: {err:.3e}"
+        worst = max(worst, err)
+    say(f"given weights ({weights}): worst xhat error {worst:.2e}")
