@@ -285,6 +285,247 @@ __global__ void __launch_bounds__(256, 1) dyn_bf16_kernel(DynParams a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// S <= 256: one 8-wave workgroup per split, both GEMMs fed by one 4-stage ring of 32 KiB
+// direct-copy stages (three chunks in flight while one is multiplied).
+//   Phase 1, chunk kc: Z rows q = 0..255 x features 64 kc .. +63 (128-byte LDS rows). Wave w
+//   owns p = 32 w .. 32 w + 31: C1[q][p] over all 256 q (8 MFMA blocks); the squared norms of
+//   its p rows come from the B fragments it reads anyway.
+//   Phase 2, chunk (ft, qc): Z rows q = 64 qc .. +63 x features 256 ft .. +255 (512-byte LDS
+//   rows), read as Z^T fragments by the LDS transpose read, times the G fragments the wave
+//   holds in registers: O^T[f][p] for 256 features x its 32 p.
+// The phase-2 chunks stream without waiting for phase 1's result: only their products do.
+namespace ring {
+
+constexpr int QR = 256;                 // q rows per split (padded)
+constexpr int STAGE = QR * ROWB;        // 32 KiB: phase 1 chunk (256 x 64 features)
+constexpr int ZB = 512;                 // phase 2 LDS row: 256 features
+constexpr int FT = 256;                 // phase 2 features per tile
+
+__device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* base, uint32_t off) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+#define DYN_WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+__global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
+  __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+  __shared__ float s_sq[QR];
+  __shared__ __align__(16) float s_rn[QR];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+
+  const int64_t split = xcd_remap(blockIdx.x, a.tiles);
+  const int64_t b = split / a.n_s;
+  const int i = (int)(split % a.n_s);
+  const int64_t base = (int64_t)i * a.S;
+  const int valid_rows = (int)min((int64_t)a.S, a.N - base);
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
+  const int nk1 = a.m_t / KC;                     // phase-1 chunks of 64 features
+  const int nk1p = (nk1 + 3) / 4 * 4;             // padded with zero chunks to a multiple of 4
+  const int nft = (a.m_t + FT - 1) / FT;
+
+  // ---- copies: 4 per wave per chunk, zeros when !valid or out of range. The two phases have
+  // separate copy routines, chosen at compile time at every call site: a run-time branch
+  // between them would join control flow around the copies, after which the compiler drains
+  // all copies before the next LDS read.
+  auto copy1 = [&](int c, uint8_t* st, bool valid, int n) {
+    // rows 32 w + 8 n .. + 7 of chunk c, 128 bytes each; lane -> row (ln >> 3), position (ln & 7)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int row = wave * 32 + n * 8 + (ln >> 3);
+    const uint32_t pc = (uint32_t)((ln & 7) ^ (int)swz<SWZ_ROW>(row));
+    const bool ok = valid && c < nk1 && row < valid_rows;
+    dma16(zr, st + (wave * 32 + n * 8) * ROWB, ok ? (uint32_t)((base + row) * a.ld_z * 2) + 16u * pc : OOB,
+          (uint32_t)c * KC * 2u);
+  };
+  auto copy2 = [&](int c2, uint8_t* st, bool valid, int n) {
+    // rows 8 w + 2 n, + 1 (512 bytes each) of q chunk qc, f tile ft; 32-byte piece
+    // (p >> 1) ^ 2 (t & 3) of row t
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int ft = c2 >> 2, qc = c2 & 3;
+    const int t = wave * 8 + n * 2 + (ln >> 5);
+    const int q = qc * 64 + t;
+    const int pp = ln & 31;
+    const int pc = (pp >> 1) ^ (2 * (t & 3));
+    const int f = ft * FT + pc * 16 + (pp & 1) * 8;
+    const bool ok = valid && c2 < 4 * nft && q < valid_rows && f < a.m_t;
+    dma16(zr, st + (wave * 8 + n * 2) * ZB, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
+  };
+
+  // ---- phase 1
+  uint32_t fq[4], fp[4];
+  frag_offsets<SWZ_ROW>(fq, 0, lane);
+  frag_offsets<SWZ_ROW>(fp, wave * 32, lane);
+  f32x16 acc1[8];
+#pragma unroll
+  for (int qb = 0; qb < 8; ++qb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc1[qb][v] = 0.f;
+  float sq = 0.f;
+  // one chunk of MFMAs from stage st; issue(ks) issues the ks-th copy of a later chunk
+  auto compute1 = [&](const uint8_t* st, auto&& issue) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 rb = lds_read16(st, fp[ks]);
+      uint4 ra[8];
+#pragma unroll
+      for (int qb = 0; qb < 8; ++qb) ra[qb] = lds_read16(st, fq[ks] + qb * 32 * ROWB);
+      sq = sumsq8(rb, sq);
+#pragma unroll
+      for (int qb = 0; qb < 8; ++qb) acc1[qb] = mfma32(as_bf16x8(ra[qb]), as_bf16x8(rb), acc1[qb]);
+      issue(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto c1 = [&](int c, uint8_t* dst) { return [=, &copy1](int n) { copy1(c, dst, true, n); }; };
+  auto c2 = [&](int c, uint8_t* dst) { return [=, &copy2](int n) { copy2(c, dst, true, n); }; };
+
+  for (int n = 0; n < 4; ++n) copy1(0, st0, true, n);
+  for (int n = 0; n < 4; ++n) copy1(1, st1, true, n);
+  for (int n = 0; n < 4; ++n) copy1(2, st2, true, n);
+  for (int kc = 0; kc + 4 < nk1p; kc += 4) {
+    DYN_WAIT_KEEP(8);
+    compute1(st0, c1(kc + 3, st3));
+    DYN_WAIT_KEEP(8);
+    compute1(st1, c1(kc + 4, st0));
+    DYN_WAIT_KEEP(8);
+    compute1(st2, c1(kc + 5, st1));
+    DYN_WAIT_KEEP(8);
+    compute1(st3, c1(kc + 6, st2));
+  }
+  {
+    // last four phase-1 chunks; the first three phase-2 chunks are copied meanwhile
+    const int kc = nk1p - 4;
+    DYN_WAIT_KEEP(8);
+    compute1(st0, c1(kc + 3, st3));
+    DYN_WAIT_KEEP(8);
+    compute1(st1, c2(0, st0));
+    DYN_WAIT_KEEP(8);
+    compute1(st2, c2(1, st1));
+    DYN_WAIT_KEEP(8);
+    compute1(st3, c2(2, st2));
+  }
+
+  // ---- norms, G (bf16) as phase-2 B fragments, r_p from the rounded values
+  {
+    const float t = sq + __shfl_xor(sq, 32);    // the two lane halves hold the two k-halves
+    if (lane < 32) s_sq[wave * 32 + lane] = t;
+  }
+  lds_sync();
+  if (tid < QR) {
+    const float ss = s_sq[tid];
+    s_rn[tid] = (tid < valid_rows && ss > 0.f) ? 1.0f / sqrtf(ss) : 0.f;
+  }
+  lds_sync();
+  uint4 gfrag[8][2];
+  float inv;
+  {
+    const float rnp = s_rn[wave * 32 + (lane & 31)];
+    float r = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < 8; ++qb) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int q0 = qb * 32 + s2 * 16 + h * 8 + (lane >> 5) * 4;   // rows of v = 8 s2 + 4 h + 0..3
+          const float4 rq = *reinterpret_cast<const float4*>(&s_rn[q0]);
+          const int v0 = s2 * 8 + h * 4;
+          const float g0 = acc1[qb][v0 + 0] * rq.x * rnp;
+          const float g1 = acc1[qb][v0 + 1] * rq.y * rnp;
+          const float g2 = acc1[qb][v0 + 2] * rq.z * rnp;
+          const float g3 = acc1[qb][v0 + 3] * rq.w * rnp;
+          pk[2 * h + 0] = pack_bf16(g0, g1);
+          pk[2 * h + 1] = pack_bf16(g2, g3);
+          r += (bf16lo(pk[2 * h]) + bf16hi(pk[2 * h])) + (bf16lo(pk[2 * h + 1]) + bf16hi(pk[2 * h + 1]));
+        }
+        gfrag[qb][s2] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
+    }
+    r += __shfl_xor(r, 32);
+    inv = 1.0f / (r + a.eps);
+  }
+
+  // ---- phase 2. G fragment (qb, s2) of lane half h holds q = 32 qb + 16 s2 + {4h .. 4h+3,
+  // 8+4h .. 8+4h+3}; the Z^T fragments are read with the same q order (two transpose reads:
+  // tokens +4h and +8+4h), features 32 fb + (l & 31).
+  uint32_t offZ[8];
+  {
+    const int s2x = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
+    const uint32_t row = (uint32_t)(4 * (lane >> 5) + ((lane & 15) >> 2)) * ZB;
+#pragma unroll
+    for (int fb = 0; fb < 8; ++fb)
+      offZ[fb] = row + (uint32_t)(((2 * fb + g1) ^ (2 * s2x)) << 5) + 8u * (lane & 3);
+  }
+  f32x16 acc2[8];
+  auto zero2 = [&]() {
+#pragma unroll
+    for (int fb = 0; fb < 8; ++fb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc2[fb][v] = 0.f;
+  };
+  zero2();
+  auto compute2 = [&](const uint8_t* st, auto qc_tag, int cnext, uint8_t* dst) {
+    // cnext: phase-2 chunk index of the copies issued meanwhile
+    constexpr int qc = decltype(qc_tag)::value;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {                 // (qb_local, s2) = (ks >> 1, ks & 1)
+      const int qbl = ks >> 1, s2 = ks & 1;
+      const uint32_t tok = (uint32_t)(32 * qbl + 16 * s2) * ZB;
+      uint4 ra[8];
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) {
+        const uint2 lo = lds_read_tr8(st, offZ[fb] + tok);
+        const uint2 hi = lds_read_tr8(st, offZ[fb] + tok + 8 * ZB);
+        ra[fb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      const uint4 gb = gfrag[2 * qc + qbl][s2];
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) acc2[fb] = mfma32(as_bf16x8(ra[fb]), as_bf16x8(gb), acc2[fb]);
+      copy2(cnext, dst, true, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  uint16_t* ob = a.out + b * a.N * a.ld_out;
+  const int p = wave * 32 + (lane & 31);
+  const bool p_ok = p < valid_rows;
+  auto epilogue = [&](int ft) {
+#pragma unroll
+    for (int fb = 0; fb < 8; ++fb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int f = ft * FT + fb * 32 + g * 8 + (lane >> 5) * 4;
+        const uint32_t lo = pack_bf16(acc2[fb][g * 4 + 0] * inv, acc2[fb][g * 4 + 1] * inv);
+        const uint32_t hi = pack_bf16(acc2[fb][g * 4 + 2] * inv, acc2[fb][g * 4 + 3] * inv);
+        if (p_ok && f < a.m_t) *reinterpret_cast<uint2*>(ob + (base + p) * a.ld_out + f) = make_uint2(lo, hi);
+      }
+  };
+  for (int ft = 0; ft < nft; ++ft) {
+    const int c0 = 4 * ft;
+    DYN_WAIT_KEEP(8);
+    compute2(st0, std::integral_constant<int, 0>{}, c0 + 3, st3);
+    DYN_WAIT_KEEP(8);
+    compute2(st1, std::integral_constant<int, 1>{}, c0 + 4, st0);
+    DYN_WAIT_KEEP(8);
+    compute2(st2, std::integral_constant<int, 2>{}, c0 + 5, st1);
+    DYN_WAIT_KEEP(8);
+    compute2(st3, std::integral_constant<int, 3>{}, c0 + 6, st2);
+    epilogue(ft);
+    zero2();
+  }
+  wait_vmem();   // the zero-filled copies issued past the last chunk land before the exit
+}
+
+}  // namespace ring
+
 template <int NQB, int NPB>
 hipError_t launch_dyn_t(DynParams p, hipStream_t stream) {
   constexpr int PWG = 4 * NPB * 32;
@@ -305,7 +546,10 @@ hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int
   p.n_s = (int)((N + S - 1) / S);
   p.tiles = B * p.n_s;
   p.pgroups = 1;
-  if (S <= 256) return launch_dyn_t<8, 2>(p, stream);
+  if (S <= 256) {
+    hipLaunchKernelGGL(ring::dyn_ring_kernel, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
   return launch_dyn_t<16, 1>(p, stream);
 }
 
