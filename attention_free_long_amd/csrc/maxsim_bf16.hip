@@ -14,7 +14,9 @@
 // One workgroup of 8 waves per CU (2 per SIMD), in a 2 x 4 grid: each wave owns 128 x 64 of the
 // fp32 accumulator (8 MFMA 32x32x16 blocks). Features stream through a 4-stage LDS ring in
 // chunks of 32 by direct global -> LDS copies, three chunks in flight while one is multiplied
-// (the copies of a chunk are issued between the MFMA groups of the chunk being multiplied);
+// (the copies of a chunk are issued between the MFMA groups of the chunk being multiplied, and
+// the wait for the next chunk comes before the last group, whose MFMAs hide the next chunk's
+// first fragment reads);
 // the next unit's first three chunks are copied while the current one finishes and during its
 // epilogue. The packed layout makes every copy instruction read 1 KiB of contiguous memory.
 //
@@ -169,43 +171,64 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   };
 
   f32x16 acc[4][2];
-  // One chunk of MFMAs from stage st, with the 4 copies of chunk kc into stage dst spread
-  // between its four MFMA groups, and the second k-step's fragments read behind the first
-  // group: copies landing in LDS then compete less with the fragment reads, which measured
-  // 6-7 % faster than issuing all reads and copies up front.
-  auto compute_copy = [&](const uint8_t* st, int kc, uint8_t* dst, bool valid) {
-    const uint8_t* sa = st;
-    const uint8_t* sb = st + T * RB;
-    uint4 ra[2][4], rb[2][2];
-    auto fetch = [&](int ks) {
+  // Fragments of k-step 0 (ra0, rb0) and 1 (ra1, rb1) of the chunk being multiplied.
+  uint4 ra0[4], rb0[2], ra1[4], rb1[2];
+  auto fetch0 = [&](const uint8_t* st) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) ra[ks][mb] = lds_read16(sa, fa[ks] + mb * 32 * RB);
+    for (int mb = 0; mb < 4; ++mb) ra0[mb] = lds_read16(st, fa[0] + mb * 32 * RB);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) rb[ks][nb] = lds_read16(sb, fb[ks] + nb * 32 * RB);
-    };
-    fetch(0);
+    for (int nb = 0; nb < 2; ++nb) rb0[nb] = lds_read16(st + T * RB, fb[0] + nb * 32 * RB);
+  };
+  auto fetch1 = [&](const uint8_t* st) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) ra1[mb] = lds_read16(st, fa[1] + mb * 32 * RB);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) rb1[nb] = lds_read16(st + T * RB, fb[1] + nb * 32 * RB);
+  };
+  // One chunk from stage st whose k-step-0 fragments are already in ra0 / rb0; the 4 copies of
+  // chunk kc into dst go between the MFMA groups. With next != nullptr the next chunk's wait
+  // and barrier come before the last MFMA group, and its k-step-0 fragments are read under it.
+  auto compute_pipe = [&](const uint8_t* st, int kc, uint8_t* dst, bool valid, const uint8_t* next) {
     int sub = lane >> 2;
     asm volatile("" : "+v"(sub));
     const uint32_t kb = (uint32_t)kc * (uint32_t)a.S * RB;
     const uint32_t c = (uint32_t)sub * RB + 16u * (uint32_t)((lane & 3) ^ ((sub >> 2) & 3));
     const uint32_t laneA = pbA + c, laneB = pbB + c;
+    auto copy = [&](int ks, int h) {
+      const int r0 = wave * 32 + ks * 16;
+      if (h == 0) dma16(xr, dst + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
+      else dma16(xr, dst + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
+    };
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+    fetch1(st);
+    copy(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+    for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = mfma32(as_bf16x8(ra[ks][mb]), as_bf16x8(rb[ks][nb]), acc[mb][nb]);
-        if (ks == 0 && h == 0) fetch(1);
-        // copy (block h, 16-row group ks) of this wave's rows, as dma() orders them
-        const int r0 = wave * 32 + ks * 16;
-        if (h == 0) dma16(xr, dst + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
-        else dma16(xr, dst + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+    copy(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
+    copy(1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) {
+      // 3 of this chunk's copies and the 4 of the previous one may stay in flight
+      WAIT_KEEP(7);
+      fetch0(next);
     }
+#pragma unroll
+    for (int mb = 2; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
+    copy(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Thread tid < 256 owns target row tid of the unit, thread tid >= 256 candidate column
@@ -247,29 +270,25 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
         for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
     // ---- K loop. Every copy is issued unconditionally (a control-flow join around a copy
     // makes the compiler drain all copies before the next LDS read) and every chunk is exactly
-    // 4 copies per wave, so WAIT_KEEP(8) leaves exactly the two newer chunks in flight.
+    // 4 copies per wave, so WAIT_KEEP(8) at a chunk boundary (WAIT_KEEP(7) before the last MFMA
+    // group, with 3 of the current chunk's copies issued) leaves exactly the newer copies in
+    // flight.
+    WAIT_KEEP(8);
+    fetch0(st0);
     for (int kc = 0; kc + 4 < nk4; kc += 4) {
-      WAIT_KEEP(8);
-      compute_copy(st0, kc + 3, st3, kc + 3 < nk);
-      WAIT_KEEP(8);
-      compute_copy(st1, kc + 4, st0, kc + 4 < nk);
-      WAIT_KEEP(8);
-      compute_copy(st2, kc + 5, st1, kc + 5 < nk);
-      WAIT_KEEP(8);
-      compute_copy(st3, kc + 6, st2, kc + 6 < nk);
+      compute_pipe(st0, kc + 3, st3, kc + 3 < nk, st1);
+      compute_pipe(st1, kc + 4, st0, kc + 4 < nk, st2);
+      compute_pipe(st2, kc + 5, st1, kc + 5 < nk, st3);
+      compute_pipe(st3, kc + 6, st2, kc + 6 < nk, st0);
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
-      WAIT_KEEP(8);
-      compute_copy(st0, kc + 3, st3, kc + 3 < nk);
-      WAIT_KEEP(8);
+      compute_pipe(st0, kc + 3, st3, kc + 3 < nk, st1);
       if (has_next) set_unit(nx);
-      compute_copy(st1, 0, st0, has_next);
-      WAIT_KEEP(8);
-      compute_copy(st2, 1, st1, has_next && 1 < nk);
-      WAIT_KEEP(8);
-      compute_copy(st3, 2, st2, has_next && 2 < nk);
+      compute_pipe(st1, 0, st0, has_next, st2);
+      compute_pipe(st2, 1, st1, has_next && 1 < nk, st3);
+      compute_pipe(st3, 2, st2, has_next && 2 < nk, nullptr);
     }
 
     // ---- epilogue (the next unit's first three chunks are in flight into stages 0-2)
