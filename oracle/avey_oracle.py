@@ -108,30 +108,46 @@ def score_matrix(x: np.ndarray, S: int) -> np.ndarray:
     return out
 
 
-def top_k(row: np.ndarray, i: int, k: int):
+def top_k(row: np.ndarray, i: int, k: int, preceding: bool = False):
     """Top-k candidates of one target split and their divide-by-max weights.
 
     [notes] 整体框架 / [summary] 3: keep the k most relevant splits, then divide each selected
     score by the largest of them. Order: score descending, ties to the lower index; the
     target itself is never a candidate. Returns (idx[k], w[k], s[k], gap) where gap is the
     relative distance between the k-th and (k+1)-th scores (inf when there is no (k+1)-th).
+
+    preceding=True is the unidirectional ranker: the candidates are the splits before the
+    target only ([summary] 3 speaks of the top-k preceding splits; the [summary] pretraining
+    ablation and the [notes] training-strategy section find that ranker direction best). When
+    fewer than k splits precede the target, the selection is padded with empty blocks:
+    index -1, weight 0 (a reading; the pages are silent on it).
     """
-    cands = sorted((j for j in range(len(row)) if j != i), key=lambda j: (-row[j], j))
+    if preceding:
+        pool = range(i)
+    else:
+        pool = (j for j in range(len(row)) if j != i)
+    cands = sorted(pool, key=lambda j: (-row[j], j))
     idx = cands[:k]
     s = np.array([row[j] for j in idx], dtype=np.float64)
-    w = s / s[0]
+    w = s / s[0] if len(idx) else s
     if len(cands) > k:
         sk, sk1 = row[cands[k - 1]], row[cands[k]]
         gap = (sk - sk1) / abs(sk) if sk != 0 else (0.0 if sk1 == sk else math.inf)
     else:
         gap = math.inf
+    npad = k - len(idx)
+    if npad:
+        idx = list(idx) + [-1] * npad
+        w = np.concatenate([w, np.zeros(npad)])
+        s = np.concatenate([s, np.full(npad, NEG_INF)])
     return np.array(idx, dtype=np.int64), w, s, gap
 
 
-def split_rank(x: np.ndarray, S: int, k: int, rows=None):
+def split_rank(x: np.ndarray, S: int, k: int, rows=None, preceding: bool = False):
     """Score rows, top-k indices and weights for the listed (b, i) target splits (default: all).
 
-    Returns dict {(b, i): (score_row, idx, w, gap)}.
+    Returns dict {(b, i): (score_row, idx, w, gap)}. preceding selects the unidirectional
+    ranker (see top_k).
     """
     B, N, _ = x.shape
     n_s = n_splits(N, S)
@@ -140,7 +156,7 @@ def split_rank(x: np.ndarray, S: int, k: int, rows=None):
     out = {}
     for b, i in rows:
         r = score_row(x[b], S, i)
-        idx, w, _, gap = top_k(r, i, k)
+        idx, w, _, gap = top_k(r, i, k, preceding)
         out[(b, i)] = (r, idx, w, gap)
     return out
 
@@ -152,12 +168,16 @@ def compress_split(x_b: np.ndarray, S: int, idx_i, w_i, P: np.ndarray, i: int, r
     [notes] 关键设计 4, eq. 8 and [summary] 4.3: X_cat stacks the current split and its k
     retrieved splits, each retrieved split scaled by its normalised score ([notes] 整体框架);
     P (S x (k+1)S) maps the (k+1)S rows back to S. The residual adds the current split's own
-    tokens ([summary] appendix H). Block order: [current, rank 1, ..., rank k].
+    tokens ([summary] appendix H). Block order: [current, rank 1, ..., rank k]. An index of -1
+    is an empty block (S zero rows), as the unidirectional ranker pads its selection.
     """
-    N = x_b.shape[0]
+    N, d = x_b.shape
     blocks = [padded_split(x_b, S, i)]
     for j, wj in zip(idx_i, w_i):
-        blocks.append(float(wj) * padded_split(x_b, S, int(j)))
+        if int(j) < 0:
+            blocks.append(np.zeros((S, d), dtype=np.float64))
+        else:
+            blocks.append(float(wj) * padded_split(x_b, S, int(j)))
     x_cat = np.concatenate(blocks, axis=0)            # [(k+1)S, d]
     xhat = np.asarray(P, dtype=np.float64) @ x_cat     # [S, d]
     if residual:

@@ -191,6 +191,59 @@ def test_topk_invariants(seed):
         assert row[a] > row[b] or (row[a] == row[b] and a < b)
 
 
+def test_preceding_topk_hand_worked():
+    """Unidirectional ranker on the hand-worked scores: candidates precede the target; missing
+    candidates are empty blocks (index -1, weight 0)."""
+    g = GOLD["maxsim"]
+    x = np.array(g["x"], dtype=np.float64)
+    ranked = O.split_rank(x[None], g["S"], 2, preceding=True)
+    _, idx0, w0, _ = ranked[(0, 0)]
+    _, idx1, w1, _ = ranked[(0, 1)]
+    _, idx2, w2, _ = ranked[(0, 2)]
+    assert list(idx0) == [-1, -1] and list(w0) == [0.0, 0.0]
+    assert list(idx1) == [0, -1] and list(w1) == [1.0, 0.0]
+    # s(2<-0) = 0.6 and s(2<-1) = -0.28 from the golden file
+    assert list(idx2) == [0, 1]
+    np.testing.assert_allclose(w2, [1.0, -0.28 / 0.6], rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_preceding_topk_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(2, 30))
+    i = int(rng.integers(0, n))
+    k = int(rng.integers(1, n))
+    row = rng.integers(1, 6, size=n).astype(np.float64)
+    row[i] = -math.inf
+    idx, w, s, _ = O.top_k(row, i, k, preceding=True)
+    real = [j for j in idx.tolist() if j >= 0]
+    assert len(idx) == k and len(real) == min(k, i)
+    assert all(j < i for j in real) and idx.tolist()[len(real):] == [-1] * (k - len(real))
+    assert np.all(w[len(real):] == 0.0)
+    brute = sorted(range(i), key=lambda j: (-row[j], j))[:k]
+    assert real == brute
+    if real:
+        assert w[0] == 1.0
+
+
+def test_compress_empty_block_is_zero():
+    """Index -1 contributes nothing, whatever its weight: same result as weight 0 on a real
+    split."""
+    rng = np.random.default_rng(8)
+    S, d, k = 4, 3, 2
+    x, idx, w, N, n_s = _rand_setup(rng, S, d, 5, N=18, k=k)
+    P = rng.standard_normal((S, (k + 1) * S))
+    idx_e, w_e = idx.copy(), w.copy()
+    idx_e[0, 2, 1] = -1
+    w_e[0, 2, 1] = 0.0
+    w_z = w.copy()
+    w_z[0, 2, 1] = 0.0
+    a = O.select_compress(x, S, idx_e, w_e, P)
+    b = O.select_compress(x, S, idx, w_z, P)
+    for key in a:
+        np.testing.assert_allclose(a[key], b[key], atol=1e-14)
+
+
 # ----------------------------------------------------------------------------- compression
 def _rand_setup(rng, S=4, d=3, n_s=5, N=None, k=2):
     N = N or S * n_s
