@@ -27,7 +27,9 @@ EXPORTS = (
     "avey_maxsim_prepare",
     "avey_maxsim_scores",
     "avey_topk_norm",
+    "avey_topk_norm_preceding",
     "avey_split_rank",
+    "avey_split_rank_preceding",
     "avey_select_compress",
     "avey_dyn_context",
 )
@@ -65,8 +67,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_maxsim_scores.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp]
     lib.avey_topk_norm.restype = i32
     lib.avey_topk_norm.argtypes = [vp, i64, i64, i32, vp, vp, vp]
-    lib.avey_split_rank.restype = i32
-    lib.avey_split_rank.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
+    lib.avey_topk_norm_preceding.restype = i32
+    lib.avey_topk_norm_preceding.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    for fn in (lib.avey_split_rank, lib.avey_split_rank_preceding):
+        fn.restype = i32
+        fn.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.avey_select_compress.restype = i32
     lib.avey_select_compress.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, i64, vp]
     lib.avey_dyn_context.restype = i32
@@ -155,21 +160,25 @@ def avey_maxsim_scores(workspace, x, S: int, scores=None):
     return scores
 
 
-def avey_topk_norm(scores, k: int, idx=None, w=None):
-    """Top-k indices [B, n_s, k] (int32) and divide-by-max weights (fp32) of a score matrix."""
+def avey_topk_norm(scores, k: int, idx=None, w=None, preceding: bool = False):
+    """Top-k indices [B, n_s, k] (int32) and divide-by-max weights (fp32) of a score matrix.
+
+    preceding=True: candidates of row i are the splits j < i; short rows end with (-1, 0)."""
     import torch
     B, n_s, _ = scores.shape
     if idx is None:
         idx = torch.empty((B, n_s, k), device=scores.device, dtype=torch.int32)
     if w is None:
         w = torch.empty((B, n_s, k), device=scores.device, dtype=torch.float32)
-    _check("avey_topk_norm", load_library().avey_topk_norm(
-        scores.data_ptr(), B, n_s, k, idx.data_ptr(), w.data_ptr(), _stream(scores)))
+    lib = load_library()
+    fn = lib.avey_topk_norm_preceding if preceding else lib.avey_topk_norm
+    _check("avey_topk_norm", fn(scores.data_ptr(), B, n_s, k, idx.data_ptr(), w.data_ptr(), _stream(scores)))
     return idx, w
 
 
-def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, workspace=None):
-    """(scores, idx, w) of the bidirectional ranker for x [B, N, d]."""
+def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, workspace=None, preceding: bool = False):
+    """(scores, idx, w) of the ranker for x [B, N, d]: bidirectional (every other split is a
+    candidate), or with preceding=True unidirectional (only earlier splits)."""
     import torch
     B, N, d, ld = _rows(x, "x")
     n_s = n_splits(N, S)
@@ -182,7 +191,9 @@ def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, workspace=
         idx = torch.empty((B, n_s, k), device=dev, dtype=torch.int32)
     if w is None:
         w = torch.empty((B, n_s, k), device=dev, dtype=torch.float32)
-    _check("avey_split_rank", load_library().avey_split_rank(
+    lib = load_library()
+    fn = lib.avey_split_rank_preceding if preceding else lib.avey_split_rank
+    _check("avey_split_rank", fn(
         x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, workspace.data_ptr(), scores.data_ptr(), idx.data_ptr(),
         w.data_ptr(), _stream(x)))
     return scores, idx, w

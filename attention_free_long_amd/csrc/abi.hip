@@ -158,11 +158,23 @@ avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t 
   bool empty = false;
   AVEY_TRY(check_topk(scores, B, n_s, k, idx, w, &empty));
   if (empty) return AVEY_OK;
-  return hip_status(launch_topk_norm(scores, B, n_s, k, idx, w, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_topk_norm(scores, B, n_s, k, false, idx, w, reinterpret_cast<hipStream_t>(stream)));
 }
 
-avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
-                            int32_t k, void* workspace, float* scores, int32_t* idx, float* w, void* stream) {
+avey_status avey_topk_norm_preceding(const float* scores, int64_t B, int64_t n_s, int32_t k, int32_t* idx, float* w,
+                                     void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_topk(scores, B, n_s, k, idx, w, &empty));
+  if (empty) return AVEY_OK;
+  return hip_status(launch_topk_norm(scores, B, n_s, k, true, idx, w, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+avey_status split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
+                       int32_t k, void* workspace, float* scores, int32_t* idx, float* w, bool preceding,
+                       void* stream) {
   // Every check of the three stages runs before the first launch.
   bool empty = false;
   AVEY_TRY(check_prepare(x, dt, B, N, d, ld_x, S, workspace, &empty));
@@ -172,7 +184,22 @@ avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, 
   AVEY_TRY(check_topk(scores, B, n_s, k, idx, w, &empty));
   AVEY_TRY(avey_maxsim_prepare(x, dt, B, N, d, ld_x, S, workspace, stream));
   AVEY_TRY(avey_maxsim_scores(workspace, dt, B, N, d, S, scores, stream));
-  return avey_topk_norm(scores, B, n_s, k, idx, w, stream);
+  return preceding ? avey_topk_norm_preceding(scores, B, n_s, k, idx, w, stream)
+                   : avey_topk_norm(scores, B, n_s, k, idx, w, stream);
+}
+}  // namespace
+
+extern "C" {
+
+avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
+                            int32_t k, void* workspace, float* scores, int32_t* idx, float* w, void* stream) {
+  return split_rank(x, dt, B, N, d, ld_x, S, k, workspace, scores, idx, w, false, stream);
+}
+
+avey_status avey_split_rank_preceding(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
+                                      int32_t S, int32_t k, void* workspace, float* scores, int32_t* idx, float* w,
+                                      void* stream) {
+  return split_rank(x, dt, B, N, d, ld_x, S, k, workspace, scores, idx, w, true, stream);
 }
 
 avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,

@@ -77,6 +77,7 @@ struct CompressParams {
 #define WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 constexpr int MAXBLK = kCompressMaxBlocks;   // k + 1 <= MAXBLK (checked by the caller)
+constexpr int kEmptyBlock = -(1 << 30);      // first token of an empty block: every copy is out of range
 
 __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE];
@@ -112,10 +113,11 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   if (tid == 0) s_slow = 0;
   __syncthreads();
   for (int r = tid; r <= a.k; r += 256) {
-    int src = r ? idx_i[r - 1] : i;
-    src = min(max(src, 0), a.n_s - 1);
-    s_tok0[r] = src * a.S;
-    const float wr = r ? w_i[r - 1] : 1.f;
+    const int src = r ? idx_i[r - 1] : i;
+    // a negative index is an empty block (zero rows, as the unidirectional ranker pads its
+    // selection): its copies load zeros and its weight is taken as 1, which changes nothing
+    s_tok0[r] = src < 0 ? kEmptyBlock : min(src, a.n_s - 1) * a.S;
+    const float wr = (r && src >= 0) ? w_i[r - 1] : 1.f;
     s_wt[r] = wr;
     if (!(wr >= 0x1p-60f && wr <= 0x1p60f)) s_slow = 1;   // also catches NaN
   }
@@ -160,7 +162,7 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
       const int c = (p >> 1) ^ (2 * (t & 3));                      // logical 32-byte piece
       const int f = f_base + c * 16 + (p & 1) * 8;
       const int64_t tok = (int64_t)tok0 + t;
-      const bool ok = valid && tok < a.N && f < a.d;
+      const bool ok = valid && tok >= 0 && tok < a.N && f < a.d;
       dma16(xr, st + (wave * 8 + n * 2) * XB, ok ? (uint32_t)((tok * a.ld_x + f) * 2) : OOB, 0);
     } else {
       const int r0 = wave * 32 + (n - 4) * 16;

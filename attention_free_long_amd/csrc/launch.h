@@ -10,8 +10,8 @@ hipError_t launch_prepare(const void* x, bool bf16, int64_t B, int64_t N, int d,
                           hipStream_t stream);
 hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
                               hipStream_t stream);
-hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, int32_t* idx, float* w,
-                            hipStream_t stream);
+hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, bool preceding, int32_t* idx,
+                            float* w, hipStream_t stream);
 constexpr int kCompressMaxBlocks = 512;   // bf16 gather + compress: k + 1 <= this
 hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                 const int32_t* idx, const float* w, const uint16_t* P, int residual, uint16_t* xhat,

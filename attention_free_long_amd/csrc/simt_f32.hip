@@ -78,7 +78,8 @@ __global__ void __launch_bounds__(256) compress_f32_kernel(const float* __restri
   float acc = 0.f;
   for (int blk = 0; blk <= k; ++blk) {
     int src = blk ? idx[(b * n_s + i) * k + blk - 1] : i;
-    src = min(max(src, 0), n_s - 1);
+    if (src < 0) continue;                 // empty block (unidirectional padding)
+    src = min(src, n_s - 1);
     const float wt = blk ? w[(b * n_s + i) * k + blk - 1] : 1.f;
     for (int slot = 0; slot < S; ++slot) {
       const int64_t tok = (int64_t)src * S + slot;

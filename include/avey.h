@@ -136,6 +136,27 @@ avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, 
                             int32_t* idx, float* w, void* stream);
 
 /*
+ * avey_topk_norm_preceding -- the unidirectional ranker's selection ([summary] section 3: the
+ * top-k preceding splits of each target split; the [summary] pretraining ablation and the
+ * [notes] training-strategy section find that ranker direction the better one).
+ * As avey_topk_norm, with the candidates of row i restricted to j < i. A row with fewer than
+ * k candidates (i < k) is completed with idx = -1, w = 0 (empty blocks for
+ * avey_select_compress); row 0 is all empty. w[..., 0] == 1 whenever row i has a candidate
+ * whose score is finite and non-zero.
+ */
+avey_status avey_topk_norm_preceding(const float* scores, int64_t B, int64_t n_s, int32_t k,
+                                     int32_t* idx, float* w, void* stream);
+
+/*
+ * avey_split_rank_preceding -- avey_maxsim_prepare, avey_maxsim_scores and
+ * avey_topk_norm_preceding on the same stream; arguments as avey_split_rank.
+ */
+avey_status avey_split_rank_preceding(const void* x, avey_dtype dt, int64_t B, int64_t N,
+                                      int64_t d, int64_t ld_x, int32_t S, int32_t k,
+                                      void* workspace, float* scores, int32_t* idx, float* w,
+                                      void* stream);
+
+/*
  * avey_select_compress -- weighted gather and neural compression ([notes] 关键设计 4, eq. 8;
  * [summary] 4.3 and appendix H).
  *
@@ -146,12 +167,16 @@ avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, 
  * and the valid rows of Xhat_i are written to xhat.
  *
  *   x        [B, N, d] row stride ld_x (input)
- *   idx, w   [B, n_s, k] int32 / float32 (inputs; every idx must lie in [0, n_s))
+ *   idx, w   [B, n_s, k] int32 / float32 (inputs; idx in [0, n_s), or negative for an empty
+ *            block of S zero rows -- the padding of avey_topk_norm_preceding; indices >= n_s
+ *            are clamped to n_s - 1)
  *   P        [S, (k+1)S] contiguous, dtype dt (input)
  *   residual 0 or 1
  *   xhat     [B, N, d] row stride ld_out, dtype dt (output)
- * Requires k >= 1. For AVEY_BF16 each retrieved row w * x is rounded to bf16 before the
- * product (the current split's rows are used as they are); the result is rounded to bf16.
+ * Requires k >= 1 (and k + 1 <= 512 for AVEY_BF16). For AVEY_BF16 the weights scale the fp32
+ * accumulator between blocks when every weight is a positive normal number in [2^-60, 2^60];
+ * otherwise block r's rows of P are multiplied by w_r and rounded to bf16 as they are read.
+ * The result is rounded to bf16.
  */
 avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
                                  int64_t ld_x, int32_t S, int32_t k, const int32_t* idx,

@@ -94,13 +94,23 @@ def test_workspace_prepare_and_scores_validation(lib):
     assert m(P16, 0, 1, 1024, 64, 64, P16 + 1, None) == ALIGN
 
 
-def test_topk_validation(lib):
-    f = lib.avey_topk_norm
+@pytest.mark.parametrize("fn", ["avey_topk_norm", "avey_topk_norm_preceding"])
+def test_topk_validation(lib, fn):
+    f = getattr(lib, fn)
     assert f(P16, 0, 16, 3, P16, P16, None) == OK
     assert f(None, 1, 16, 3, P16, P16, None) == NULL
     assert f(P16, 1, 16, 16, P16, P16, None) == SHAPE
     assert f(P16, 1, 1, 1, P16, P16, None) == SHAPE
     assert f(P16 + 1, 1, 16, 3, P16, P16, None) == ALIGN
+
+
+def test_split_rank_preceding_validation(lib):
+    f = lib.avey_split_rank_preceding
+    # same argument list and checks as avey_split_rank
+    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None, None) == OK
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 96, 96, 64, 3, P16, P16, P16, P16, None) == UNSUP
 
 
 def test_select_compress_validation(lib):
@@ -114,6 +124,7 @@ def test_select_compress_validation(lib):
     assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, 1, P16, 60, None) == SHAPE   # ld_out < d
     assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P4, 1, P16, 64, None) == ALIGN    # P alignment
     assert f(P16, 1, 1, 1024, 64, 64, 32, 3, P16, P16, P16, 1, P16, 64, None) == UNSUP   # bf16 S % 64
+    assert f(P16, 1, 1, 1 << 20, 64, 64, 64, 600, P16, P16, P16, 1, P16, 64, None) == UNSUP   # bf16 k + 1 > 512
 
 
 def test_dyn_context_validation(lib):

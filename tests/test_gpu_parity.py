@@ -229,3 +229,45 @@ def test_compress_given_weights(gpu_ok, weights):
         assert err <= TOL["bf16"]["out"], f"xhat split {(b, i)}: {err:.3e}"
         worst = max(worst, err)
     say(f"given weights ({weights}): worst xhat error {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "tiny"])
+def test_preceding_ranker_parity(gpu_ok, name):
+    """Unidirectional ranker: candidates precede the target; short rows end with (-1, 0); the
+    compression takes the padded selection (empty blocks are zero rows)."""
+    cfg = SMALL[name]
+    tol = TOL[cfg.dtype]
+    inp = make_inputs(cfg)
+    say(f"{name}: split_rank_preceding + select_compress")
+    x, P, _, _ = upload(inp)
+    scores, idx, w = A.avey_split_rank(x, cfg.S, cfg.k, preceding=True)
+    xhat = A.avey_select_compress(x, idx, w, P, cfg.S)
+    torch.cuda.synchronize()
+    g_s = scores.cpu().numpy().astype(np.float64)
+    g_i, g_w = idx.cpu().numpy(), w.cpu().numpy()
+    x64 = inp.x_f64()
+    ranked = O.split_rank(x64, cfg.S, cfg.k, preceding=True)
+    for (b, i), (o_row, o_idx, o_w, gap) in ranked.items():
+        check_score_row(g_s[b, i], o_row, i, tol["scores"])
+        n_real = min(cfg.k, i)
+        gi = [int(v) for v in g_i[b, i]]
+        assert gi[n_real:] == [-1] * (cfg.k - n_real) and np.all(g_w[b, i, n_real:] == 0.0)
+        real = gi[:n_real]
+        assert all(0 <= j < i for j in real) and len(set(real)) == n_real
+        if n_real == 0:
+            continue
+        assert g_w[b, i, 0] == 1.0
+        o_real = [int(v) for v in o_idx[:n_real]]
+        if gap >= 1e-3:
+            assert set(real) == set(o_real), f"row {(b, i)}: {real} vs {o_real}"
+        else:
+            kth = o_row[o_real[-1]]
+            for j in set(real) ^ set(o_real):
+                assert abs(o_row[j] - kth) <= 1e-3 * abs(kth)
+        ow = np.array([o_row[j] for j in real]) / o_row[real[0]]
+        assert np.max(np.abs(g_w[b, i, :n_real] - ow) / np.abs(ow)) <= tol["w"]
+    comp = O.select_compress(x64, cfg.S, g_i, g_w.astype(np.float64), inp.P_f64(), residual=True)
+    got = host_f64(xhat)
+    for (b, i), rows in comp.items():
+        err = row_rel_err(got[b, split_rows_of(cfg.N, cfg.S, i)], rows)
+        assert err <= tol["out"], f"xhat split {(b, i)}: {err:.3e}"
