@@ -271,3 +271,33 @@ def test_preceding_ranker_parity(gpu_ok, name):
     for (b, i), rows in comp.items():
         err = row_rel_err(got[b, split_rows_of(cfg.N, cfg.S, i)], rows)
         assert err <= tol["out"], f"xhat split {(b, i)}: {err:.3e}"
+
+
+def test_side_stream_and_workspace_reuse(gpu_ok):
+    """Work is enqueued on the caller's current stream, and one workspace serves calls of
+    different sizes in a row: results equal the default-stream ones bitwise."""
+    cfg = SMALL["small_bf16"]
+    inp = make_inputs(cfg)
+    say("side stream, workspace reuse")
+    x, P, z, z_tail = upload(inp)
+    ref = [t.clone() for t in A.avey_split_rank(x, cfg.S, cfg.k)]
+    ref_x = A.avey_select_compress(x, ref[1], ref[2], P, cfg.S)
+    ref_o = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
+    torch.cuda.synchronize()
+    ws = A.rank_workspace(x, cfg.S)
+    small = x[:1, :1100]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        s1 = A.avey_split_rank(small, cfg.S, cfg.k, workspace=ws)   # smaller problem first
+        s2 = A.avey_split_rank(x, cfg.S, cfg.k, workspace=ws)
+        xh = A.avey_select_compress(x, s2[1], s2[2], P, cfg.S)
+        o = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
+    side.synchronize()
+    for a_, b_ in zip(ref, s2):
+        assert torch.equal(a_, b_)
+    assert torch.equal(ref_x.view(torch.int16), xh.view(torch.int16))
+    assert torch.equal(ref_o.view(torch.int16), o.view(torch.int16))
+    s1_ref = A.avey_split_rank(small, cfg.S, cfg.k)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(s1_ref, s1):
+        assert torch.equal(a_, b_)
