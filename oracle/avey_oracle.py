@@ -222,6 +222,55 @@ def dyn_context(z: np.ndarray, S: int, eps: float, splits=None):
     return {(b, i): dyn_context_split(z[b], S, eps, i) for b, i in splits}
 
 
+# ----------------------------------------------------------------------------- contextualizer layers
+def activation(a: np.ndarray, act: str) -> np.ndarray:
+    """sigma of the contextualizer layers: the pages only ask for a monotone activation
+    ([summary] 4, relevance-monotonic updates); this oracle offers identity and ReLU."""
+    if act == "identity":
+        return a
+    if act == "relu":
+        return np.maximum(a, 0.0)
+    raise ValueError(act)
+
+
+def static_layer_split(z_b: np.ndarray, S: int, V: np.ndarray, bias: np.ndarray, act: str, i: int) -> np.ndarray:
+    """c_static(Z) = sigma(V Z_t + b) for one split, valid rows only ([notes] 关键设计 2: the
+    static layer is a learned linear map of the split's tail followed by an activation; V is
+    the S x S cross-embedding matrix of [summary] 3, mixing the split's token positions).
+    b holds one value per token position of the split (a reading). Padding tokens are zero
+    rows of Z_t, so they add nothing to the valid rows."""
+    N = z_b.shape[0]
+    zt = padded_split(z_b, S, i)                             # [S, m_t], zero padding rows
+    y = np.asarray(V, dtype=np.float64) @ zt + np.asarray(bias, dtype=np.float64)[:, None]
+    return activation(y, act)[: len(split_rows(N, S, i))]
+
+
+def dyn_layer_split(z_b: np.ndarray, S: int, eps: float, bias: np.ndarray, act: str, i: int) -> np.ndarray:
+    """c_dyn(Z) = sigma(S~ Z_t + b) for one split, valid rows only ([notes] 关键设计 2 and 3):
+    the dynamic core of dyn_context_split, plus one bias per token position, then sigma."""
+    core = dyn_context_split(z_b, S, eps, i)
+    b = np.asarray(bias, dtype=np.float64)[: core.shape[0], None]
+    return activation(core + b, act)
+
+
+def static_layer(z: np.ndarray, S: int, V: np.ndarray, bias: np.ndarray, act: str, splits=None):
+    """static_layer_split over the listed (b, i) splits (default: all). Returns {(b, i): rows}."""
+    B, N, _ = z.shape
+    n_s = n_splits(N, S)
+    if splits is None:
+        splits = [(b, i) for b in range(B) for i in range(n_s)]
+    return {(b, i): static_layer_split(z[b], S, V, bias, act, i) for b, i in splits}
+
+
+def dyn_layer(z: np.ndarray, S: int, eps: float, bias: np.ndarray, act: str, splits=None):
+    """dyn_layer_split over the listed (b, i) splits (default: all). Returns {(b, i): rows}."""
+    B, N, _ = z.shape
+    n_s = n_splits(N, S)
+    if splits is None:
+        splits = [(b, i) for b in range(B) for i in range(n_s)]
+    return {(b, i): dyn_layer_split(z[b], S, eps, bias, act, i) for b, i in splits}
+
+
 def assemble(parts: dict, B: int, N: int, S: int, width: int) -> np.ndarray:
     """Stack per-split results {(b, i): rows} into a [B, N, width] array (NaN where absent)."""
     out = np.full((B, N, width), np.nan)

@@ -404,3 +404,53 @@ def test_dyn_brute_force_tiny():
             for c in range(m):
                 want = sum(g[bq] * z[0, q, c] for bq, q in enumerate(toks)) / den
                 assert res[(0, i)][a, c] == pytest.approx(want, abs=1e-12)
+
+
+# ----------------------------------------------------------------------------- contextualizer layers
+def test_static_layer_closed_forms():
+    """V = I gives Z_t back; a permutation V permutes the split's tokens (padding rows are
+    zero, so a valid row that draws from a padding slot is zero); the bias adds one value per
+    token position; ReLU clips the identity result at 0."""
+    rng = np.random.default_rng(21)
+    S, m = 4, 3
+    z = rng.standard_normal((1, 10, m))                 # splits of 4, 4, 2 valid tokens
+    zero_b = np.zeros(S)
+    out = O.static_layer(z, S, np.eye(S), zero_b, "identity")
+    for (b, i), rows in out.items():
+        r = O.split_rows(10, S, i)
+        np.testing.assert_array_equal(rows, z[0, r.start:r.stop])
+    perm = [2, 0, 3, 1]
+    V = np.eye(S)[perm]                                 # row s of V picks token perm[s]
+    out = O.static_layer(z, S, V, zero_b, "identity")
+    for i in range(3):
+        r = O.split_rows(10, S, i)
+        for s_, src in enumerate(perm[: len(r)]):
+            want = z[0, i * S + src] if i * S + src < 10 else np.zeros(m)
+            np.testing.assert_array_equal(out[(0, i)][s_], want)
+    bias = rng.standard_normal(S)
+    a = O.static_layer(z, S, V, bias, "identity")
+    c = O.static_layer(z, S, V, bias, "relu")
+    for key in a:
+        n = a[key].shape[0]
+        base = O.static_layer(z, S, V, zero_b, "identity")[key]
+        np.testing.assert_allclose(a[key] - base, np.repeat(bias[:n, None], m, axis=1), atol=1e-15)
+        np.testing.assert_array_equal(c[key], np.where(a[key] > 0, a[key], 0.0))
+
+
+def test_dyn_layer_reduces_to_core():
+    """With b = 0 and the identity the layer is the core S~ Z_t; ReLU output is
+    non-negative and equals the clipped identity result."""
+    rng = np.random.default_rng(22)
+    S, m = 5, 4
+    z = rng.standard_normal((2, 13, m))
+    zero_b = np.zeros(S)
+    core = O.dyn_context(z, S, 1e-8)
+    lay = O.dyn_layer(z, S, 1e-8, zero_b, "identity")
+    for key in core:
+        np.testing.assert_array_equal(lay[key], core[key])
+    bias = rng.standard_normal(S)
+    a = O.dyn_layer(z, S, 1e-8, bias, "identity")
+    c = O.dyn_layer(z, S, 1e-8, bias, "relu")
+    for key in a:
+        assert np.all(c[key] >= 0)
+        np.testing.assert_array_equal(c[key], np.where(a[key] > 0, a[key], 0.0))
