@@ -6,6 +6,8 @@ runs in the library's HIP kernels. torch supplies device memory and the current 
     scores, idx, w = avey_split_rank(x, S, k)        # allocates the ranker workspace if not given
     xhat = avey_select_compress(x, idx, w, P, S, residual=True)
     out = avey_dyn_context(z_tail, S, eps)
+    out = avey_dyn_layer(z_tail, S, eps, bias, act="relu")       # sigma(S~ Z_t + b)
+    out = avey_static_layer(z_tail, V, S, bias, act="identity")  # sigma(V Z_t + b)
 
 Tensors are [B, N, width] with unit stride along width and any row stride (ld); bf16 or fp32.
 There is no fallback: if libavey.so is missing or fails to load, every call raises.
@@ -18,6 +20,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libavey.so")
 
 AVEY_F32, AVEY_BF16 = 0, 1
+AVEY_ACT = {"identity": 0, "relu": 1}
 AVEY_ABI_VERSION = 1
 
 EXPORTS = (
@@ -32,6 +35,8 @@ EXPORTS = (
     "avey_split_rank_preceding",
     "avey_select_compress",
     "avey_dyn_context",
+    "avey_dyn_layer",
+    "avey_static_layer",
 )
 
 
@@ -76,6 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_select_compress.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, i64, vp]
     lib.avey_dyn_context.restype = i32
     lib.avey_dyn_context.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, vp, i64, vp]
+    lib.avey_dyn_layer.restype = i32
+    lib.avey_dyn_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, vp, i32, vp, i64, vp]
+    lib.avey_static_layer.restype = i32
+    lib.avey_static_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, i32, vp, i64, vp]
     ver = lib.avey_abi_version()
     if ver != AVEY_ABI_VERSION:
         raise AveyError("load_library", -101, f"ABI version {ver}, expected {AVEY_ABI_VERSION}")
@@ -233,4 +242,52 @@ def avey_dyn_context(z_tail, S: int, eps: float, out=None):
     _check("avey_dyn_context", load_library().avey_dyn_context(
         z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, float(eps), out.data_ptr(), ld_out,
         _stream(z_tail)))
+    return out
+
+
+def _layer_args(fn: str, z_tail, S: int, bias, act: str):
+    """Shared marshalling of the two contextualizer layers: (bias pointer or 0, act code)."""
+    import torch
+    if act not in AVEY_ACT:
+        raise AveyError(fn, -2, f"act must be one of {sorted(AVEY_ACT)}")
+    if bias is None:
+        return 0, AVEY_ACT[act]
+    if bias.dtype != torch.float32 or not bias.is_contiguous() or tuple(bias.shape) != (S,):
+        raise AveyError(fn, -2, f"bias must be a contiguous float32 [S] = [{S}] tensor")
+    if bias.device != z_tail.device:
+        raise AveyError(fn, -1, "bias must be on the device of z_tail")
+    return bias.data_ptr(), AVEY_ACT[act]
+
+
+def avey_dyn_layer(z_tail, S: int, eps: float, bias=None, act: str = "identity", out=None):
+    """act(S~ Z_t + bias[slot]) per split: the dynamic layer with its bias and activation."""
+    import torch
+    B, N, m_t, ld = _rows(z_tail, "z_tail")
+    bptr, code = _layer_args("avey_dyn_layer", z_tail, S, bias, act)
+    if out is None:
+        out = torch.empty((B, N, m_t), device=z_tail.device, dtype=z_tail.dtype)
+    if out.dtype != z_tail.dtype:
+        raise AveyError("avey_dyn_layer", -3, "out must have the dtype of z_tail")
+    _, _, _, ld_out = _rows(out, "out")
+    _check("avey_dyn_layer", load_library().avey_dyn_layer(
+        z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, float(eps), bptr, code, out.data_ptr(),
+        ld_out, _stream(z_tail)))
+    return out
+
+
+def avey_static_layer(z_tail, V, S: int, bias=None, act: str = "identity", out=None):
+    """act(V Z_t + bias[slot]) per split, V [S, S] mixing the split's token positions."""
+    import torch
+    B, N, m_t, ld = _rows(z_tail, "z_tail")
+    bptr, code = _layer_args("avey_static_layer", z_tail, S, bias, act)
+    if V.dtype != z_tail.dtype or not V.is_contiguous() or tuple(V.shape) != (S, S):
+        raise AveyError("avey_static_layer", -2, f"V must be a contiguous [S, S] = [{S}, {S}] tensor of z_tail's dtype")
+    if out is None:
+        out = torch.empty((B, N, m_t), device=z_tail.device, dtype=z_tail.dtype)
+    if out.dtype != z_tail.dtype:
+        raise AveyError("avey_static_layer", -3, "out must have the dtype of z_tail")
+    _, _, _, ld_out = _rows(out, "out")
+    _check("avey_static_layer", load_library().avey_static_layer(
+        z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, V.data_ptr(), bptr, code, out.data_ptr(),
+        ld_out, _stream(z_tail)))
     return out

@@ -187,6 +187,35 @@ avey_status split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64
   return preceding ? avey_topk_norm_preceding(scores, B, n_s, k, idx, w, stream)
                    : avey_topk_norm(scores, B, n_s, k, idx, w, stream);
 }
+// Layer epilogue arguments: bias may be NULL (no bias), act is an avey_act.
+avey_status check_epi(const float* bias, int32_t act, LayerEpi* epi) {
+  if (act != AVEY_ACT_IDENTITY && act != AVEY_ACT_RELU) return AVEY_ERR_SHAPE;
+  if (bias && !aligned(bias, 4)) return AVEY_ERR_ALIGN;
+  epi->bias = bias;
+  epi->act = act;
+  return AVEY_OK;
+}
+
+avey_status dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t, int64_t ld_z, int32_t S,
+                      float eps, LayerEpi epi, void* out, int64_t ld_out, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_common(dt, B, N, S, &empty));
+  if (empty) return AVEY_OK;
+  AVEY_TRY(check_tensor(z_tail, dt, N, m_t, ld_z));
+  AVEY_TRY(check_tensor(out, dt, N, m_t, ld_out));
+  AVEY_TRY(check_split_bf16(dt, S));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dt == AVEY_BF16) {
+    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * (S > 256 ? 2 : 1);
+    if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
+    return hip_status(launch_dyn_bf16(static_cast<const uint16_t*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
+                                      static_cast<uint16_t*>(out), ld_out, st, epi));
+  }
+  if (B * N > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_dyn_f32(static_cast<const float*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
+                                   static_cast<float*>(out), ld_out, st, epi));
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,22 +262,44 @@ avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_
 
 avey_status avey_dyn_context(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t, int64_t ld_z,
                              int32_t S, float eps, void* out, int64_t ld_out, void* stream) {
+  return dyn_layer(z_tail, dt, B, N, m_t, ld_z, S, eps, LayerEpi{}, out, ld_out, stream);
+}
+
+avey_status avey_dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t, int64_t ld_z,
+                           int32_t S, float eps, const float* bias, int32_t act, void* out, int64_t ld_out,
+                           void* stream) {
+  LayerEpi epi;
+  AVEY_TRY(check_epi(bias, act, &epi));
+  return dyn_layer(z_tail, dt, B, N, m_t, ld_z, S, eps, epi, out, ld_out, stream);
+}
+
+avey_status avey_static_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t, int64_t ld_z,
+                              int32_t S, const void* V, const float* bias, int32_t act, void* out, int64_t ld_out,
+                              void* stream) {
   bool empty = false;
   AVEY_TRY(check_common(dt, B, N, S, &empty));
   if (empty) return AVEY_OK;
+  LayerEpi epi;
+  AVEY_TRY(check_epi(bias, act, &epi));
+  if (!V) return AVEY_ERR_NULL;
   AVEY_TRY(check_tensor(z_tail, dt, N, m_t, ld_z));
   AVEY_TRY(check_tensor(out, dt, N, m_t, ld_out));
   AVEY_TRY(check_split_bf16(dt, S));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // V Z_i is the gather + compress product with no retrieved block (k = 0: X_cat = Z_i, P = V)
   if (dt == AVEY_BF16) {
-    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * (S > 256 ? 2 : 1);
+    if (!aligned(V, 16)) return AVEY_ERR_ALIGN;
+    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * ((m_t + 255) / 256);
     if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
-    return hip_status(launch_dyn_bf16(static_cast<const uint16_t*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
-                                      static_cast<uint16_t*>(out), ld_out, st));
+    return hip_status(launch_compress_bf16(static_cast<const uint16_t*>(z_tail), B, N, (int)m_t, ld_z, S, 0,
+                                           nullptr, nullptr, static_cast<const uint16_t*>(V), 0,
+                                           static_cast<uint16_t*>(out), ld_out, st, epi));
   }
-  if (B * N > kI32) return AVEY_ERR_UNSUPPORTED;
-  return hip_status(launch_dyn_f32(static_cast<const float*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
-                                   static_cast<float*>(out), ld_out, st));
+  if (!aligned(V, 4)) return AVEY_ERR_ALIGN;
+  if ((B * N * m_t + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_compress_f32(static_cast<const float*>(z_tail), B, N, (int)m_t, ld_z, S, 0, nullptr,
+                                        nullptr, static_cast<const float*>(V), 0, static_cast<float*>(out), ld_out,
+                                        st, epi));
 }
 
 }  // extern "C"

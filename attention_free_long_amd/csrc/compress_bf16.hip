@@ -71,6 +71,7 @@ struct CompressParams {
   uint16_t* xhat;
   int64_t N, ld_x, ld_out, tiles;
   int d, S, k, n_s, s_tiles, f_tiles, residual;
+  LayerEpi epi;
 };
 
 // This wave's copies except the newest n are complete, then a workgroup barrier.
@@ -276,32 +277,40 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
 
   // Epilogue: lane owns token s, four consecutive features per (mb, g). The residual rows of a
   // token block are all loaded before any store (stores could alias them as far as the
-  // compiler knows, which would otherwise serialise one load round trip per store).
+  // compiler knows, which would otherwise serialise one load round trip per store). Without
+  // the residual the loads are out of range and return zeros without touching memory. The
+  // layer epilogue (bias per token position, activation) is applied last.
   uint16_t* ob = a.xhat + b * a.N * a.ld_out;
-  const float rf = a.residual ? 1.f : 0.f;
+  const bool relu = a.epi.act != 0;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int s = stl * TS + wn * 64 + nb * 32 + (lane & 31);
     const int64_t tok = (int64_t)i * a.S + s;
     const bool tok_ok = s < a.S && tok < a.N;
+    const bool res_ok = tok_ok && a.residual;
+    const float bv = (tok_ok && a.epi.bias) ? a.epi.bias[s] : 0.f;
     uint2 res[4][4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int f = f_base + wm * 128 + mb * 32 + g * 8 + (lane >> 5) * 4;
-        res[mb][g] = buf_load8(xr, (tok_ok && f < a.d) ? (uint32_t)((tok * a.ld_x + f) * 2) : OOB, 0);
+        res[mb][g] = buf_load8(xr, (res_ok && f < a.d) ? (uint32_t)((tok * a.ld_x + f) * 2) : OOB, 0);
       }
+    auto out = [&](float acc, float r) {
+      const float v = (acc + r) + bv;
+      return relu ? fmaxf(v, 0.f) : v;
+    };
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int f = f_base + wm * 128 + mb * 32 + g * 8 + (lane >> 5) * 4;
         const uint2 r = res[mb][g];
-        const float v0 = fmaf(rf, bf16lo(r.x), acc[mb][nb][g * 4 + 0]);
-        const float v1 = fmaf(rf, bf16hi(r.x), acc[mb][nb][g * 4 + 1]);
-        const float v2 = fmaf(rf, bf16lo(r.y), acc[mb][nb][g * 4 + 2]);
-        const float v3 = fmaf(rf, bf16hi(r.y), acc[mb][nb][g * 4 + 3]);
+        const float v0 = out(acc[mb][nb][g * 4 + 0], bf16lo(r.x));
+        const float v1 = out(acc[mb][nb][g * 4 + 1], bf16hi(r.x));
+        const float v2 = out(acc[mb][nb][g * 4 + 2], bf16lo(r.y));
+        const float v3 = out(acc[mb][nb][g * 4 + 3], bf16hi(r.y));
         if (tok_ok && f < a.d)
           *reinterpret_cast<uint2*>(ob + tok * a.ld_out + f) = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
       }
@@ -312,7 +321,7 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
 
 hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                 const int32_t* idx, const float* w, const uint16_t* P, int residual, uint16_t* xhat,
-                                int64_t ld_out, hipStream_t stream) {
+                                int64_t ld_out, hipStream_t stream, LayerEpi epi) {
   CompressParams p;
   p.x = x; p.idx = idx; p.w = w; p.P = P; p.xhat = xhat;
   p.N = N; p.ld_x = ld_x; p.ld_out = ld_out;
@@ -321,6 +330,7 @@ hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, 
   p.s_tiles = (S + TS - 1) / TS;
   p.f_tiles = (d + TF - 1) / TF;
   p.residual = residual;
+  p.epi = epi;
   p.tiles = B * p.n_s * p.s_tiles * p.f_tiles;
   hipLaunchKernelGGL(compress_bf16_kernel, dim3((unsigned)p.tiles), dim3(256), 0, stream, p);
   return hipGetLastError();

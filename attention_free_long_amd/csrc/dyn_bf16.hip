@@ -31,7 +31,22 @@ struct DynParams {
   int64_t N, ld_z, ld_out, tiles;
   int m_t, S, n_s, pgroups;
   float eps;
+  LayerEpi epi;
 };
+
+// Bias of token position p (0 without a bias), loaded before any copy is issued and forced to
+// complete there, so that no load but the copies is outstanding in the pipelined loops.
+__device__ __forceinline__ float layer_bias(const LayerEpi& e, int p, bool p_ok) {
+  float bv = 0.f;
+  if (e.bias && p_ok) bv = e.bias[p];
+  asm volatile("" : "+v"(bv));
+  return bv;
+}
+
+__device__ __forceinline__ float layer_out(float v, float scale, float bv, bool relu) {
+  const float y = fmaf(v, scale, bv);
+  return relu ? fmaxf(y, 0.f) : y;
+}
 
 template <int NQB, int NPB>
 __global__ void __launch_bounds__(256, 1) dyn_bf16_kernel(DynParams a) {
@@ -71,6 +86,13 @@ __global__ void __launch_bounds__(256, 1) dyn_bf16_kernel(DynParams a) {
   }
   const int prow0 = pg * PWG + wave * NPB * 32;   // this wave's first p (split-local)
   const int nrow0 = kNormFromP ? prow0 : wave * 128;
+  const bool relu = a.epi.act != 0;
+  float bv[NPB];
+#pragma unroll
+  for (int nb = 0; nb < NPB; ++nb) {
+    const int p = prow0 + nb * 32 + (lane & 31);
+    bv[nb] = layer_bias(a.epi, p, p < a.S && base + p < a.N);
+  }
   uint32_t fq[4], fp[4], fn[4];
   frag_offsets<SWZ_ROW>(fq, 0, lane);
   frag_offsets<SWZ_ROW>(fp, prow0, lane);
@@ -254,9 +276,11 @@ __global__ void __launch_bounds__(256, 1) dyn_bf16_kernel(DynParams a) {
         for (int g = 0; g < 4; ++g) {
           const int f = ft * FT + fb * 32 + g * 8 + (lane >> 5) * 4;
           if (f >= a.m_t) continue;
-          const float sc = inv[nb];
-          const uint32_t lo = pack_bf16(acc2[fb][nb][g * 4 + 0] * sc, acc2[fb][nb][g * 4 + 1] * sc);
-          const uint32_t hi = pack_bf16(acc2[fb][nb][g * 4 + 2] * sc, acc2[fb][nb][g * 4 + 3] * sc);
+          const float sc = inv[nb], bb = bv[nb];
+          const uint32_t lo = pack_bf16(layer_out(acc2[fb][nb][g * 4 + 0], sc, bb, relu),
+                                        layer_out(acc2[fb][nb][g * 4 + 1], sc, bb, relu));
+          const uint32_t hi = pack_bf16(layer_out(acc2[fb][nb][g * 4 + 2], sc, bb, relu),
+                                        layer_out(acc2[fb][nb][g * 4 + 3], sc, bb, relu));
           *reinterpret_cast<uint2*>(ob + tok * a.ld_out + f) = make_uint2(lo, hi);
         }
     }
@@ -326,6 +350,10 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   const int64_t base = (int64_t)i * a.S;
   const int valid_rows = (int)min((int64_t)a.S, a.N - base);
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
+  const int p = wave * 32 + (lane & 31);          // this lane's output token (split-local)
+  const bool p_ok = p < valid_rows;
+  const bool relu = a.epi.act != 0;
+  const float bv = layer_bias(a.epi, p, p_ok);
   const int nk1 = a.m_t / KC;                     // phase-1 chunks of 64 features
   const int nk1p = (nk1 + 3) / 4 * 4;             // padded with zero chunks to a multiple of 4
   const int nft = (a.m_t + FT - 1) / FT;
@@ -495,16 +523,16 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     }
   };
   uint16_t* ob = a.out + b * a.N * a.ld_out;
-  const int p = wave * 32 + (lane & 31);
-  const bool p_ok = p < valid_rows;
   auto epilogue = [&](int ft) {
 #pragma unroll
     for (int fb = 0; fb < 8; ++fb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int f = ft * FT + fb * 32 + g * 8 + (lane >> 5) * 4;
-        const uint32_t lo = pack_bf16(acc2[fb][g * 4 + 0] * inv, acc2[fb][g * 4 + 1] * inv);
-        const uint32_t hi = pack_bf16(acc2[fb][g * 4 + 2] * inv, acc2[fb][g * 4 + 3] * inv);
+        const uint32_t lo = pack_bf16(layer_out(acc2[fb][g * 4 + 0], inv, bv, relu),
+                                      layer_out(acc2[fb][g * 4 + 1], inv, bv, relu));
+        const uint32_t hi = pack_bf16(layer_out(acc2[fb][g * 4 + 2], inv, bv, relu),
+                                      layer_out(acc2[fb][g * 4 + 3], inv, bv, relu));
         if (p_ok && f < a.m_t) *reinterpret_cast<uint2*>(ob + (base + p) * a.ld_out + f) = make_uint2(lo, hi);
       }
   };
@@ -538,11 +566,12 @@ hipError_t launch_dyn_t(DynParams p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps,
-                           uint16_t* out, int64_t ld_out, hipStream_t stream) {
+                           uint16_t* out, int64_t ld_out, hipStream_t stream, LayerEpi epi) {
   DynParams p;
   p.z = z; p.out = out;
   p.N = N; p.ld_z = ld_z; p.ld_out = ld_out;
   p.m_t = m_t; p.S = S; p.eps = eps;
+  p.epi = epi;
   p.n_s = (int)((N + S - 1) / S);
   p.tiles = B * p.n_s;
   p.pgroups = 1;

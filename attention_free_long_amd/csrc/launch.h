@@ -12,18 +12,26 @@ hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, i
                               hipStream_t stream);
 hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, bool preceding, int32_t* idx,
                             float* w, hipStream_t stream);
+
+// Output epilogue of a contextualizer layer, y = act(v + bias[s]) with s the token's position in
+// its split: bias holds S fp32 values (nullptr: no bias); act 0 is the identity, 1 is ReLU.
+struct LayerEpi {
+  const float* bias = nullptr;
+  int act = 0;
+};
+
 constexpr int kCompressMaxBlocks = 512;   // bf16 gather + compress: k + 1 <= this
 hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                 const int32_t* idx, const float* w, const uint16_t* P, int residual, uint16_t* xhat,
-                                int64_t ld_out, hipStream_t stream);
+                                int64_t ld_out, hipStream_t stream, LayerEpi epi = {});
 hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps,
-                           uint16_t* out, int64_t ld_out, hipStream_t stream);
+                           uint16_t* out, int64_t ld_out, hipStream_t stream, LayerEpi epi = {});
 
 hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S, float* scores, hipStream_t stream);
 hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                const int32_t* idx, const float* w, const float* P, int residual, float* xhat,
-                               int64_t ld_out, hipStream_t stream);
+                               int64_t ld_out, hipStream_t stream, LayerEpi epi = {});
 hipError_t launch_dyn_f32(const float* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps, float* out,
-                          int64_t ld_out, hipStream_t stream);
+                          int64_t ld_out, hipStream_t stream, LayerEpi epi = {});
 
 }  // namespace avey

@@ -65,7 +65,8 @@ __global__ void __launch_bounds__(256) compress_f32_kernel(const float* __restri
                                                             int64_t ld_x, int S, int k, int n_s,
                                                             const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                             const float* __restrict__ P, int residual,
-                                                            float* __restrict__ xhat, int64_t ld_out) {
+                                                            float* __restrict__ xhat, int64_t ld_out,
+                                                            LayerEpi epi) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= B * N * d) return;
   const int f = (int)(e % d);
@@ -88,12 +89,15 @@ __global__ void __launch_bounds__(256) compress_f32_kernel(const float* __restri
     }
   }
   if (residual) acc += xb[t * ld_x + f];
+  if (epi.bias) acc += epi.bias[s];
+  if (epi.act) acc = fmaxf(acc, 0.f);
   xhat[(b * N + t) * ld_out + f] = acc;
 }
 
 // One workgroup per (b, token p): cosine row G_p., its sum, then the mixed output row.
 __global__ void __launch_bounds__(256) dyn_f32_kernel(const float* __restrict__ z, int64_t N, int m_t, int64_t ld_z,
-                                                       int S, float eps, float* __restrict__ out, int64_t ld_out) {
+                                                       int S, float eps, float* __restrict__ out, int64_t ld_out,
+                                                       LayerEpi epi) {
   __shared__ float g[512];
   __shared__ float red[4];
   const int64_t bt = blockIdx.x;
@@ -115,10 +119,13 @@ __global__ void __launch_bounds__(256) dyn_f32_kernel(const float* __restrict__ 
   }
   const float r = block_sum(part, red);   // contains a barrier: g[] is complete afterwards
   const float den = r + eps;
+  const float bv = epi.bias ? epi.bias[t - base] : 0.f;
   for (int f = threadIdx.x; f < m_t; f += 256) {
     float acc = 0.f;
     for (int q = 0; q < nv; ++q) acc = fmaf(g[q], zb[(base + q) * ld_z + f], acc);
-    out[(b * N + t) * ld_out + f] = acc / den;
+    float y = acc / den + bv;
+    if (epi.act) y = fmaxf(y, 0.f);
+    out[(b * N + t) * ld_out + f] = y;
   }
 }
 
@@ -133,18 +140,18 @@ hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S
 
 hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                const int32_t* idx, const float* w, const float* P, int residual, float* xhat,
-                               int64_t ld_out, hipStream_t stream) {
+                               int64_t ld_out, hipStream_t stream, LayerEpi epi) {
   const int n_s = (int)((N + S - 1) / S);
   const int64_t total = B * N * d;
   hipLaunchKernelGGL(compress_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, x, B, N, d,
-                     ld_x, S, k, n_s, idx, w, P, residual, xhat, ld_out);
+                     ld_x, S, k, n_s, idx, w, P, residual, xhat, ld_out, epi);
   return hipGetLastError();
 }
 
 hipError_t launch_dyn_f32(const float* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps, float* out,
-                          int64_t ld_out, hipStream_t stream) {
+                          int64_t ld_out, hipStream_t stream, LayerEpi epi) {
   hipLaunchKernelGGL(dyn_f32_kernel, dim3((unsigned)(B * N)), dim3(256), 0, stream, z, N, m_t, ld_z, S, eps, out,
-                     ld_out);
+                     ld_out, epi);
   return hipGetLastError();
 }
 

@@ -77,6 +77,9 @@ def algorithmic(cfg):
                      "bytes": (k + 2) * B * N * d * eb + S * (k + 1) * S * eb},
         # read the tail once, write the output once
         "dyn": {"flop": 4.0 * B * n_s * S * S * m_t, "bytes": 2 * B * N * m_t * eb},
+        # contextualizer layers outside the step: the tail in, the output out, V and the bias once
+        "static_layer": {"flop": 2.0 * B * n_s * S * S * m_t, "bytes": 2 * B * N * m_t * eb + S * S * eb + S * 4},
+        "dyn_layer": {"flop": 4.0 * B * n_s * S * S * m_t, "bytes": 2 * B * N * m_t * eb + S * 4},
     }
 
 
@@ -126,6 +129,41 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     }
 
 
+def time_layers(A, cfg, inp, z_tail, work, steps: int, peak: float):
+    """The static and dynamic contextualizer layers (bias and ReLU) on the same tail, timed apart
+    from the step with HIP events on the launch stream; not part of the step's throughput."""
+    import numpy as np
+    import torch
+    from synth import layer_params
+    V, bias = layer_params(inp)
+    if cfg.dtype == "bf16":
+        Vd = torch.from_numpy(np.ascontiguousarray(V).view(np.int16)).to("cuda").view(torch.bfloat16)
+    else:
+        Vd = torch.from_numpy(V).to("cuda")
+    bd = torch.from_numpy(bias).to("cuda")
+    out = torch.empty((cfg.B, cfg.N, cfg.m_t), device="cuda", dtype=z_tail.dtype)
+    calls = {
+        "static_layer": lambda: A.avey_static_layer(z_tail, Vd, cfg.S, bd, "relu", out=out),
+        "dyn_layer": lambda: A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu", out=out),
+    }
+    res = {}
+    for name, call in calls.items():
+        for _ in range(5):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for j in range(steps):
+            call()
+            ev[j + 1].record()
+        torch.cuda.synchronize()
+        t = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for j in range(steps)])) * 1e-3
+        res[name] = {"avg_us": round(t * 1e6, 3),
+                     "hbm_frac": round(work[name]["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4),
+                     "mfma_frac": round(work[name]["flop"] / t / 1e12 / peak, 4),
+                     "launches": steps, "act": "relu", "bias": True}
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +172,8 @@ def main(argv=None):
     ap.add_argument("--config", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the separate timing of the static and dynamic layers (bias + ReLU)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (the "
                          "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -255,6 +295,8 @@ def main(argv=None):
         "dyn_mfma_frac": round(work["dyn"]["flop"] / dyn_t / 1e12 / peak, 4),
         "kernels": {n: {kk: round(v, 3) for kk, v in e.items()} for n, e in kern.items()},
     }
+    if not args.no_layers:
+        result["layers"] = time_layers(A, cfg, inp, z_tail, work, max(10, args.steps // 2), peak)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
         result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 2)

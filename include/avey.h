@@ -191,7 +191,7 @@ avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_
  *   n_p = z_p / |z_p|  (0 for a zero row)
  *   G_pq = n_p . n_q,   r_p = sum_q G_pq
  *   out_p = sum_q G_pq z_q / (r_p + eps)
- * The activation and bias that follow in the full layer are not applied.
+ * The bias and activation of the full layer are not applied (avey_dyn_layer applies them).
  *
  *   z_tail  [B, N, m_t] row stride ld_z (input; point it at the first tail column of Z)
  *   out     [B, N, m_t] row stride ld_out, dtype dt (output)
@@ -201,6 +201,48 @@ avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_
 avey_status avey_dyn_context(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t,
                              int64_t ld_z, int32_t S, float eps, void* out, int64_t ld_out,
                              void* stream);
+
+/*
+ * Activation sigma of the contextualizer layers. The pages require only that it be monotone
+ * ([summary] 4.2 and appendix A, relevance-monotonic updates); identity and ReLU are offered.
+ */
+typedef enum { AVEY_ACT_IDENTITY = 0, AVEY_ACT_RELU = 1 } avey_act;
+
+/*
+ * avey_dyn_layer -- dynamic contextualizer layer c_dyn = sigma(S~ Z_t + b) ([notes] 关键设计 2
+ * and 3): the core of avey_dyn_context, then for each valid token p of split i
+ *   out_p = act(core_p + bias[p - i S])      (one bias value per token position of a split)
+ *
+ *   z_tail, out, S, eps  as avey_dyn_context
+ *   bias    [S] float32 (input), or NULL for no bias
+ *   act     an avey_act (other values: AVEY_ERR_SHAPE)
+ * For AVEY_BF16 the bias is added to the fp32 value before the activation and the single
+ * rounding to bf16.
+ */
+avey_status avey_dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t,
+                           int64_t ld_z, int32_t S, float eps, const float* bias, int32_t act,
+                           void* out, int64_t ld_out, void* stream);
+
+/*
+ * avey_static_layer -- static contextualizer layer c_static = sigma(V Z_t + b) ([notes]
+ * 关键设计 2: a learned linear map of the split's tail followed by the activation; [summary]
+ * 4.2: its weights do not depend on the input). V mixes the S token positions of a split.
+ *
+ * For each split (b, i), with Z_i its S tail rows (padding rows zero):
+ *   out[s][c] = act( sum_q V[s][q] Z_i[q][c] + bias[s] )
+ * and the valid rows s are written.
+ *
+ *   z_tail  [B, N, m_t] row stride ld_z (input; point it at the first tail column of Z)
+ *   V       [S, S] contiguous, dtype dt (input): V[s][q] weighs token q for output token s
+ *   bias    [S] float32 (input), or NULL for no bias
+ *   act     an avey_act (other values: AVEY_ERR_SHAPE)
+ *   out     [B, N, m_t] row stride ld_out, dtype dt (output)
+ * Computed by the kernels of avey_select_compress with no retrieved block (X_cat = Z_i, P = V,
+ * no residual). For AVEY_BF16 the result is rounded to bf16 once, after bias and activation.
+ */
+avey_status avey_static_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t,
+                              int64_t ld_z, int32_t S, const void* V, const float* bias,
+                              int32_t act, void* out, int64_t ld_out, void* stream);
 
 #ifdef __cplusplus
 }

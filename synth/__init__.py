@@ -9,6 +9,7 @@ from .inputs import (  # noqa: F401
     Inputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    layer_params,
     make_inputs,
     n_splits,
 )

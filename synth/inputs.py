@@ -200,3 +200,30 @@ def make_inputs(cfg: Config | str, seed: int | None = None) -> Inputs:
         raise ValueError(cfg.z_kind)
 
     return Inputs(cfg=cfg, x=x, P=P, z=z, meta={"dups": dups})
+
+
+def layer_params(inp: Inputs) -> tuple[np.ndarray, np.ndarray]:
+    """Weights of a static contextualizer layer and one bias vector for either layer.
+
+    * ``V`` [S, S], stored as ``x`` is: a Toeplitz band with signed values, decaying with the
+      distance from the diagonal, plus a small dense signed part. Learned static matrices come
+      out Toeplitz-like, diagonally dominant and concentrated near the diagonal, with signed
+      weights (paperlayer.ai "Avey-B" summary, appendix B).
+    * ``bias`` [S] float32, one value per token position of a split: N(0, 1) scaled by the spread
+      of the tail values and shifted down by their mean, so that a ReLU after the layer clips a
+      good part of each output while leaving the rest (statistics from at most 4096 rows).
+
+    Drawn from the seed's streams 6 and 7, after the six ``make_inputs`` uses.
+    """
+    cfg = inp.cfg
+    S = cfg.S
+    r_v, r_b = (np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(cfg.seed).spawn(8)[6:])
+    delta = np.arange(S)[:, None] - np.arange(S)[None, :]
+    diag = r_v.standard_normal(2 * S - 1).astype(np.float32)
+    v32 = np.exp(-np.abs(delta) / 4.0).astype(np.float32) * diag[delta + S - 1]
+    v32 += np.float32(0.5 / np.sqrt(S)) * r_v.standard_normal((S, S), dtype=np.float32)
+    V = _store(cfg, v32)
+    sample = inp.z_tail_f64(0, slice(0, min(cfg.N, 4096)))
+    mu, sd = float(sample.mean()), float(sample.std())
+    bias = (sd * r_b.standard_normal(S) - mu).astype(np.float32)
+    return V, bias

@@ -143,3 +143,31 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(A.AveyError):
         A.avey_split_rank(torch.zeros(1, 1024, 64, dtype=torch.bfloat16), 64, 3)
+
+
+def test_dyn_layer_validation(lib):
+    f = lib.avey_dyn_layer
+    # (z_tail, dt, B, N, m_t, ld_z, S, eps, bias, act, out, ld_out, stream)
+    assert f(None, 1, 0, 1024, 64, 64, 64, 1e-8, None, 0, None, 64, None) == OK
+    assert f(None, 1, 1, 1024, 64, 64, 64, 1e-8, None, 0, P16, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, None, 2, P16, 64, None) == SHAPE     # unknown act
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, None, -1, P16, 64, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, P16 + 2, 1, P16, 64, None) == ALIGN  # bias not 4-aligned
+    assert f(P16, 1, 1, 1024, 64, 64, 96, 1e-8, None, 1, P16, 64, None) == UNSUP    # bf16 S % 64
+    assert f(P16, 9, 1, 1024, 64, 64, 64, 1e-8, None, 0, P16, 64, None) == DTYPE
+
+
+def test_static_layer_validation(lib):
+    f = lib.avey_static_layer
+    # (z_tail, dt, B, N, m_t, ld_z, S, V, bias, act, out, ld_out, stream)
+    assert f(None, 1, 0, 1024, 64, 64, 64, None, None, 0, None, 64, None) == OK
+    assert f(P16, 1, 1, 1024, 64, 64, 64, None, None, 0, P16, 64, None) == NULL      # V
+    assert f(None, 1, 1, 1024, 64, 64, 64, P16, None, 0, P16, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, P16, None, 0, None, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, P16, None, 5, P16, 64, None) == SHAPE     # unknown act
+    assert f(P16, 1, 1, 1024, 64, 64, 64, P16 + 8, None, 0, P16, 64, None) == ALIGN  # bf16 V 16-aligned
+    assert f(P16, 0, 1, 1024, 64, 64, 64, P16 + 2, None, 0, P16, 64, None) == ALIGN  # f32 V 4-aligned
+    assert f(P16, 1, 1, 1024, 64, 64, 64, P16, P16 + 1, 0, P16, 64, None) == ALIGN   # bias
+    assert f(P16, 1, 1, 1024, 64, 64, 32, P16, None, 0, P16, 64, None) == UNSUP     # bf16 S % 64
+    assert f(P16, 1, 1, 1024, 64, 32, 64, P16, None, 0, P16, 64, None) == SHAPE     # ld_z < m_t
+    assert f(P16, 1, 1, 1024, 64, 64, 0, P16, None, 0, P16, 64, None) == SHAPE      # S < 1

@@ -1,0 +1,187 @@
+"""GPU parity of the two contextualizer layers (static c = act(V Z_t + b), dynamic
+c = act(S~ Z_t + b)) against the float64 oracle, through the C ABI.
+
+Rows are compared as in the other parity tests (||g - o||_2 / ||o||_2 per token). With ReLU the
+denominator is the oracle's row before the activation: ReLU is 1-Lipschitz, so a pre-activation
+error within the tolerance stays within it after the activation, while the clipped row itself
+can be arbitrarily small. Where the oracle's pre-activation value lies below minus the
+tolerance times its row norm, the GPU output must be exactly zero.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_free_long_amd as A
+from oracle import avey_oracle as O
+from synth import CONFIGS, Config, layer_params, make_inputs
+
+from helpers import TOL, dev_tensor, host_f64, split_rows_of, upload
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # 8 splits of 256 (last one 208 tokens), 2 sequences, m_t = 320 (a 256-feature tile and a 64-feature one)
+    "small_bf16": Config("small_bf16", B=2, N=2000, d=256, S=256, k=3, m_t=320, m=384, dtype="bf16",
+                         x_dist="mixture", n_centroids=16),
+    # S = 512 (two 256-token halves per split), last split 40 tokens
+    "s512_bf16": Config("s512_bf16", B=1, N=1576, d=128, S=512, k=2, m_t=192, m=256, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+    # S = 64: a quarter of an output tile per split
+    "s64_bf16": Config("s64_bf16", B=1, N=700, d=64, S=64, k=2, m_t=64, m=128, dtype="bf16",
+                       x_dist="mixture", n_centroids=8),
+    "tiny": CONFIGS["tiny"],
+}
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def check_layer(g, pre, post, cfg, tol, what):
+    """g: GPU output [B, N, m_t]; pre / post: oracle rows per split before / after act."""
+    worst = 0.0
+    for (b, i), o_post in post.items():
+        o_pre = pre[(b, i)]
+        rows = g[b, split_rows_of(cfg.N, cfg.S, i)]
+        num = np.linalg.norm(rows - o_post, axis=-1)
+        den = np.maximum(np.linalg.norm(o_pre, axis=-1), 1e-30)
+        err = float((num / den).max())
+        assert err <= tol, f"{what} split {(b, i)}: {err:.3e}"
+        worst = max(worst, err)
+        clipped = o_pre < -tol * den[:, None]
+        if o_post is not o_pre:
+            assert np.all(rows[clipped] == 0.0), f"{what} split {(b, i)}: ReLU left a negative value"
+            assert np.all(rows >= 0.0)
+    return worst
+
+
+@pytest.mark.parametrize("act", ["identity", "relu"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_layers_parity(gpu_ok, name, act):
+    cfg = CASES[name]
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    V, bias = layer_params(inp)
+    say(f"{name}/{act}: static + dynamic layer B={cfg.B} N={cfg.N} S={cfg.S} m_t={cfg.m_t}")
+    _, _, _, z_tail = upload(inp)
+    Vd = dev_tensor(V, cfg.dtype)
+    bd = torch.from_numpy(bias).to("cuda")
+    g_s = host_f64(A.avey_static_layer(z_tail, Vd, cfg.S, bd, act))
+    g_d = host_f64(A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, act))
+    torch.cuda.synchronize()
+
+    z64 = inp.z_tail_f64()
+    V64 = inp._as_f64(V)
+    b64 = bias.astype(np.float64)
+    s_pre = O.static_layer(z64, cfg.S, V64, b64, "identity")
+    s_post = s_pre if act == "identity" else O.static_layer(z64, cfg.S, V64, b64, act)
+    d_pre = O.dyn_layer(z64, cfg.S, cfg.eps, b64, "identity")
+    d_post = d_pre if act == "identity" else O.dyn_layer(z64, cfg.S, cfg.eps, b64, act)
+    ws = check_layer(g_s, s_pre, s_post, cfg, tol, "static")
+    wd = check_layer(g_d, d_pre, d_post, cfg, tol, "dynamic")
+    if act == "relu":
+        frac = np.mean([np.mean(v == 0.0) for v in d_post.values()])
+        assert 0.05 < frac < 0.95, f"bias leaves ReLU nothing to do: {frac:.2f} of outputs zero"
+    say(f"{name}/{act}: worst relative errors static {ws:.2e}, dynamic {wd:.2e}")
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "s512_bf16", "tiny"])
+def test_static_identity_and_permutation_exact(gpu_ok, name):
+    """V = I returns Z_t bit for bit; a permutation V moves whole tokens (a slot past the split's
+    valid tokens gives a zero row); a bias of zeros with ReLU clips exactly the negatives."""
+    cfg = CASES[name]
+    inp = make_inputs(cfg)
+    say(f"{name}: static layer with identity and permutation V")
+    _, _, _, z_tail = upload(inp)
+    tdt = z_tail.dtype
+    S = cfg.S
+    eye = torch.eye(S, dtype=tdt, device="cuda")
+    g = A.avey_static_layer(z_tail, eye, S)
+    assert torch.equal(g, z_tail)
+    perm = np.random.default_rng(5).permutation(S)
+    Vp = torch.from_numpy(np.eye(S, dtype=np.float32)[perm]).to("cuda").to(tdt)
+    g = host_f64(A.avey_static_layer(z_tail, Vp, S))
+    z64 = inp.z_tail_f64()
+    for b in range(cfg.B):
+        for i in range(cfg.n_s):
+            r = split_rows_of(cfg.N, S, i)
+            for s_ in range(r.stop - r.start):
+                src = i * S + perm[s_]
+                want = z64[b, src] if src < cfg.N else np.zeros(cfg.m_t)
+                assert np.array_equal(g[b, r.start + s_], want), (b, i, s_)
+    neg = -z_tail                                     # exact negation: every value <= 0
+    g = A.avey_static_layer(neg, eye, S, torch.zeros(S, device="cuda"), "relu")
+    assert torch.count_nonzero(g).item() == 0
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "s512_bf16", "tiny"])
+def test_dyn_layer_defaults_equal_core(gpu_ok, name):
+    cfg = CASES[name]
+    inp = make_inputs(cfg)
+    say(f"{name}: dynamic layer without bias and activation vs the core")
+    _, _, _, z_tail = upload(inp)
+    core = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
+    lay = A.avey_dyn_layer(z_tail, cfg.S, cfg.eps)
+    assert torch.equal(core, lay)
+
+
+def test_static_then_dynamic(gpu_ok):
+    """S -> D: the static layer's output (contiguous, row stride m_t) feeds the dynamic layer.
+    Each GPU layer is compared with the oracle on the GPU's own input to that layer."""
+    cfg = CASES["small_bf16"]
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    V, bias = layer_params(inp)
+    say("static (ReLU) -> dynamic (ReLU), small_bf16")
+    _, _, _, z_tail = upload(inp)
+    bd = torch.from_numpy(bias).to("cuda")
+    h = A.avey_static_layer(z_tail, dev_tensor(V, cfg.dtype), cfg.S, bd, "relu")
+    out = A.avey_dyn_layer(h, cfg.S, cfg.eps, bd, "relu")
+    torch.cuda.synchronize()
+    h64, g = host_f64(h), host_f64(out)
+    b64 = bias.astype(np.float64)
+    pre = O.dyn_layer(h64, cfg.S, cfg.eps, b64, "identity")
+    post = O.dyn_layer(h64, cfg.S, cfg.eps, b64, "relu")
+    check_layer(g, pre, post, cfg, tol, "S->D dynamic")
+    # the static layer's own output, against the oracle on the original tail
+    z64 = inp.z_tail_f64()
+    V64 = inp._as_f64(V)
+    check_layer(h64, O.static_layer(z64, cfg.S, V64, b64, "identity"),
+                O.static_layer(z64, cfg.S, V64, b64, "relu"), cfg, tol, "S->D static")
+
+
+def test_layers_full_size_sampled(gpu_ok):
+    """The 2 x 32768-token workload (S = 256, m_t = 1536 at row stride 3072), both layers with
+    bias and ReLU, checked on sampled splits including the first and the last."""
+    cfg = CONFIGS["long"]
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    V, bias = layer_params(inp)
+    say(f"long: static + dynamic layer, B={cfg.B} N={cfg.N} m_t={cfg.m_t}")
+    _, _, _, z_tail = upload(inp)
+    bd = torch.from_numpy(bias).to("cuda")
+    g_s = A.avey_static_layer(z_tail, dev_tensor(V, cfg.dtype), cfg.S, bd, "relu")
+    g_d = A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    picks = sorted({(0, 0), (cfg.B - 1, cfg.n_s - 1)} |
+                   {(int(b), int(i)) for b, i in zip(rng.integers(0, cfg.B, 6), rng.integers(0, cfg.n_s, 6))})
+    V64 = inp._as_f64(V)
+    b64 = bias.astype(np.float64)
+    for b, i in picks:
+        r = split_rows_of(cfg.N, cfg.S, i)
+        zb = inp.z_tail_f64(b)
+        gs = host_f64(g_s[b, r])
+        gd = host_f64(g_d[b, r])
+        s_pre = O.static_layer_split(zb, cfg.S, V64, b64, "identity", i)
+        d_pre = O.dyn_layer_split(zb, cfg.S, cfg.eps, b64, "identity", i)
+        for g, pre, what in ((gs, s_pre, "static"), (gd, d_pre, "dynamic")):
+            post = np.maximum(pre, 0.0)
+            den = np.linalg.norm(pre, axis=-1)
+            err = float((np.linalg.norm(g - post, axis=-1) / den).max())
+            assert err <= tol, f"{what} split {(b, i)}: {err:.3e}"
+            assert np.all(g[pre < -tol * den[:, None]] == 0.0)
+    say(f"long: {len(picks)} sampled splits within {tol}")
