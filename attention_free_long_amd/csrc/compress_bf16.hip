@@ -317,6 +317,369 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Persistent variant for problems with at least one unit per CU. A unit is 256 features x all
+// output tokens of a split (256 of them; at S = 512 two units per split), one 8-wave workgroup
+// per CU in a 2 x 4 wave grid (each wave 128 features x 64 tokens, as above), a 4-stage ring of
+// 32 KiB (three chunks in flight) and the next unit's first three chunks copied while the
+// current one finishes. Compared with the tiled kernel, each gathered X row is staged once per
+// feature tile instead of once per 128 output tokens.
+//   * Features of wave (wm, mb): 64 mb + 32 wm + (0..31), so that the four 64-feature slices of
+//     the output tile are whole 128-byte row pieces.
+//   * Residual: the split's own block comes last; in the chunk of it that holds a wave's token
+//     block nb, 8 more MFMAs of that chunk's X^T fragments with an identity B operand add
+//     X_i[s][f] to C[f][s] exactly.
+//   * Epilogue, through stage 3 in four rounds (one 64-feature slice each): lanes write their
+//     4-feature groups into a [256 tokens][64 features] bf16 tile, then 8 lanes per token store
+//     whole 128-byte rows (scattered 8-byte stores would cost a write request per lane).
+//   * Source splits and weights of the next unit are read with scalar loads into a second LDS
+//     table, so that the copies stay the only vector-memory operations of the K loop.
+namespace unit {
+
+constexpr int TU = 256;                 // output tokens per unit
+constexpr int USTAGE = XS + TU * PB;    // 32 KiB: 32 X rows of 256 features + 256 P rows
+
+struct UnitPos {
+  int64_t b;
+  int i, su, f_base;
+};
+
+typedef const __attribute__((address_space(4))) int32_t* sc_i32;
+typedef const __attribute__((address_space(4))) float* sc_f32;
+
+// Compile-time pipeline position 0..3 of a chunk (its stage).
+template <int P>
+using Pos = std::integral_constant<int, P>;
+
+__global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a) {
+  __shared__ __align__(16) uint8_t st0[USTAGE], st1[USTAGE], st2[USTAGE], st3[USTAGE];
+  __shared__ int s_tok0[2][MAXBLK];   // per unit (two tables): first token of block r's split
+  __shared__ float s_wt[2][MAXBLK];   // weight of block r
+  __shared__ int s_slow[2][8];        // per wave: a weight outside [2^-60, 2^60]
+  __shared__ float s_bias[512];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6), wm = wave >> 2, wn = wave & 3;
+
+  // XCD x owns units [xs, xs + cnt); its workgroup l takes every Gx-th of them from l.
+  const int G = gridDim.x, wg = blockIdx.x, xcd = wg % NXCD, l = wg / NXCD;
+  const int Gx = (G - xcd + NXCD - 1) / NXCD;
+  const int64_t q8 = a.tiles / NXCD, r8 = a.tiles % NXCD;
+  const int64_t xs = xcd * q8 + (xcd < r8 ? xcd : r8), cnt = q8 + (xcd < r8 ? 1 : 0);
+  int64_t t = l;
+  if (t >= cnt) return;
+
+  const int KP = (a.k + 1) * a.S;
+  const int cpb = a.S / KH;               // chunks per block
+  const int nk = KP / KH;
+  const int nk4 = (nk + 3) / 4 * 4;       // padded with zero chunks: every unit starts on stage 0
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((int64_t)a.S * KP * 2));
+
+  auto unit_pos = [&](int64_t tl) {
+    UnitPos u;
+    const int64_t L = xs + tl;
+    const int ft = (int)(L % a.f_tiles);
+    const int64_t rest = L / a.f_tiles;
+    u.su = (int)(rest % a.s_tiles);
+    const int64_t split = rest / a.s_tiles;
+    u.b = split / a.n_s;
+    u.i = (int)(split % a.n_s);
+    u.f_base = ft * TF;
+    return u;
+  };
+  auto fill_table = [&](const UnitPos& u, int bf) {
+    const int64_t row = (u.b * a.n_s + u.i) * (int64_t)a.k;
+    int slow = 0;
+    for (int r = wave; r <= a.k; r += 8) {
+      int src = u.i;
+      float wr = 1.f;
+      if (r) {
+        src = ((sc_i32)a.idx)[row + r - 1];
+        if (src >= 0) wr = ((sc_f32)a.w)[row + r - 1];
+      }
+      // a negative index is an empty block: its copies load zeros, its weight is taken as 1
+      s_tok0[bf][r] = src < 0 ? kEmptyBlock : min(src, a.n_s - 1) * a.S;
+      s_wt[bf][r] = wr;
+      if (!(wr >= 0x1p-60f && wr <= 0x1p60f)) slow = 1;   // also catches NaN
+    }
+    s_slow[bf][wave] = slow;
+  };
+  s_bias[tid] = (a.epi.bias && tid < a.S) ? a.epi.bias[tid] : 0.f;
+
+  // ---- copy side: the unit whose chunks are being copied (the next one near a unit's end)
+  __amdgpu_buffer_rsrc_t xr;
+  int c_bf = 0, c_su = 0, c_fb = 0;
+  auto set_copy_unit = [&](const UnitPos& u, int bf) {
+    xr = make_rsrc(a.x + u.b * a.N * a.ld_x, (uint32_t)(a.N * a.ld_x * 2));
+    c_bf = bf;
+    c_su = u.su;
+    c_fb = u.f_base;
+  };
+  // Chunk c covers block (c / cpb + 1) mod (k + 1): blocks 1..k, then block 0.
+  auto chunk_block = [&](int c, int& r, int& j) {
+    const int q = c / cpb;
+    r = q < a.k ? q + 1 : 0;
+    j = c - q * cpb;
+  };
+  auto chunk_tok0 = [&](int kc) {
+    int r, j;
+    chunk_block(kc, r, j);
+    return uniform(s_tok0[c_bf][r]) + j * KH;
+  };
+  // Copy n of chunk kc into stage st: n = 0, 1 are X rows 4 w + 2 n, + 1 (1 KiB), n = 2, 3 are
+  // P rows 32 w + 16 (n - 2) .. + 15. Tokens past N, features past d and rows past S load zeros.
+  auto copy = [&](int kc, uint8_t* st, bool valid, int n, int tok0) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (n < 2) {
+      const int tr = wave * 4 + n * 2 + (ln >> 5);
+      const int p = ln & 31;
+      const int c = (p >> 1) ^ (2 * (tr & 3));
+      const int f = c_fb + c * 16 + (p & 1) * 8;
+      const int64_t tok = (int64_t)tok0 + tr;
+      const bool ok = valid && tok >= 0 && tok < a.N && f < a.d;
+      dma16(xr, st + (wave * 4 + n * 2) * XB, ok ? (uint32_t)((tok * a.ld_x + f) * 2) : OOB, 0);
+    } else {
+      const int r0 = wave * 32 + (n - 2) * 16;
+      const int row = r0 + (ln >> 2);
+      const int s = c_su * TU + row;
+      const uint32_t piece = (uint32_t)((ln & 3) ^ (int)sw4(row));
+      int r, j;
+      chunk_block(kc, r, j);
+      const int kk0 = r * a.S + j * KH;
+      const bool ok = valid && s < a.S;
+      dma16(pr, st + XS + r0 * PB, ok ? (uint32_t)s * (uint32_t)KP * 2u + 16u * piece : OOB, (uint32_t)kk0 * 2u);
+    }
+  };
+  auto dma = [&](int kc, uint8_t* st, bool valid) {
+    const int tok0 = chunk_tok0(kc);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) copy(kc, st, valid, n, tok0);
+  };
+
+  // ---- fragments (transpose reads of X for A, P rows for B), feature blocks 64 mb + 32 wm
+  uint32_t offA[4];
+  {
+    const int s2 = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
+    const uint32_t row = (uint32_t)(8 * (lane >> 5) + ((lane & 15) >> 2)) * XB;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      offA[mb] = row + (uint32_t)((((4 * mb + 2 * wm) ^ (2 * s2)) + g1) << 5) + 8u * (lane & 3);
+  }
+  uint32_t offB[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int rb = wn * 64 + (lane & 31);
+    offB[ks] = (uint32_t)XS + (uint32_t)rb * PB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(rb)) << 4);
+  }
+  f32x16 acc[4][2];
+  uint4 ra0[4], rb0[2], ra1[4], rb1[2];
+  auto fetchA = [&](const uint8_t* st, int ks, uint4 (&ra)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const uint2 lo = lds_read_tr8(st, offA[mb] + (uint32_t)(16 * ks) * XB);
+      const uint2 hi = lds_read_tr8(st, offA[mb] + (uint32_t)(16 * ks + 4) * XB);
+      ra[mb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
+  auto fetchB = [&](const uint8_t* st, int ks, float wt, uint4 (&rb)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint4 v = lds_read16(st, offB[ks] + nb * 32 * PB);
+      rb[nb] = wt == 1.f ? v : scale8(v, wt);
+    }
+  };
+
+  // ---- compute side: the unit being multiplied
+  int bf = 0, cur_su = 0;
+  bool slow = false;
+  auto wt_of = [&](int c) {   // weight applied to chunk c's P fragments (slow path only)
+    if (!slow || c >= nk) return 1.f;
+    int r, j;
+    chunk_block(c, r, j);
+    return s_wt[bf][r];
+  };
+  // After chunk c: at the last chunk of a retrieved block r, multiply the accumulator by
+  // w_r / w_{r+1} (by w_k after block k).
+  auto post = [&](int c) {
+    if (slow || c >= nk || (c + 1) % cpb) return;
+    int r, j;
+    chunk_block(c, r, j);
+    if (r == 0) return;
+    const float f = r < a.k ? s_wt[bf][r] / s_wt[bf][r + 1] : s_wt[bf][r];
+    if (f == 1.f) return;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] *= f;
+  };
+  // Residual. Identity fragment of k-step ks: lane l (column l & 31) holds 1.0 at element
+  // (l & 31) - 16 ks - 8 (l >> 5) when that lies in 0..7. Token block nb of this wave sits in
+  // chunk k cpb + 8 su + 2 wn + nb; block 0 starts on an even chunk (cpb is even), so that chunk
+  // is at an odd pipeline position exactly when nb = 1.
+  uint4 idB[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int j = (lane & 31) - 16 * ks - 8 * (lane >> 5);
+    uint32_t wv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wv[q] = (j >> 1) == q ? ((j & 1) ? 0x3F800000u : 0x00003F80u) : 0u;
+    idB[ks] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+  auto res_chunk = [&](int nb) {
+    const int jt = cur_su * 8 + 2 * wn + nb;
+    return jt < cpb ? a.k * cpb + jt : -1;
+  };
+  auto res_mfma = [&](auto POS, bool on, const uint4 (&ra)[4], int ks) {
+    if (on) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        acc[mb][POS.value & 1] = mfma32(as_bf16x8(ra[mb]), as_bf16x8(idB[ks]), acc[mb][POS.value & 1]);
+    }
+  };
+
+  // One chunk c from stage st at position POS (k-step-0 fragments already in ra0 / rb0). The 4
+  // copies of chunk kc of the copy unit into dst go between the MFMA groups; with next, the
+  // next chunk's wait and barrier come before the last group and its first fragments are read
+  // under it.
+  auto compute_pipe = [&](auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
+                          const uint8_t* next) {
+    const int tok0 = chunk_tok0(kc);
+    const float wt = wt_of(c);
+    const bool ron = a.residual && (c == res_chunk(0) || c == res_chunk(1));
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+    fetchA(st, 1, ra1);
+    fetchB(st, 1, wt, rb1);
+    copy(kc, dst, valid, 0, tok0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 2; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+    copy(kc, dst, valid, 1, tok0);
+    __builtin_amdgcn_sched_barrier(0);
+    res_mfma(POS, ron, ra0, 0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
+    copy(kc, dst, valid, 2, tok0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) {
+      // 3 of this chunk's copies and the 4 of the previous one may stay in flight
+      WAIT_KEEP(7);
+      const float wnx = wt_of(c + 1);
+      fetchA(next, 0, ra0);
+      fetchB(next, 0, wnx, rb0);
+    }
+#pragma unroll
+    for (int mb = 2; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
+    copy(kc, dst, valid, 3, tok0);
+    __builtin_amdgcn_sched_barrier(0);
+    res_mfma(POS, ron, ra1, 1);
+    post(c);
+  };
+
+  UnitPos cur = unit_pos(t);
+  fill_table(cur, 0);
+  __syncthreads();
+  set_copy_unit(cur, 0);
+  dma(0, st0, true);
+  dma(1, st1, 1 < nk);
+  dma(2, st2, 2 < nk);
+
+  const bool relu = a.epi.act != 0;
+  for (;;) {
+    const bool has_next = t + Gx < cnt;
+    UnitPos nx = cur;
+    if (has_next) nx = unit_pos(t + Gx);
+    cur_su = cur.su;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+
+    // Every chunk is exactly 4 copies per wave and every copy is issued unconditionally, so
+    // WAIT_KEEP(8) at a chunk boundary leaves exactly the two newer chunks in flight (any
+    // epilogue stores of the previous unit are older and only make the wait stricter).
+    WAIT_KEEP(8);
+    if (has_next) fill_table(nx, bf ^ 1);   // its readers come after later barriers
+    {
+      int sl = 0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) sl |= s_slow[bf][w];
+      slow = sl != 0;
+    }
+    fetchA(st0, 0, ra0);
+    fetchB(st0, 0, wt_of(0), rb0);
+    for (int kc = 0; kc + 4 < nk4; kc += 4) {
+      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      compute_pipe(Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
+      compute_pipe(Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
+      compute_pipe(Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+    }
+    {
+      // last four chunks; the next unit's first three are copied meanwhile
+      const int kc = nk4 - 4;
+      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      if (has_next) set_copy_unit(nx, bf ^ 1);
+      compute_pipe(Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
+      compute_pipe(Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
+      compute_pipe(Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
+    }
+
+    // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)
+    uint16_t* ob = a.xhat + cur.b * a.N * a.ld_out;
+    lds_sync();   // every wave is done reading stage 3
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int sl = wn * 64 + nb * 32 + (lane & 31);
+        const float bv = s_bias[(cur.su * TU + sl) & 511];
+        const uint32_t rowo = (uint32_t)sl * 128u + 8u * (uint32_t)(lane >> 5);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float y = acc[mb][nb][g * 4 + e] + bv;
+            v[e] = relu ? fmaxf(y, 0.f) : y;
+          }
+          const uint32_t pc = (uint32_t)(4 * wm + g) ^ (uint32_t)((sl >> 1) & 7);
+          *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        }
+      }
+      lds_sync();
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int sl = wave * 32 + it * 8 + (lane >> 3);
+        const int p = lane & 7;
+        const uint4 v = lds_read16(st3, (uint32_t)sl * 128u + ((uint32_t)(p ^ ((sl >> 1) & 7)) << 4));
+        const int s = cur.su * TU + sl;
+        const int64_t tok = (int64_t)cur.i * a.S + s;
+        const int f = cur.f_base + mb * 64 + p * 8;
+        if (s < a.S && tok < a.N && f < a.d) *reinterpret_cast<uint4*>(ob + tok * a.ld_out + f) = v;
+      }
+      if (mb < 3) lds_sync();
+    }
+    if (!has_next) break;
+    t += Gx;
+    cur = nx;
+    bf ^= 1;
+  }
+  wait_vmem();   // the zero-filled copies issued past the last unit land before the exit
+}
+
+}  // namespace unit
+
 }  // namespace
 
 hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
@@ -331,6 +694,19 @@ hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, 
   p.f_tiles = (d + TF - 1) / TF;
   p.residual = residual;
   p.epi = epi;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  // At least one 256 x 256 unit per CU: the persistent kernel; otherwise the tiled one, whose
+  // smaller tiles keep more CUs busy.
+  const int64_t units = B * p.n_s * ((S + unit::TU - 1) / unit::TU) * p.f_tiles;
+  if (units >= cus) {
+    p.s_tiles = (S + unit::TU - 1) / unit::TU;
+    p.tiles = units;
+    hipLaunchKernelGGL(unit::compress_unit_kernel, dim3((unsigned)cus), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
   p.tiles = B * p.n_s * p.s_tiles * p.f_tiles;
   hipLaunchKernelGGL(compress_bf16_kernel, dim3((unsigned)p.tiles), dim3(256), 0, stream, p);
   return hipGetLastError();

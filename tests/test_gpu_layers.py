@@ -185,3 +185,24 @@ def test_layers_full_size_sampled(gpu_ok):
             assert err <= tol, f"{what} split {(b, i)}: {err:.3e}"
             assert np.all(g[pre < -tol * den[:, None]] == 0.0)
     say(f"long: {len(picks)} sampled splits within {tol}")
+
+
+def test_static_layer_persistent_kernel(gpu_ok):
+    """The static layer at 256 units (2 x 32668 tokens, S = 256, m_t = 64): every split, with
+    bias and ReLU, on the persistent kernel."""
+    cfg = Config("p256", B=2, N=32668, d=64, S=256, k=0, m_t=64, m=64, dtype="bf16",
+                 x_dist="mixture", n_centroids=32, z_kind="relu2_x")
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    V, bias = layer_params(inp)
+    say(f"static layer, persistent kernel: B={cfg.B} N={cfg.N} m_t={cfg.m_t}")
+    _, _, _, z_tail = upload(inp)
+    bd = torch.from_numpy(bias).to("cuda")
+    g = host_f64(A.avey_static_layer(z_tail, dev_tensor(V, cfg.dtype), cfg.S, bd, "relu"))
+    torch.cuda.synchronize()
+    z64 = inp.z_tail_f64()
+    V64 = inp._as_f64(V)
+    b64 = bias.astype(np.float64)
+    w = check_layer(g, O.static_layer(z64, cfg.S, V64, b64, "identity"),
+                    O.static_layer(z64, cfg.S, V64, b64, "relu"), cfg, tol, "static")
+    say(f"static layer, persistent kernel: worst {w:.2e}")

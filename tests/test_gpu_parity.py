@@ -301,3 +301,46 @@ def test_side_stream_and_workspace_reuse(gpu_ok):
     torch.cuda.synchronize()
     for a_, b_ in zip(s1_ref, s1):
         assert torch.equal(a_, b_)
+
+
+# Shapes with at least one 256-feature x 256-token unit per CU (256 CUs), so that compression
+# runs on the persistent kernel, small enough for the oracle to check every split.
+PERSISTENT = {
+    # units = B * n_s * ceil(S / 256) * ceil(d / 256)
+    "s256_res": (Config("p256", B=2, N=32668, d=64, S=256, k=3, m_t=64, m=64, dtype="bf16",
+                        x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+    "s256_nores": (Config("p256", B=2, N=32668, d=64, S=256, k=3, m_t=64, m=64, dtype="bf16",
+                          x_dist="mixture", n_centroids=32, z_kind="relu2_x"), False),
+    "s512": (Config("p512", B=2, N=32468, d=128, S=512, k=7, m_t=128, m=128, dtype="bf16",
+                    x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+    "s64": (Config("p64", B=4, N=16374, d=64, S=64, k=2, m_t=64, m=64, dtype="bf16",
+                   x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+}
+
+
+@pytest.mark.parametrize("name", list(PERSISTENT))
+def test_compress_persistent_kernel(gpu_ok, name):
+    """Every split against the oracle on caller-given idx / w, with an empty block (index -1),
+    a zero weight (per-fragment weighting in that unit) and a ragged last split."""
+    cfg, residual = PERSISTENT[name]
+    inp = make_inputs(cfg)
+    say(f"persistent compress {name}: B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S} k={cfg.k} residual={residual}")
+    x, P, _, _ = upload(inp)
+    rng = np.random.default_rng(3)
+    B, n_s, k = cfg.B, cfg.n_s, cfg.k
+    idx = np.stack([rng.permutation(n_s)[:k] for _ in range(B * n_s)]).reshape(B, n_s, k).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, size=(B, n_s, k)).astype(np.float32)
+    idx[0, 5, k - 1] = -1
+    w[0, 5, k - 1] = 0.0
+    w[B - 1, n_s - 1, 0] = 0.0
+    g = A.avey_select_compress(x, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), P, cfg.S,
+                               residual=residual)
+    torch.cuda.synchronize()
+    got = host_f64(g)
+    ref = O.select_compress(inp.x_f64(), cfg.S, idx, w.astype(np.float64), inp.P_f64(), residual=residual)
+    worst = 0.0
+    for (b, i), rows in ref.items():
+        err = row_rel_err(got[b, split_rows_of(cfg.N, cfg.S, i)], rows)
+        assert err <= TOL["bf16"]["out"], f"xhat split {(b, i)}: {err:.3e}"
+        worst = max(worst, err)
+    say(f"persistent compress {name}: worst xhat error {worst:.2e}")
