@@ -522,19 +522,40 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Epilogue of feature tile ft, through stage 3 in four rounds of 64 features: each lane writes
+  // its 4-feature groups into a [256 tokens][64 features] bf16 tile (16-byte piece c of row t at
+  // c ^ ((t >> 1) & 7)), then 8 lanes per token store whole 128-byte row pieces (scattered
+  // 8-byte stores would cost a write request per lane).
   uint16_t* ob = a.out + b * a.N * a.ld_out;
   auto epilogue = [&](int ft) {
+    lds_sync();   // every wave is done reading stage 3
+    const uint32_t rowo = (uint32_t)p * 128u + 8u * (uint32_t)(lane >> 5);
 #pragma unroll
-    for (int fb = 0; fb < 8; ++fb)
+    for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int f = ft * FT + fb * 32 + g * 8 + (lane >> 5) * 4;
-        const uint32_t lo = pack_bf16(layer_out(acc2[fb][g * 4 + 0], inv, bv, relu),
-                                      layer_out(acc2[fb][g * 4 + 1], inv, bv, relu));
-        const uint32_t hi = pack_bf16(layer_out(acc2[fb][g * 4 + 2], inv, bv, relu),
-                                      layer_out(acc2[fb][g * 4 + 3], inv, bv, relu));
-        if (p_ok && f < a.m_t) *reinterpret_cast<uint2*>(ob + (base + p) * a.ld_out + f) = make_uint2(lo, hi);
+      for (int fh = 0; fh < 2; ++fh) {
+        const int fb = 2 * rr + fh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = pack_bf16(layer_out(acc2[fb][g * 4 + 0], inv, bv, relu),
+                                        layer_out(acc2[fb][g * 4 + 1], inv, bv, relu));
+          const uint32_t hi = pack_bf16(layer_out(acc2[fb][g * 4 + 2], inv, bv, relu),
+                                        layer_out(acc2[fb][g * 4 + 3], inv, bv, relu));
+          const uint32_t pc = (uint32_t)(4 * fh + g) ^ (uint32_t)((p >> 1) & 7);
+          *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(lo, hi);
+        }
       }
+      lds_sync();
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int t = wave * 32 + it * 8 + (lane >> 3);
+        const int pp = lane & 7;
+        const uint4 v = lds_read16(st3, (uint32_t)t * 128u + ((uint32_t)(pp ^ ((t >> 1) & 7)) << 4));
+        const int f = ft * FT + rr * 64 + pp * 8;
+        if (t < valid_rows && f < a.m_t) *reinterpret_cast<uint4*>(ob + (base + t) * a.ld_out + f) = v;
+      }
+      if (rr < 3) lds_sync();
+    }
   };
   for (int ft = 0; ft < nft; ++ft) {
     const int c0 = 4 * ft;
