@@ -196,30 +196,54 @@ def select_compress(x: np.ndarray, S: int, idx: np.ndarray, w: np.ndarray, P: np
 
 
 # ----------------------------------------------------------------------------- dynamic layer
-def dyn_context_split(z_b: np.ndarray, S: int, eps: float, i: int) -> np.ndarray:
+NORMS = ("sum", "softmax", "rms", "none")
+
+
+def row_normalise(sim: np.ndarray, norm: str, eps: float) -> np.ndarray:
+    """Row normalisation of the cosine matrix of one split.
+
+    "sum": eq. 6 of [notes] 关键设计 3, S~_pq = S_pq / (sum_q S_pq + eps). The variants the
+    [summary] compares against it (appendix B, normalisation ablation; appendix H, removing the
+    row-wise normalisation), in the plainest reading: "softmax" over each row (temperature 1),
+    "rms" divides each row by its root mean square, sqrt(mean_q S_pq^2 + eps), and "none" keeps
+    S itself. Every row runs over the split's valid tokens only.
+    """
+    if norm == "sum":
+        return sim / (sim.sum(axis=1) + eps)[:, None]
+    if norm == "softmax":
+        e = np.exp(sim)
+        return e / e.sum(axis=1)[:, None]
+    if norm == "rms":
+        return sim / np.sqrt((sim * sim).mean(axis=1) + eps)[:, None]
+    if norm == "none":
+        return sim
+    raise ValueError(norm)
+
+
+def dyn_context_split(z_b: np.ndarray, S: int, eps: float, i: int, norm: str = "sum") -> np.ndarray:
     """S~ Z_t for one split, valid rows only.
 
     [notes] 关键设计 2: the dynamic layer forms the cosine matrix N(Z_t) N(Z_t)^T over the
     tokens of the split and multiplies Z_t by it; 关键设计 3, eq. 6: each row is divided by
-    its own sum plus eps. Within-split, bidirectional (no mask between valid tokens).
+    its own sum plus eps (norm="sum"; the other normalisations are row_normalise's). Within-
+    split, bidirectional (no mask between valid tokens).
     """
     N = z_b.shape[0]
     r = split_rows(N, S, i)
     zt = np.asarray(z_b[r.start:r.stop], dtype=np.float64)   # [n_valid, m_t]
     nz = unit_rows(zt)
     sim = nz @ nz.T                                            # S = N(Z_t) N(Z_t)^T
-    rowsum = sim.sum(axis=1)
-    s_tilde = sim / (rowsum + eps)[:, None]                    # eq. 6
+    s_tilde = row_normalise(sim, norm, eps)                    # eq. 6 for "sum"
     return s_tilde @ zt
 
 
-def dyn_context(z: np.ndarray, S: int, eps: float, splits=None):
+def dyn_context(z: np.ndarray, S: int, eps: float, splits=None, norm: str = "sum"):
     """dyn_context_split over the listed (b, i) splits (default: all). Returns {(b, i): rows}."""
     B, N, _ = z.shape
     n_s = n_splits(N, S)
     if splits is None:
         splits = [(b, i) for b in range(B) for i in range(n_s)]
-    return {(b, i): dyn_context_split(z[b], S, eps, i) for b, i in splits}
+    return {(b, i): dyn_context_split(z[b], S, eps, i, norm) for b, i in splits}
 
 
 # ----------------------------------------------------------------------------- contextualizer layers
@@ -245,10 +269,11 @@ def static_layer_split(z_b: np.ndarray, S: int, V: np.ndarray, bias: np.ndarray,
     return activation(y, act)[: len(split_rows(N, S, i))]
 
 
-def dyn_layer_split(z_b: np.ndarray, S: int, eps: float, bias: np.ndarray, act: str, i: int) -> np.ndarray:
+def dyn_layer_split(z_b: np.ndarray, S: int, eps: float, bias: np.ndarray, act: str, i: int,
+                    norm: str = "sum") -> np.ndarray:
     """c_dyn(Z) = sigma(S~ Z_t + b) for one split, valid rows only ([notes] 关键设计 2 and 3):
     the dynamic core of dyn_context_split, plus one bias per token position, then sigma."""
-    core = dyn_context_split(z_b, S, eps, i)
+    core = dyn_context_split(z_b, S, eps, i, norm)
     b = np.asarray(bias, dtype=np.float64)[: core.shape[0], None]
     return activation(core + b, act)
 
@@ -262,13 +287,13 @@ def static_layer(z: np.ndarray, S: int, V: np.ndarray, bias: np.ndarray, act: st
     return {(b, i): static_layer_split(z[b], S, V, bias, act, i) for b, i in splits}
 
 
-def dyn_layer(z: np.ndarray, S: int, eps: float, bias: np.ndarray, act: str, splits=None):
+def dyn_layer(z: np.ndarray, S: int, eps: float, bias: np.ndarray, act: str, splits=None, norm: str = "sum"):
     """dyn_layer_split over the listed (b, i) splits (default: all). Returns {(b, i): rows}."""
     B, N, _ = z.shape
     n_s = n_splits(N, S)
     if splits is None:
         splits = [(b, i) for b in range(B) for i in range(n_s)]
-    return {(b, i): dyn_layer_split(z[b], S, eps, bias, act, i) for b, i in splits}
+    return {(b, i): dyn_layer_split(z[b], S, eps, bias, act, i, norm) for b, i in splits}
 
 
 def assemble(parts: dict, B: int, N: int, S: int, width: int) -> np.ndarray:

@@ -454,3 +454,52 @@ def test_dyn_layer_reduces_to_core():
     for key in a:
         assert np.all(c[key] >= 0)
         np.testing.assert_array_equal(c[key], np.where(a[key] > 0, a[key], 0.0))
+
+
+# ----------------------------------------------------------------------------- normalisation variants
+def test_norm_variants_closed_forms():
+    """Orthogonal tokens (G = I on the n valid tokens): softmax weights e / (e + n - 1) on the
+    diagonal and 1 / (e + n - 1) elsewhere; rms weight sqrt(n / (1 + n eps)) on the diagonal;
+    none gives Z back; sum gives Z / (1 + eps). A constant split (G = all ones): softmax 1 / n,
+    rms 1 / sqrt(1 + eps), none 1, sum 1 / (n + eps), each times the shared token."""
+    eps = 1e-3
+    n, m = 3, 5
+    z = np.zeros((1, n, m))
+    z[0, 0, 0], z[0, 1, 1], z[0, 2, 4] = 2.0, -1.5, 0.5           # pairwise orthogonal
+    e = math.e
+    soft = O.dyn_context(z, n, eps, norm="softmax")[(0, 0)]
+    want = np.array([[(e if p == q else 1.0) / (e + n - 1) for q in range(n)] for p in range(n)]) @ z[0]
+    np.testing.assert_allclose(soft, want, rtol=1e-14, atol=1e-15)
+    rms = O.dyn_context(z, n, eps, norm="rms")[(0, 0)]
+    np.testing.assert_allclose(rms, math.sqrt(n / (1 + n * eps)) * z[0], rtol=1e-14)
+    np.testing.assert_allclose(O.dyn_context(z, n, eps, norm="none")[(0, 0)], z[0], rtol=1e-15)
+    np.testing.assert_allclose(O.dyn_context(z, n, eps, norm="sum")[(0, 0)], z[0] / (1 + eps), rtol=1e-15)
+    c = np.tile(np.array([0.3, -1.0, 2.0, 0.0, 0.7]), (1, 4, 1))
+    for norm, f in (("softmax", 4 * (1 / 4)), ("rms", 4 / math.sqrt(1 + eps)), ("none", 4.0),
+                    ("sum", 4 / (4 + eps))):
+        out = O.dyn_context(c, 4, eps, norm=norm)[(0, 0)]
+        np.testing.assert_allclose(out, f * c[0], rtol=1e-13, err_msg=norm)
+
+
+def test_norm_variants_row_properties_and_padding():
+    """Softmax rows sum to 1 and stay positive with signed cosines; rms rows have unit mean
+    square up to eps; padding tokens take part in no row (ragged split equals the same tokens
+    alone); the default is the sum normalisation."""
+    rng = np.random.default_rng(31)
+    S, m = 6, 4
+    z = rng.standard_normal((1, 10, m))                 # splits of 6 and 4 valid tokens
+    for i in range(2):
+        r = O.split_rows(10, S, i)
+        nz = O.unit_rows(z[0, r.start:r.stop])
+        sim = nz @ nz.T
+        sm = O.row_normalise(sim, "softmax", 1e-8)
+        np.testing.assert_allclose(sm.sum(axis=1), 1.0, rtol=1e-14)
+        assert np.all(sm > 0)
+        rm = O.row_normalise(sim, "rms", 0.0)
+        np.testing.assert_allclose((rm * rm).mean(axis=1), 1.0, rtol=1e-13)
+        for norm in O.NORMS:
+            alone = O.dyn_context(z[:, r.start:r.stop], S, 1e-8, norm=norm)[(0, 0)]
+            np.testing.assert_allclose(O.dyn_context(z, S, 1e-8, norm=norm)[(0, i)], alone, rtol=1e-14)
+    np.testing.assert_array_equal(O.dyn_context(z, S, 1e-8)[(0, 1)], O.dyn_context(z, S, 1e-8, norm="sum")[(0, 1)])
+    with pytest.raises(ValueError):
+        O.row_normalise(np.eye(2), "l1", 1e-8)
