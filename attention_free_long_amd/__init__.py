@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libavey.so"
 
 AVEY_F32, AVEY_BF16 = 0, 1
 AVEY_ACT = {"identity": 0, "relu": 1}
+AVEY_NORM = {"sum": 0, "softmax": 1, "rms": 2, "none": 3}
 AVEY_ABI_VERSION = 1
 
 EXPORTS = (
@@ -82,7 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_dyn_context.restype = i32
     lib.avey_dyn_context.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, vp, i64, vp]
     lib.avey_dyn_layer.restype = i32
-    lib.avey_dyn_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, vp, i32, vp, i64, vp]
+    lib.avey_dyn_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, i32, vp, i32, vp, i64, vp]
     lib.avey_static_layer.restype = i32
     lib.avey_static_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, i32, vp, i64, vp]
     ver = lib.avey_abi_version()
@@ -259,19 +260,22 @@ def _layer_args(fn: str, z_tail, S: int, bias, act: str):
     return bias.data_ptr(), AVEY_ACT[act]
 
 
-def avey_dyn_layer(z_tail, S: int, eps: float, bias=None, act: str = "identity", out=None):
-    """act(S~ Z_t + bias[slot]) per split: the dynamic layer with its bias and activation."""
+def avey_dyn_layer(z_tail, S: int, eps: float, bias=None, act: str = "identity", out=None, norm: str = "sum"):
+    """act(S~ Z_t + bias[slot]) per split: the dynamic layer with its bias and activation; norm
+    selects the row normalisation of the cosine matrix ("sum", "softmax", "rms" or "none")."""
     import torch
     B, N, m_t, ld = _rows(z_tail, "z_tail")
     bptr, code = _layer_args("avey_dyn_layer", z_tail, S, bias, act)
+    if norm not in AVEY_NORM:
+        raise AveyError("avey_dyn_layer", -2, f"norm must be one of {sorted(AVEY_NORM)}")
     if out is None:
         out = torch.empty((B, N, m_t), device=z_tail.device, dtype=z_tail.dtype)
     if out.dtype != z_tail.dtype:
         raise AveyError("avey_dyn_layer", -3, "out must have the dtype of z_tail")
     _, _, _, ld_out = _rows(out, "out")
     _check("avey_dyn_layer", load_library().avey_dyn_layer(
-        z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, float(eps), bptr, code, out.data_ptr(),
-        ld_out, _stream(z_tail)))
+        z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, float(eps), AVEY_NORM[norm], bptr, code,
+        out.data_ptr(), ld_out, _stream(z_tail)))
     return out
 
 

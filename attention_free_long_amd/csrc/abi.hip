@@ -266,10 +266,13 @@ avey_status avey_dyn_context(const void* z_tail, avey_dtype dt, int64_t B, int64
 }
 
 avey_status avey_dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t, int64_t ld_z,
-                           int32_t S, float eps, const float* bias, int32_t act, void* out, int64_t ld_out,
-                           void* stream) {
+                           int32_t S, float eps, int32_t norm, const float* bias, int32_t act, void* out,
+                           int64_t ld_out, void* stream) {
   LayerEpi epi;
   AVEY_TRY(check_epi(bias, act, &epi));
+  if (norm != AVEY_NORM_SUM && norm != AVEY_NORM_SOFTMAX && norm != AVEY_NORM_RMS && norm != AVEY_NORM_NONE)
+    return AVEY_ERR_SHAPE;
+  epi.norm = norm;
   return dyn_layer(z_tail, dt, B, N, m_t, ld_z, S, eps, epi, out, ld_out, stream);
 }
 

@@ -43,6 +43,33 @@ __device__ __forceinline__ float layer_bias(const LayerEpi& e, int p, bool p_ok)
   return bv;
 }
 
+// Row normalisation (LayerEpi::norm). Four cosines G_pq of row p, q = q0 .. q0 + 3, become the
+// weights the second GEMM uses, rounded to bf16 (two packed pairs); stat accumulates what the
+// row's scale is computed from, over the rounded weights: their sum (sum, softmax) or the sum
+// of their squares (rms). Softmax weights are exp(G_pq) for valid q and 0 for padding q.
+__device__ __forceinline__ void g_weights(float g0, float g1, float g2, float g3, int q0, int nvalid, int norm,
+                                          uint32_t& lo, uint32_t& hi, float& stat) {
+  if (norm == kNormSoftmax) {
+    g0 = q0 + 0 < nvalid ? __expf(g0) : 0.f;
+    g1 = q0 + 1 < nvalid ? __expf(g1) : 0.f;
+    g2 = q0 + 2 < nvalid ? __expf(g2) : 0.f;
+    g3 = q0 + 3 < nvalid ? __expf(g3) : 0.f;
+  }
+  lo = pack_bf16(g0, g1);
+  hi = pack_bf16(g2, g3);
+  const float r0 = bf16lo(lo), r1 = bf16hi(lo), r2 = bf16lo(hi), r3 = bf16hi(hi);
+  stat += norm == kNormRms ? (r0 * r0 + r1 * r1) + (r2 * r2 + r3 * r3) : (r0 + r1) + (r2 + r3);
+}
+
+// Scale of row p from its statistic: 1 / (sum + eps) (eq. 6), 1 / sum (softmax),
+// 1 / sqrt(mean square + eps) over the nvalid tokens (rms), 1 (none).
+__device__ __forceinline__ float row_scale(int norm, float stat, float eps, int nvalid) {
+  if (norm == kNormSum) return 1.0f / (stat + eps);
+  if (norm == kNormSoftmax) return 1.0f / stat;
+  if (norm == kNormRms) return 1.0f / sqrtf(stat / (float)nvalid + eps);
+  return 1.0f;
+}
+
 __device__ __forceinline__ float layer_out(float v, float scale, float bv, bool relu) {
   const float y = fmaf(v, scale, bv);
   return relu ? fmaxf(y, 0.f) : y;
@@ -71,6 +98,7 @@ __global__ void __launch_bounds__(256, 1) dyn_bf16_kernel(DynParams a) {
   const int64_t b = split / a.n_s;
   const int i = (int)(split % a.n_s);
   const int64_t base = (int64_t)i * a.S;
+  const int nvalid = (int)min((int64_t)a.S, a.N - base);   // valid tokens of the split
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
   const int nk = a.m_t / KC;
 
@@ -186,19 +214,15 @@ __global__ void __launch_bounds__(256, 1) dyn_bf16_kernel(DynParams a) {
           const int q0 = qb * 32 + s2 * 16 + h * 8 + (lane >> 5) * 4;   // rows of v = 8*s2 + 4*h + 0..3
           const float4 rq = *reinterpret_cast<const float4*>(&s_rn[q0]);
           const int v0 = s2 * 8 + h * 4;
-          const float g0 = acc1[qb][nb][v0 + 0] * rq.x * rnp;
-          const float g1 = acc1[qb][nb][v0 + 1] * rq.y * rnp;
-          const float g2 = acc1[qb][nb][v0 + 2] * rq.z * rnp;
-          const float g3 = acc1[qb][nb][v0 + 3] * rq.w * rnp;
-          pk[2 * h + 0] = pack_bf16(g0, g1);
-          pk[2 * h + 1] = pack_bf16(g2, g3);
-          r += (bf16lo(pk[2 * h]) + bf16hi(pk[2 * h])) + (bf16lo(pk[2 * h + 1]) + bf16hi(pk[2 * h + 1]));
+          g_weights(acc1[qb][nb][v0 + 0] * rq.x * rnp, acc1[qb][nb][v0 + 1] * rq.y * rnp,
+                    acc1[qb][nb][v0 + 2] * rq.z * rnp, acc1[qb][nb][v0 + 3] * rq.w * rnp, q0, nvalid, a.epi.norm,
+                    pk[2 * h + 0], pk[2 * h + 1], r);
         }
         gfrag[qb][s2][nb] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     }
     r += __shfl_xor(r, 32);
-    inv[nb] = 1.0f / (r + a.eps);
+    inv[nb] = row_scale(a.epi.norm, r, a.eps, nvalid);
   }
 
   // ------------------------------------------------------------------ GEMM 2
@@ -467,19 +491,14 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
           const int q0 = qb * 32 + s2 * 16 + h * 8 + (lane >> 5) * 4;   // rows of v = 8 s2 + 4 h + 0..3
           const float4 rq = *reinterpret_cast<const float4*>(&s_rn[q0]);
           const int v0 = s2 * 8 + h * 4;
-          const float g0 = acc1[qb][v0 + 0] * rq.x * rnp;
-          const float g1 = acc1[qb][v0 + 1] * rq.y * rnp;
-          const float g2 = acc1[qb][v0 + 2] * rq.z * rnp;
-          const float g3 = acc1[qb][v0 + 3] * rq.w * rnp;
-          pk[2 * h + 0] = pack_bf16(g0, g1);
-          pk[2 * h + 1] = pack_bf16(g2, g3);
-          r += (bf16lo(pk[2 * h]) + bf16hi(pk[2 * h])) + (bf16lo(pk[2 * h + 1]) + bf16hi(pk[2 * h + 1]));
+          g_weights(acc1[qb][v0 + 0] * rq.x * rnp, acc1[qb][v0 + 1] * rq.y * rnp, acc1[qb][v0 + 2] * rq.z * rnp,
+                    acc1[qb][v0 + 3] * rq.w * rnp, q0, valid_rows, a.epi.norm, pk[2 * h + 0], pk[2 * h + 1], r);
         }
         gfrag[qb][s2] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     }
     r += __shfl_xor(r, 32);
-    inv = 1.0f / (r + a.eps);
+    inv = row_scale(a.epi.norm, r, a.eps, valid_rows);
   }
 
   // ---- phase 2. G fragment (qb, s2) of lane half h holds q = 32 qb + 16 s2 + {4h .. 4h+3,

@@ -13,11 +13,17 @@ hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, i
 hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, bool preceding, int32_t* idx,
                             float* w, hipStream_t stream);
 
+// Row normalisation of the dynamic layer's cosine matrix: divide by sum + eps (eq. 6), softmax,
+// divide by the root mean square, or none.
+constexpr int kNormSum = 0, kNormSoftmax = 1, kNormRms = 2, kNormNone = 3;
+
 // Output epilogue of a contextualizer layer, y = act(v + bias[s]) with s the token's position in
-// its split: bias holds S fp32 values (nullptr: no bias); act 0 is the identity, 1 is ReLU.
+// its split: bias holds S fp32 values (nullptr: no bias); act 0 is the identity, 1 is ReLU. norm
+// is the dynamic layer's row normalisation (one of kNorm*; the static layer ignores it).
 struct LayerEpi {
   const float* bias = nullptr;
   int act = 0;
+  int norm = kNormSum;
 };
 
 constexpr int kCompressMaxBlocks = 512;   // bf16 gather + compress: k + 1 <= this

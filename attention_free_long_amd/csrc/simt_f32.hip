@@ -113,12 +113,16 @@ __global__ void __launch_bounds__(256) dyn_f32_kernel(const float* __restrict__ 
     const float nq = norm_f32(zq, m_t);
     float dot = 0.f;
     for (int c = 0; c < m_t; ++c) dot = fmaf(zp[c], zq[c], dot);
-    const float gq = (np_ > 0.f && nq > 0.f) ? dot / (np_ * nq) : 0.f;
+    float gq = (np_ > 0.f && nq > 0.f) ? dot / (np_ * nq) : 0.f;
+    if (epi.norm == kNormSoftmax) gq = expf(gq);
     g[q] = gq;
-    part += gq;
+    part += epi.norm == kNormRms ? gq * gq : gq;
   }
   const float r = block_sum(part, red);   // contains a barrier: g[] is complete afterwards
-  const float den = r + eps;
+  // row scale: 1 / (sum + eps) (eq. 6), 1 / sum (softmax), 1 / sqrt(mean square + eps), 1
+  const float den = epi.norm == kNormSum ? r + eps
+                  : epi.norm == kNormSoftmax ? r
+                  : epi.norm == kNormRms ? sqrtf(r / (float)nv + eps) : 1.f;
   const float bv = epi.bias ? epi.bias[t - base] : 0.f;
   for (int f = threadIdx.x; f < m_t; f += 256) {
     float acc = 0.f;

@@ -209,19 +209,33 @@ avey_status avey_dyn_context(const void* z_tail, avey_dtype dt, int64_t B, int64
 typedef enum { AVEY_ACT_IDENTITY = 0, AVEY_ACT_RELU = 1 } avey_act;
 
 /*
+ * Row normalisation of the dynamic layer's cosine matrix G (per split, over its valid tokens):
+ *   AVEY_NORM_SUM      S~_pq = G_pq / (sum_q G_pq + eps)              ([notes] 关键设计 3, eq. 6)
+ *   AVEY_NORM_SOFTMAX  S~_pq = exp(G_pq) / sum_q exp(G_pq)
+ *   AVEY_NORM_RMS      S~_pq = G_pq / sqrt(mean_q G_pq^2 + eps)
+ *   AVEY_NORM_NONE     S~_pq = G_pq
+ * The last three are the alternatives the [summary] compares (appendix B, normalisation
+ * ablation; appendix H, no row-wise normalisation).
+ */
+typedef enum { AVEY_NORM_SUM = 0, AVEY_NORM_SOFTMAX = 1, AVEY_NORM_RMS = 2, AVEY_NORM_NONE = 3 } avey_norm;
+
+/*
  * avey_dyn_layer -- dynamic contextualizer layer c_dyn = sigma(S~ Z_t + b) ([notes] 关键设计 2
- * and 3): the core of avey_dyn_context, then for each valid token p of split i
+ * and 3): the core of avey_dyn_context with the row normalisation `norm`, then for each valid
+ * token p of split i
  *   out_p = act(core_p + bias[p - i S])      (one bias value per token position of a split)
  *
  *   z_tail, out, S, eps  as avey_dyn_context
+ *   norm    an avey_norm (AVEY_NORM_SUM is avey_dyn_context's; other values: AVEY_ERR_SHAPE)
  *   bias    [S] float32 (input), or NULL for no bias
  *   act     an avey_act (other values: AVEY_ERR_SHAPE)
- * For AVEY_BF16 the bias is added to the fp32 value before the activation and the single
- * rounding to bf16.
+ * For AVEY_BF16 the weights S~ use G rounded to bf16 (for softmax: exp(G) rounded), the row
+ * statistic is taken over those rounded values, and the bias is added to the fp32 value before
+ * the activation and the single rounding to bf16.
  */
 avey_status avey_dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, int64_t m_t,
-                           int64_t ld_z, int32_t S, float eps, const float* bias, int32_t act,
-                           void* out, int64_t ld_out, void* stream);
+                           int64_t ld_z, int32_t S, float eps, int32_t norm, const float* bias,
+                           int32_t act, void* out, int64_t ld_out, void* stream);
 
 /*
  * avey_static_layer -- static contextualizer layer c_static = sigma(V Z_t + b) ([notes]

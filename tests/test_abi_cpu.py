@@ -147,14 +147,16 @@ def test_binding_refuses_host_tensors():
 
 def test_dyn_layer_validation(lib):
     f = lib.avey_dyn_layer
-    # (z_tail, dt, B, N, m_t, ld_z, S, eps, bias, act, out, ld_out, stream)
-    assert f(None, 1, 0, 1024, 64, 64, 64, 1e-8, None, 0, None, 64, None) == OK
-    assert f(None, 1, 1, 1024, 64, 64, 64, 1e-8, None, 0, P16, 64, None) == NULL
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, None, 2, P16, 64, None) == SHAPE     # unknown act
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, None, -1, P16, 64, None) == SHAPE
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, P16 + 2, 1, P16, 64, None) == ALIGN  # bias not 4-aligned
-    assert f(P16, 1, 1, 1024, 64, 64, 96, 1e-8, None, 1, P16, 64, None) == UNSUP    # bf16 S % 64
-    assert f(P16, 9, 1, 1024, 64, 64, 64, 1e-8, None, 0, P16, 64, None) == DTYPE
+    # (z_tail, dt, B, N, m_t, ld_z, S, eps, norm, bias, act, out, ld_out, stream)
+    assert f(None, 1, 0, 1024, 64, 64, 64, 1e-8, 0, None, 0, None, 64, None) == OK
+    assert f(None, 1, 1, 1024, 64, 64, 64, 1e-8, 0, None, 0, P16, 64, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, 0, None, 2, P16, 64, None) == SHAPE     # unknown act
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, 0, None, -1, P16, 64, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, 4, None, 0, P16, 64, None) == SHAPE     # unknown norm
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, -1, None, 0, P16, 64, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, 1, P16 + 2, 1, P16, 64, None) == ALIGN  # bias not 4-aligned
+    assert f(P16, 1, 1, 1024, 64, 64, 96, 1e-8, 2, None, 1, P16, 64, None) == UNSUP    # bf16 S % 64
+    assert f(P16, 9, 1, 1024, 64, 64, 64, 1e-8, 3, None, 0, P16, 64, None) == DTYPE
 
 
 def test_static_layer_validation(lib):

@@ -206,3 +206,44 @@ def test_static_layer_persistent_kernel(gpu_ok):
     w = check_layer(g, O.static_layer(z64, cfg.S, V64, b64, "identity"),
                     O.static_layer(z64, cfg.S, V64, b64, "relu"), cfg, tol, "static")
     say(f"static layer, persistent kernel: worst {w:.2e}")
+
+
+@pytest.mark.parametrize("norm", ["softmax", "rms", "none"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_dyn_norm_variants(gpu_ok, name, norm):
+    """The dynamic layer with each row normalisation other than eq. 6, with a bias, against the
+    oracle on every split (identity activation, so rows compare by their own norm)."""
+    cfg = CASES[name]
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    _, bias = layer_params(inp)
+    say(f"{name}/{norm}: dynamic layer B={cfg.B} N={cfg.N} S={cfg.S} m_t={cfg.m_t}")
+    _, _, _, z_tail = upload(inp)
+    bd = torch.from_numpy(bias).to("cuda")
+    g = host_f64(A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "identity", norm=norm))
+    torch.cuda.synchronize()
+    ref = O.dyn_layer(inp.z_tail_f64(), cfg.S, cfg.eps, bias.astype(np.float64), "identity", norm=norm)
+    w = check_layer(g, ref, ref, cfg, tol, f"dynamic/{norm}")
+    say(f"{name}/{norm}: worst relative error {w:.2e}")
+
+
+@pytest.mark.parametrize("norm", ["softmax", "rms"])
+def test_dyn_norm_full_size_sampled(gpu_ok, norm):
+    """Softmax and RMS normalisation on the 2 x 32768-token workload (m_t = 1536 at row stride
+    3072), sampled splits including the first and the last."""
+    cfg = CONFIGS["long"]
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    say(f"long/{norm}: dynamic layer")
+    _, _, _, z_tail = upload(inp)
+    g = A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, norm=norm)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    picks = sorted({(0, 0), (cfg.B - 1, cfg.n_s - 1)} |
+                   {(int(b), int(i)) for b, i in zip(rng.integers(0, cfg.B, 4), rng.integers(0, cfg.n_s, 4))})
+    for b, i in picks:
+        r = split_rows_of(cfg.N, cfg.S, i)
+        o = O.dyn_context_split(inp.z_tail_f64(b), cfg.S, cfg.eps, i, norm)
+        err = float((np.linalg.norm(host_f64(g[b, r]) - o, axis=-1) / np.linalg.norm(o, axis=-1)).max())
+        assert err <= tol, f"{norm} split {(b, i)}: {err:.3e}"
+    say(f"long/{norm}: {len(picks)} sampled splits within {tol}")
