@@ -296,6 +296,37 @@ def dyn_layer(z: np.ndarray, S: int, eps: float, bias: np.ndarray, act: str, spl
     return {(b, i): dyn_layer_split(z[b], S, eps, bias, act, i, norm) for b, i in splits}
 
 
+# ----------------------------------------------------------------------------- enricher and fuser
+def enrich(x: np.ndarray, U: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Z = ReLU(X U + b)^2 row by row ([notes] 整体框架: the enricher is a position-wise map
+    Z = sigma(X U + b) from d up to m > d features; [summary] appendix A: its activation is
+    ReLU squared, which keeps Z non-negative). x [..., d], U [d, m], b [m] -> [..., m]."""
+    h = np.asarray(x, dtype=np.float64) @ np.asarray(U, dtype=np.float64) + np.asarray(b, dtype=np.float64)
+    r = np.maximum(h, 0.0)
+    return r * r
+
+
+def fuse(z: np.ndarray, m_h: int, c: np.ndarray, O: np.ndarray, x_res: np.ndarray) -> np.ndarray:
+    """Y = [Z_h || c(Z_t)] O + X ([notes] 整体框架: the fuser joins the bypassed head Z_h, the
+    first m_h features of Z, with the contextualised tail and projects them back to d, then
+    adds the layer's input; [summary] section 3). z [..., m] (only its head is read), c [..., m_t],
+    O [m_h + m_t, d], x_res [..., d]."""
+    z = np.asarray(z, dtype=np.float64)
+    joined = np.concatenate([z[..., :m_h], np.asarray(c, dtype=np.float64)], axis=-1)
+    return joined @ np.asarray(O, dtype=np.float64) + np.asarray(x_res, dtype=np.float64)
+
+
+def neural_layer(x: np.ndarray, S: int, U: np.ndarray, b: np.ndarray, m_h: int, O: np.ndarray,
+                 contextualise) -> np.ndarray:
+    """One neural-processor layer over whole sequences: enrich, contextualise the tail split by
+    split (contextualise(z_tail) -> {(b, i): rows}, e.g. a dynamic or static layer), fuse with
+    the residual ([notes] 整体框架; [summary] section 3). x [B, N, d] -> [B, N, d]."""
+    B, N, _ = x.shape
+    z = enrich(x, U, b)
+    c = assemble(contextualise(z[..., m_h:]), B, N, S, z.shape[-1] - m_h)
+    return fuse(z, m_h, c, O, x)
+
+
 def assemble(parts: dict, B: int, N: int, S: int, width: int) -> np.ndarray:
     """Stack per-split results {(b, i): rows} into a [B, N, width] array (NaN where absent)."""
     out = np.full((B, N, width), np.nan)

@@ -503,3 +503,52 @@ def test_norm_variants_row_properties_and_padding():
     np.testing.assert_array_equal(O.dyn_context(z, S, 1e-8)[(0, 1)], O.dyn_context(z, S, 1e-8, norm="sum")[(0, 1)])
     with pytest.raises(ValueError):
         O.row_normalise(np.eye(2), "l1", 1e-8)
+
+
+# ----------------------------------------------------------------------------- enricher and fuser
+def test_enrich_closed_forms():
+    """U = I and b = 0 give ReLU(x)^2; a one-hot column of U picks a feature; the bias shifts
+    before the activation; the output is never negative."""
+    x = np.array([[1.5, -2.0, 0.25], [-0.5, 3.0, 0.0]])
+    np.testing.assert_array_equal(O.enrich(x, np.eye(3), np.zeros(3)), np.maximum(x, 0) ** 2)
+    U = np.zeros((3, 4))
+    U[2, 0] = 1.0
+    U[0, 3] = -2.0
+    b = np.array([0.5, -1.0, 0.0, 1.0])
+    want = np.stack([np.maximum(x[:, 2] + 0.5, 0) ** 2, np.zeros(2), np.zeros(2),
+                     np.maximum(-2 * x[:, 0] + 1.0, 0) ** 2], axis=1)
+    np.testing.assert_allclose(O.enrich(x, U, b), want, rtol=1e-15)
+    rng = np.random.default_rng(41)
+    assert np.all(O.enrich(rng.standard_normal((5, 6)), rng.standard_normal((6, 9)), rng.standard_normal(9)) >= 0)
+
+
+def test_fuse_closed_forms():
+    """O = I returns the joined head and contextualised tail plus the residual; the head part of
+    O only sees Z_h (the tail of z is never read) and its tail part only sees c."""
+    rng = np.random.default_rng(42)
+    m_h, m_t, d = 3, 2, 5
+    z = rng.standard_normal((4, m_h + m_t))
+    c = rng.standard_normal((4, m_t))
+    xr = rng.standard_normal((4, d))
+    np.testing.assert_allclose(O.fuse(z, m_h, c, np.eye(d), xr), np.concatenate([z[:, :m_h], c], 1) + xr, rtol=1e-15)
+    Oh = np.zeros((m_h + m_t, d))
+    Oh[:m_h] = rng.standard_normal((m_h, d))
+    z2 = z.copy()
+    z2[:, m_h:] = 1e6                                    # the tail of Z is not read
+    np.testing.assert_allclose(O.fuse(z2, m_h, c, Oh, 0 * xr), z[:, :m_h] @ Oh[:m_h], rtol=1e-14)
+    Ot = np.zeros((m_h + m_t, d))
+    Ot[m_h:] = rng.standard_normal((m_t, d))
+    np.testing.assert_allclose(O.fuse(z, m_h, c, Ot, 0 * xr), c @ Ot[m_h:], rtol=1e-14)
+
+
+def test_neural_layer_reduces_to_parts():
+    """With U = I (m = d), b = 0, no head and O = I the layer is X + c(ReLU(X)^2); with a zero O
+    it is the residual alone."""
+    rng = np.random.default_rng(43)
+    S, d = 4, 3
+    x = rng.standard_normal((1, 10, d))
+    ctx = lambda zt: O.dyn_context(zt, S, 1e-8)
+    y = O.neural_layer(x, S, np.eye(d), np.zeros(d), 0, np.eye(d), ctx)
+    c = O.assemble(O.dyn_context(np.maximum(x, 0) ** 2, S, 1e-8), 1, 10, S, d)
+    np.testing.assert_allclose(y, x + c, rtol=1e-14)
+    np.testing.assert_array_equal(O.neural_layer(x, S, np.eye(d), np.zeros(d), 1, np.zeros((d, d)), ctx), x)
