@@ -8,6 +8,8 @@ runs in the library's HIP kernels. torch supplies device memory and the current 
     out = avey_dyn_context(z_tail, S, eps)
     out = avey_dyn_layer(z_tail, S, eps, bias, act="relu")       # sigma(S~ Z_t + b)
     out = avey_static_layer(z_tail, V, S, bias, act="identity")  # sigma(V Z_t + b)
+    z = avey_enrich(x, U, b)                                    # ReLU(X U + b)^2
+    y = avey_fuse(z, m_h, c, O, x)                              # [Z_h || c] O + X
 
 Tensors are [B, N, width] with unit stride along width and any row stride (ld); bf16 or fp32.
 There is no fallback: if libavey.so is missing or fails to load, every call raises.
@@ -38,6 +40,8 @@ EXPORTS = (
     "avey_dyn_context",
     "avey_dyn_layer",
     "avey_static_layer",
+    "avey_enrich",
+    "avey_fuse",
 )
 
 
@@ -84,6 +88,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_dyn_context.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, vp, i64, vp]
     lib.avey_dyn_layer.restype = i32
     lib.avey_dyn_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, f32, i32, vp, i32, vp, i64, vp]
+    lib.avey_enrich.restype = i32
+    lib.avey_enrich.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp]
+    lib.avey_fuse.restype = i32
+    lib.avey_fuse.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.avey_static_layer.restype = i32
     lib.avey_static_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, i32, vp, i64, vp]
     ver = lib.avey_abi_version()
@@ -294,4 +302,46 @@ def avey_static_layer(z_tail, V, S: int, bias=None, act: str = "identity", out=N
     _check("avey_static_layer", load_library().avey_static_layer(
         z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, V.data_ptr(), bptr, code, out.data_ptr(),
         ld_out, _stream(z_tail)))
+    return out
+
+
+def avey_enrich(x, U, b=None, out=None):
+    """Z [B, N, m] = ReLU(X U + b)^2 for x [B, N, d], U [d, m], b [m] float32 (or None)."""
+    import torch
+    B, N, d, ld = _rows(x, "x")
+    if U.dtype != x.dtype or not U.is_contiguous() or U.dim() != 2 or U.shape[0] != d:
+        raise AveyError("avey_enrich", -2, f"U must be a contiguous [d, m] tensor of x's dtype (d = {d})")
+    m = U.shape[1]
+    if b is not None and (b.dtype != torch.float32 or not b.is_contiguous() or tuple(b.shape) != (m,)):
+        raise AveyError("avey_enrich", -2, f"b must be a contiguous float32 [{m}] tensor")
+    if out is None:
+        out = torch.empty((B, N, m), device=x.device, dtype=x.dtype)
+    if out.dtype != x.dtype:
+        raise AveyError("avey_enrich", -3, "out must have x's dtype")
+    _, _, _, ld_out = _rows(out, "out")
+    _check("avey_enrich", load_library().avey_enrich(
+        x.data_ptr(), _dtype_code(x), B * N, d, ld, U.data_ptr(), m, b.data_ptr() if b is not None else 0,
+        out.data_ptr(), ld_out, _stream(x)))
+    return out
+
+
+def avey_fuse(z, m_h: int, c, O, x, out=None):
+    """Y [B, N, d] = [Z_h || C] O + X: z [B, N, >= m_h] (head = its first m_h columns), c [B, N, m_t],
+    O [m_h + m_t, d], x [B, N, d] the layer's input."""
+    import torch
+    B, N, d, ld_x = _rows(x, "x")
+    _, _, m_t, ld_c = _rows(c, "c")
+    _, _, wz, ld_z = _rows(z, "z")
+    if wz < m_h:
+        raise AveyError("avey_fuse", -2, f"z has {wz} columns, fewer than m_h = {m_h}")
+    if O.dtype != x.dtype or not O.is_contiguous() or tuple(O.shape) != (m_h + m_t, d):
+        raise AveyError("avey_fuse", -2, f"O must be a contiguous [{m_h + m_t}, {d}] tensor of x's dtype")
+    if z.dtype != x.dtype or c.dtype != x.dtype:
+        raise AveyError("avey_fuse", -3, "z, c, O and x must share one dtype")
+    if out is None:
+        out = torch.empty((B, N, d), device=x.device, dtype=x.dtype)
+    _, _, _, ld_y = _rows(out, "out")
+    _check("avey_fuse", load_library().avey_fuse(
+        z.data_ptr(), _dtype_code(x), B * N, m_h, ld_z, c.data_ptr(), m_t, ld_c, O.data_ptr(), d,
+        x.data_ptr(), ld_x, out.data_ptr(), ld_y, _stream(x)))
     return out

@@ -187,6 +187,14 @@ avey_status split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64
   return preceding ? avey_topk_norm_preceding(scores, B, n_s, k, idx, w, stream)
                    : avey_topk_norm(scores, B, n_s, k, idx, w, stream);
 }
+// Row-wise (position-wise) entry points: a [M, width] operand set.
+avey_status check_rows(avey_dtype dt, int64_t M, bool* empty) {
+  if (dt != AVEY_F32 && dt != AVEY_BF16) return AVEY_ERR_DTYPE;
+  if (M < 0) return AVEY_ERR_SHAPE;
+  *empty = M == 0;
+  return AVEY_OK;
+}
+
 // Layer epilogue arguments: bias may be NULL (no bias), act is an avey_act.
 avey_status check_epi(const float* bias, int32_t act, LayerEpi* epi) {
   if (act != AVEY_ACT_IDENTITY && act != AVEY_ACT_RELU) return AVEY_ERR_SHAPE;
@@ -303,6 +311,58 @@ avey_status avey_static_layer(const void* z_tail, avey_dtype dt, int64_t B, int6
   return hip_status(launch_compress_f32(static_cast<const float*>(z_tail), B, N, (int)m_t, ld_z, S, 0, nullptr,
                                         nullptr, static_cast<const float*>(V), 0, static_cast<float*>(out), ld_out,
                                         st, epi));
+}
+
+avey_status avey_enrich(const void* x, avey_dtype dt, int64_t M, int64_t d, int64_t ld_x, const void* U,
+                        int64_t m, const float* b, void* z, int64_t ld_z, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_rows(dt, M, &empty));
+  if (empty) return AVEY_OK;
+  if (!U) return AVEY_ERR_NULL;
+  AVEY_TRY(check_tensor(x, dt, M, d, ld_x));
+  AVEY_TRY(check_tensor(z, dt, M, m, ld_z));
+  if (b && !aligned(b, 4)) return AVEY_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dt == AVEY_BF16) {
+    if (!aligned(U, 16)) return AVEY_ERR_ALIGN;
+    if (d * m >= (1LL << 30) || (b && m > kEnrichMaxWidth)) return AVEY_ERR_UNSUPPORTED;
+    return hip_status(launch_enrich_bf16(static_cast<const uint16_t*>(x), M, (int)d, ld_x,
+                                         static_cast<const uint16_t*>(U), (int)m, b, static_cast<uint16_t*>(z),
+                                         ld_z, st));
+  }
+  if (!aligned(U, 4)) return AVEY_ERR_ALIGN;
+  if ((M * m + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_enrich_f32(static_cast<const float*>(x), M, (int)d, ld_x, static_cast<const float*>(U),
+                                      (int)m, b, static_cast<float*>(z), ld_z, st));
+}
+
+avey_status avey_fuse(const void* z, avey_dtype dt, int64_t M, int64_t m_h, int64_t ld_z, const void* c,
+                      int64_t m_t, int64_t ld_c, const void* O, int64_t d, const void* x, int64_t ld_x,
+                      void* y, int64_t ld_y, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_rows(dt, M, &empty));
+  if (empty) return AVEY_OK;
+  if (!O) return AVEY_ERR_NULL;
+  if (m_h < 0) return AVEY_ERR_SHAPE;
+  if (m_h > 0) AVEY_TRY(check_tensor(z, dt, M, m_h, ld_z));
+  AVEY_TRY(check_tensor(c, dt, M, m_t, ld_c));
+  AVEY_TRY(check_tensor(x, dt, M, d, ld_x));
+  AVEY_TRY(check_tensor(y, dt, M, d, ld_y));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dt == AVEY_BF16) {
+    if (m_h % 64) return AVEY_ERR_UNSUPPORTED;
+    if (!aligned(O, 16)) return AVEY_ERR_ALIGN;
+    if ((m_h + m_t) * d >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;
+    return hip_status(launch_fuse_bf16(static_cast<const uint16_t*>(z), M, (int)m_h, ld_z,
+                                       static_cast<const uint16_t*>(c), (int)m_t, ld_c,
+                                       static_cast<const uint16_t*>(O), (int)d, static_cast<const uint16_t*>(x),
+                                       ld_x, static_cast<uint16_t*>(y), ld_y, st));
+  }
+  if (!aligned(O, 4)) return AVEY_ERR_ALIGN;
+  if ((M * d + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  return hip_status(launch_fuse_f32(static_cast<const float*>(z), M, (int)m_h, ld_z, static_cast<const float*>(c),
+                                    (int)m_t, ld_c, static_cast<const float*>(O), (int)d,
+                                    static_cast<const float*>(x), ld_x, static_cast<float*>(y), ld_y, st));
 }
 
 }  // extern "C"

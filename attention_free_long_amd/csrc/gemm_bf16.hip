@@ -1,0 +1,346 @@
+// The dense GEMMs of a neural-processor layer around the contextualizer, on bf16 MFMA (gfx950):
+//   enricher  Z = ReLU(X U + b)^2       U [d][m]: each token's d features up to m
+//   fuser     Y = [Z_h || C] O + X      O [m_h + m_t][d]: the bypassed head of Z joined with the
+//                                       contextualised tail C, projected back to d, plus the
+//                                       layer's input
+// (papernotes.org Avey-B note, 方法详解/整体框架; paperlayer.ai "Avey-B" summary, section 3 and
+// appendix A for the squared ReLU.)
+//
+// Both are C^T[f][t] = sum_k W[k][f] A[t][k] with W = U or O row-major [K][F] and A the token
+// rows: the structure of the persistent compression kernel (compress_bf16.hip) without the
+// gather and the block weights. A unit is 256 output features x 256 tokens; W streams through
+// LDS as 32-row chunks of 256 features (512-byte rows, read back with the LDS transpose read)
+// and A as 256 token rows x 32 K-values (64 bytes) per chunk, through a 4-stage ring of 32 KiB
+// direct-copy stages, one 8-wave workgroup per CU (2 x 4 waves of 128 features x 64 tokens).
+//   * The fuser's A is two tensors along K: columns [0, m_h) of Z (its head), then C.
+//   * The fuser's residual: 8 more chunks stage the unit's 256 token rows of X (256 features)
+//     in the W part, with zeros in the A part; in the chunk holding a wave's token block, 8
+//     MFMAs of those rows' transposed fragments against an identity operand add X[t][f] to
+//     C^T[f][t] exactly (products with 1.0, fp32 accumulation).
+//   * Epilogue through stage 3 in four 64-feature rounds, stored as whole 128-byte row pieces;
+//     the enricher adds b[f] and squares the ReLU in fp32 before the single rounding to bf16.
+#include "avey_common.h"
+#include "launch.h"
+
+namespace avey {
+
+namespace {
+
+constexpr int TF = 256;                 // output features per unit
+constexpr int TT = 256;                 // tokens per unit
+constexpr int KH = 32;                  // K per chunk
+constexpr int XB = TF * 2;              // bytes per W row in LDS
+constexpr int XS = KH * XB;             // W part of a stage (16 KiB)
+constexpr int PB = KH * 2;              // bytes per A row in LDS
+constexpr int STAGE = XS + TT * PB;     // 32 KiB
+constexpr int kMaxF = 4096;             // features held in the LDS bias table
+
+__device__ __forceinline__ uint32_t sw4(int r) { return (uint32_t)((r >> 2) & 3); }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* base, uint32_t off) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+struct GemmParams {
+  const uint16_t* W;       // [K][F], row stride ldw
+  const uint16_t* A1;      // A columns [0, k1): [M][k1] rows of stride lda1
+  const uint16_t* A2;      // A columns [k1, K): [M][K - k1] rows of stride lda2 (nullptr if k1 == K)
+  const uint16_t* R;       // residual [M][F] (stride ldr) or nullptr
+  uint16_t* C;             // [M][F], row stride ldc
+  const float* bias;       // [F] or nullptr
+  int64_t ldw, lda1, lda2, ldr, ldc, M, units;
+  int F, K, k1, f_tiles, relu2;
+};
+
+#define WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+template <int P>
+using Pos = std::integral_constant<int, P>;
+
+__global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
+  __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+  __shared__ __align__(16) float s_bias[kMaxF];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6), wm = wave >> 2, wn = wave & 3;
+
+  // XCD x owns units [xs, xs + cnt) (consecutive units share a token tile); its workgroup l
+  // takes every Gx-th of them from l.
+  const int G = gridDim.x, wg = blockIdx.x, xcd = wg % NXCD, l = wg / NXCD;
+  const int Gx = (G - xcd + NXCD - 1) / NXCD;
+  const int64_t q8 = a.units / NXCD, r8 = a.units % NXCD;
+  const int64_t xs = xcd * q8 + (xcd < r8 ? xcd : r8), cnt = q8 + (xcd < r8 ? 1 : 0);
+  int64_t t = l;
+  if (t >= cnt) return;
+
+  for (int f = tid; f < kMaxF; f += 512) s_bias[f] = (a.bias && f < a.F) ? a.bias[f] : 0.f;
+  lds_sync();   // the bias table is complete (its loads were waited for before the LDS writes)
+
+  const int nreg = a.K / KH;                       // chunks of W x A
+  const int nk = nreg + (a.R ? TT / KH : 0);       // then the residual chunks
+  const int nk4 = (nk + 3) / 4 * 4;                // padded with zero chunks to a multiple of 4
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.W, (uint32_t)((int64_t)a.K * a.ldw * 2));
+  const __amdgpu_buffer_rsrc_t a1r = make_rsrc(a.A1, (uint32_t)(a.M * a.lda1 * 2));
+  const __amdgpu_buffer_rsrc_t a2r = make_rsrc(a.A2, a.A2 ? (uint32_t)(a.M * a.lda2 * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R, a.R ? (uint32_t)(a.M * a.ldr * 2) : 0u);
+
+  // ---- copy side: the unit whose chunks are being copied
+  int64_t c_t0 = 0;
+  int c_f0 = 0;
+  auto set_copy_unit = [&](int64_t tl) {
+    const int64_t L = xs + tl;
+    c_f0 = (int)(L % a.f_tiles) * TF;
+    c_t0 = (L / a.f_tiles) * TT;
+  };
+  // Copy n of chunk kc into stage st: n = 0, 1 are W rows 4 w + 2 n, + 1 (1 KiB; in the
+  // residual chunks the unit's token rows of R), n = 2, 3 are A rows 32 w + 16 (n - 2) .. + 15
+  // (zeros in the residual chunks). Everything past M, F or K loads zeros. The source buffer is
+  // selected per chunk without a branch (a control-flow join around a copy makes the compiler
+  // drain every copy in flight).
+  auto copy = [&](int kc, uint8_t* st, bool valid, int n) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const bool res = kc >= nreg;
+    if (n < 2) {
+      const int tr = wave * 4 + n * 2 + (ln >> 5);
+      const int p = ln & 31;
+      const int c = (p >> 1) ^ (2 * (tr & 3));
+      const int f = c_f0 + c * 16 + (p & 1) * 8;
+      const int64_t row = res ? c_t0 + (int64_t)(kc - nreg) * KH + tr : (int64_t)kc * KH + tr;
+      const int64_t ld = res ? a.ldr : a.ldw;
+      const bool ok = valid && f < a.F && (!res || row < a.M);
+      dma16(res ? rr : wr, st + (wave * 4 + n * 2) * XB, ok ? (uint32_t)((row * ld + f) * 2) : OOB, 0);
+    } else {
+      const int r0 = wave * 32 + (n - 2) * 16;
+      const int64_t tok = c_t0 + r0 + (ln >> 2);
+      const uint32_t piece = (uint32_t)((ln & 3) ^ (int)sw4(r0 + (ln >> 2)));
+      const int k0 = kc * KH;
+      const bool first = k0 < a.k1;
+      const int64_t ld = first ? a.lda1 : a.lda2;
+      const int kk = first ? k0 : k0 - a.k1;
+      const bool ok = valid && !res && tok < a.M;
+      dma16(first ? a1r : a2r, st + XS + r0 * PB, ok ? (uint32_t)(tok * ld * 2) + 16u * piece : OOB,
+            ok ? (uint32_t)kk * 2u : 0u);
+    }
+  };
+  auto dma = [&](int kc, uint8_t* st, bool valid) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) copy(kc, st, valid, n);
+  };
+
+  // ---- fragments: transposed W for the A operand (features 64 mb + 32 wm), A rows for B
+  uint32_t offA[4];
+  {
+    const int s2 = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
+    const uint32_t row = (uint32_t)(8 * (lane >> 5) + ((lane & 15) >> 2)) * XB;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      offA[mb] = row + (uint32_t)((((4 * mb + 2 * wm) ^ (2 * s2)) + g1) << 5) + 8u * (lane & 3);
+  }
+  uint32_t offB[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int rb = wn * 64 + (lane & 31);
+    offB[ks] = (uint32_t)XS + (uint32_t)rb * PB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(rb)) << 4);
+  }
+  f32x16 acc[4][2];
+  uint4 ra0[4], rb0[2], ra1[4], rb1[2];
+  auto fetch = [&](const uint8_t* st, int ks, uint4 (&ra)[4], uint4 (&rb)[2]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const uint2 lo = lds_read_tr8(st, offA[mb] + (uint32_t)(16 * ks) * XB);
+      const uint2 hi = lds_read_tr8(st, offA[mb] + (uint32_t)(16 * ks + 4) * XB);
+      ra[mb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) rb[nb] = lds_read16(st, offB[ks] + nb * 32 * PB);
+  };
+
+  // Residual. Identity fragment of k-step ks: lane l (column l & 31) holds 1.0 at element
+  // (l & 31) - 16 ks - 8 (l >> 5) when that lies in 0..7. Token block nb of this wave sits in
+  // chunk nreg + 2 wn + nb; nreg is even (K % 64 == 0), so that chunk is at an odd pipeline
+  // position exactly when nb = 1.
+  uint4 idB[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int j = (lane & 31) - 16 * ks - 8 * (lane >> 5);
+    uint32_t wv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wv[q] = (j >> 1) == q ? ((j & 1) ? 0x3F800000u : 0x00003F80u) : 0u;
+    idB[ks] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+  auto res_mfma = [&](auto POS, bool on, const uint4 (&ra)[4], int ks) {
+    if (on) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        acc[mb][POS.value & 1] = mfma32(as_bf16x8(ra[mb]), as_bf16x8(idB[ks]), acc[mb][POS.value & 1]);
+    }
+  };
+  const bool has_res = a.R != nullptr;
+
+  // One chunk c from stage st at pipeline position POS (k-step-0 fragments already in ra0 /
+  // rb0); the 4 copies of chunk kc of the copy unit into dst go between the MFMA groups.
+  auto compute_pipe = [&](auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
+                          const uint8_t* next) {
+    const bool ron = has_res && (c == nreg + 2 * wn || c == nreg + 2 * wn + 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+    fetch(st, 1, ra1, rb1);
+    copy(kc, dst, valid, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 2; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+    copy(kc, dst, valid, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    res_mfma(POS, ron, ra0, 0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
+    copy(kc, dst, valid, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) {
+      // 3 of this chunk's copies and the 4 of the previous one may stay in flight
+      WAIT_KEEP(7);
+      fetch(next, 0, ra0, rb0);
+    }
+#pragma unroll
+    for (int mb = 2; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
+    copy(kc, dst, valid, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    res_mfma(POS, ron, ra1, 1);
+  };
+
+  set_copy_unit(t);
+  dma(0, st0, true);
+  dma(1, st1, 1 < nk);
+  dma(2, st2, 2 < nk);
+
+  const bool relu2 = a.relu2 != 0;
+  for (;;) {
+    const bool has_next = t + Gx < cnt;
+    const int64_t Lc = xs + t;
+    const int f0 = (int)(Lc % a.f_tiles) * TF;
+    const int64_t t0 = (Lc / a.f_tiles) * TT;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+
+    // Every chunk is exactly 4 copies per wave, issued unconditionally, so WAIT_KEEP(8) at a
+    // chunk boundary leaves exactly the two newer chunks in flight (older epilogue stores only
+    // make the wait stricter).
+    WAIT_KEEP(8);
+    fetch(st0, 0, ra0, rb0);
+    for (int kc = 0; kc + 4 < nk4; kc += 4) {
+      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      compute_pipe(Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
+      compute_pipe(Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
+      compute_pipe(Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+    }
+    {
+      // last four chunks; the next unit's first three are copied meanwhile
+      const int kc = nk4 - 4;
+      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      if (has_next) set_copy_unit(t + Gx);
+      compute_pipe(Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
+      compute_pipe(Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
+      compute_pipe(Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
+    }
+
+    // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)
+    lds_sync();   // every wave is done reading stage 3
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int sl = wn * 64 + nb * 32 + (lane & 31);
+        const uint32_t rowo = (uint32_t)sl * 128u + 8u * (uint32_t)(lane >> 5);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int fl = mb * 64 + wm * 32 + g * 8 + (lane >> 5) * 4;   // feature in the unit
+          const float4 bq = *reinterpret_cast<const float4*>(&s_bias[(f0 + fl) & (kMaxF - 1)]);
+          const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float y = acc[mb][nb][g * 4 + e] + bb[e];
+            const float r = fmaxf(y, 0.f);
+            v[e] = relu2 ? r * r : y;
+          }
+          const uint32_t pc = (uint32_t)(4 * wm + g) ^ (uint32_t)((sl >> 1) & 7);
+          *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        }
+      }
+      lds_sync();
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int sl = wave * 32 + it * 8 + (lane >> 3);
+        const int p = lane & 7;
+        const uint4 v = lds_read16(st3, (uint32_t)sl * 128u + ((uint32_t)(p ^ ((sl >> 1) & 7)) << 4));
+        const int64_t tok = t0 + sl;
+        const int f = f0 + mb * 64 + p * 8;
+        if (tok < a.M && f < a.F) *reinterpret_cast<uint4*>(a.C + tok * a.ldc + f) = v;
+      }
+      if (mb < 3) lds_sync();
+    }
+    if (!has_next) break;
+    t += Gx;
+  }
+  wait_vmem();   // the zero-filled copies issued past the last unit land before the exit
+}
+
+hipError_t launch_gemm(const GemmParams& p0, hipStream_t stream) {
+  GemmParams p = p0;
+  p.f_tiles = (p.F + TF - 1) / TF;
+  p.units = (p.M + TT - 1) / TT * p.f_tiles;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t grid = p.units < cus ? p.units : cus;
+  hipLaunchKernelGGL(gemm_unit_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_enrich_bf16(const uint16_t* x, int64_t M, int d, int64_t ld_x, const uint16_t* U, int m,
+                              const float* bias, uint16_t* z, int64_t ld_z, hipStream_t stream) {
+  GemmParams p{};
+  p.W = U; p.ldw = m;
+  p.A1 = x; p.lda1 = ld_x; p.k1 = d;
+  p.A2 = nullptr; p.lda2 = 0;
+  p.R = nullptr; p.ldr = 0;
+  p.C = z; p.ldc = ld_z;
+  p.bias = bias; p.relu2 = 1;
+  p.M = M; p.F = m; p.K = d;
+  return launch_gemm(p, stream);
+}
+
+hipError_t launch_fuse_bf16(const uint16_t* z, int64_t M, int m_h, int64_t ld_z, const uint16_t* c, int m_t,
+                            int64_t ld_c, const uint16_t* O, int d, const uint16_t* x_res, int64_t ld_res,
+                            uint16_t* y, int64_t ld_y, hipStream_t stream) {
+  GemmParams p{};
+  p.W = O; p.ldw = d;
+  p.A1 = z; p.lda1 = ld_z; p.k1 = m_h;
+  p.A2 = c; p.lda2 = ld_c;
+  p.R = x_res; p.ldr = ld_res;
+  p.C = y; p.ldc = ld_y;
+  p.bias = nullptr; p.relu2 = 0;
+  p.M = M; p.F = d; p.K = m_h + m_t;
+  return launch_gemm(p, stream);
+}
+
+}  // namespace avey

@@ -33,6 +33,18 @@ hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, 
 hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps,
                            uint16_t* out, int64_t ld_out, hipStream_t stream, LayerEpi epi = {});
 
+constexpr int kEnrichMaxWidth = 4096;   // bf16 enricher: m <= this (LDS bias table)
+hipError_t launch_enrich_bf16(const uint16_t* x, int64_t M, int d, int64_t ld_x, const uint16_t* U, int m,
+                              const float* bias, uint16_t* z, int64_t ld_z, hipStream_t stream);
+hipError_t launch_fuse_bf16(const uint16_t* z, int64_t M, int m_h, int64_t ld_z, const uint16_t* c, int m_t,
+                            int64_t ld_c, const uint16_t* O, int d, const uint16_t* x_res, int64_t ld_res,
+                            uint16_t* y, int64_t ld_y, hipStream_t stream);
+hipError_t launch_enrich_f32(const float* x, int64_t M, int d, int64_t ld_x, const float* U, int m,
+                             const float* bias, float* z, int64_t ld_z, hipStream_t stream);
+hipError_t launch_fuse_f32(const float* z, int64_t M, int m_h, int64_t ld_z, const float* c, int m_t, int64_t ld_c,
+                           const float* O, int d, const float* x_res, int64_t ld_res, float* y, int64_t ld_y,
+                           hipStream_t stream);
+
 hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S, float* scores, hipStream_t stream);
 hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                const int32_t* idx, const float* w, const float* P, int residual, float* xhat,

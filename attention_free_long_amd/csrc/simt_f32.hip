@@ -133,7 +133,54 @@ __global__ void __launch_bounds__(256) dyn_f32_kernel(const float* __restrict__ 
   }
 }
 
+// Enricher: one thread per output element (token t, feature j): ReLU(x_t . U[:, j] + b_j)^2.
+__global__ void __launch_bounds__(256) enrich_f32_kernel(const float* __restrict__ x, int64_t M, int d, int64_t ld_x,
+                                                          const float* __restrict__ U, int m,
+                                                          const float* __restrict__ bias, float* __restrict__ z,
+                                                          int64_t ld_z) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= M * m) return;
+  const int j = (int)(e % m);
+  const int64_t t = e / m;
+  float acc = bias ? bias[j] : 0.f;
+  for (int c = 0; c < d; ++c) acc = fmaf(x[t * ld_x + c], U[(int64_t)c * m + j], acc);
+  const float r = fmaxf(acc, 0.f);
+  z[t * ld_z + j] = r * r;
+}
+
+// Fuser: one thread per output element (token t, feature f):
+// sum_j<m_h z[t][j] O[j][f] + sum_j<m_t c[t][j] O[m_h + j][f] + x_res[t][f].
+__global__ void __launch_bounds__(256) fuse_f32_kernel(const float* __restrict__ z, int64_t M, int m_h, int64_t ld_z,
+                                                        const float* __restrict__ c, int m_t, int64_t ld_c,
+                                                        const float* __restrict__ O, int d,
+                                                        const float* __restrict__ xr, int64_t ld_res,
+                                                        float* __restrict__ y, int64_t ld_y) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= M * d) return;
+  const int f = (int)(e % d);
+  const int64_t t = e / d;
+  float acc = 0.f;
+  for (int j = 0; j < m_h; ++j) acc = fmaf(z[t * ld_z + j], O[(int64_t)j * d + f], acc);
+  for (int j = 0; j < m_t; ++j) acc = fmaf(c[t * ld_c + j], O[(int64_t)(m_h + j) * d + f], acc);
+  y[t * ld_y + f] = acc + xr[t * ld_res + f];
+}
+
 }  // namespace
+
+hipError_t launch_enrich_f32(const float* x, int64_t M, int d, int64_t ld_x, const float* U, int m,
+                             const float* bias, float* z, int64_t ld_z, hipStream_t stream) {
+  hipLaunchKernelGGL(enrich_f32_kernel, dim3((unsigned)((M * m + 255) / 256)), dim3(256), 0, stream, x, M, d, ld_x,
+                     U, m, bias, z, ld_z);
+  return hipGetLastError();
+}
+
+hipError_t launch_fuse_f32(const float* z, int64_t M, int m_h, int64_t ld_z, const float* c, int m_t, int64_t ld_c,
+                           const float* O, int d, const float* x_res, int64_t ld_res, float* y, int64_t ld_y,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(fuse_f32_kernel, dim3((unsigned)((M * d + 255) / 256)), dim3(256), 0, stream, z, M, m_h, ld_z,
+                     c, m_t, ld_c, O, d, x_res, ld_res, y, ld_y);
+  return hipGetLastError();
+}
 
 hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S, float* scores, hipStream_t stream) {
   const int n_s = (int)((N + S - 1) / S);

@@ -80,6 +80,11 @@ def algorithmic(cfg):
         # contextualizer layers outside the step: the tail in, the output out, V and the bias once
         "static_layer": {"flop": 2.0 * B * n_s * S * S * m_t, "bytes": 2 * B * N * m_t * eb + S * S * eb + S * 4},
         "dyn_layer": {"flop": 4.0 * B * n_s * S * S * m_t, "bytes": 2 * B * N * m_t * eb + S * 4},
+        # enricher X [M, d] -> Z [M, m]; fuser [Z_h || c] [M, m] -> Y [M, d] (+ X); weights once
+        "enrich": {"flop": 2.0 * B * N * d * cfg.m,
+                   "bytes": B * N * (d + cfg.m) * eb + d * cfg.m * eb + cfg.m * 4},
+        "fuse": {"flop": 2.0 * B * N * cfg.m * d,
+                 "bytes": B * N * (cfg.m + 2 * d) * eb + cfg.m * d * eb},
     }
 
 
@@ -130,8 +135,10 @@ def cpu_baseline(inp, budget_s: float = 12.0):
 
 
 def time_layers(A, cfg, inp, z_tail, work, steps: int, peak: float):
-    """The static and dynamic contextualizer layers (bias and ReLU) on the same tail, timed apart
-    from the step with HIP events on the launch stream; not part of the step's throughput."""
+    """The rest of a neural-processor layer on the same workload, timed apart from the step with
+    HIP events on the launch stream (not part of the step's throughput): the static and dynamic
+    contextualizer layers (bias and ReLU) on the tail, the enricher X -> Z (d -> m) and the
+    fuser [Z_h || c] -> Y (m -> d, with the residual)."""
     import numpy as np
     import torch
     from synth import layer_params
@@ -142,9 +149,20 @@ def time_layers(A, cfg, inp, z_tail, work, steps: int, peak: float):
         Vd = torch.from_numpy(V).to("cuda")
     bd = torch.from_numpy(bias).to("cuda")
     out = torch.empty((cfg.B, cfg.N, cfg.m_t), device="cuda", dtype=z_tail.dtype)
+    from synth import processor_params
+    U, bU, Ow = processor_params(cfg, cfg.m, u_std=0.02, o_std=0.02, b_std=0.02)
+    dev = (lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(torch.bfloat16)) \
+        if cfg.dtype == "bf16" else (lambda a: torch.from_numpy(a).to("cuda"))
+    Ud, Od, bUd = dev(U), dev(Ow), torch.from_numpy(bU).to("cuda")
+    x = dev(inp.x)
+    zf = torch.empty((cfg.B, cfg.N, cfg.m), device="cuda", dtype=z_tail.dtype)
+    y = torch.empty((cfg.B, cfg.N, cfg.d), device="cuda", dtype=z_tail.dtype)
+    m_h = cfg.m - cfg.m_t
     calls = {
         "static_layer": lambda: A.avey_static_layer(z_tail, Vd, cfg.S, bd, "relu", out=out),
         "dyn_layer": lambda: A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu", out=out),
+        "enrich": lambda: A.avey_enrich(x, Ud, bUd, out=zf),
+        "fuse": lambda: A.avey_fuse(zf, m_h, out, Od, x, out=y),
     }
     res = {}
     for name, call in calls.items():
@@ -160,7 +178,7 @@ def time_layers(A, cfg, inp, z_tail, work, steps: int, peak: float):
         res[name] = {"avg_us": round(t * 1e6, 3),
                      "hbm_frac": round(work[name]["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4),
                      "mfma_frac": round(work[name]["flop"] / t / 1e12 / peak, 4),
-                     "launches": steps, "act": "relu", "bias": True}
+                     "launches": steps}
     return res
 
 
@@ -173,7 +191,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-layers", action="store_true",
-                    help="skip the separate timing of the static and dynamic layers (bias + ReLU)")
+                    help="skip the separate timing of the rest of a layer (static, dynamic, enricher, fuser)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (the "
                          "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")

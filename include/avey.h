@@ -258,6 +258,42 @@ avey_status avey_static_layer(const void* z_tail, avey_dtype dt, int64_t B, int6
                               int64_t ld_z, int32_t S, const void* V, const float* bias,
                               int32_t act, void* out, int64_t ld_out, void* stream);
 
+/*
+ * avey_enrich -- enricher of a neural-processor layer ([notes] 方法详解/整体框架: Z = sigma(X U + b),
+ * a position-wise expansion from d to m features; [summary] appendix A: sigma is ReLU squared).
+ *
+ * For every row t < M (tokens of all sequences, flattened):  z_t = ReLU(x_t U + b)^2.
+ *
+ *   x     [M, d] row stride ld_x (input)
+ *   U     [d, m] contiguous, dtype dt (input)
+ *   b     [m] float32 (input), or NULL for none
+ *   z     [M, m] row stride ld_z, dtype dt (output); its last m_t columns are the tail Z_t the
+ *         contextualizer takes, the first m - m_t the bypassed head
+ * For AVEY_BF16: d and m multiples of 64, m <= 4096 when b is given; fp32 accumulation, one
+ * rounding to bf16 after the bias, ReLU and square.
+ */
+avey_status avey_enrich(const void* x, avey_dtype dt, int64_t M, int64_t d, int64_t ld_x, const void* U,
+                        int64_t m, const float* b, void* z, int64_t ld_z, void* stream);
+
+/*
+ * avey_fuse -- fuser of a neural-processor layer ([notes] 方法详解/整体框架: f(Z) = [Z_h || c(Z_t)] O,
+ * then a residual addition of the layer's input; [summary] section 3).
+ *
+ * For every row t < M:  y_t = [z_t[0 .. m_h) || c_t] O + x_t.
+ *
+ *   z     [M, >= m_h] row stride ld_z (input): only its first m_h columns (the head) are read
+ *   c     [M, m_t] row stride ld_c (input): the contextualised tail (avey_dyn_layer,
+ *         avey_static_layer)
+ *   O     [m_h + m_t, d] contiguous, dtype dt (input)
+ *   x     [M, d] row stride ld_x (input): the layer's input, added to the projection
+ *   y     [M, d] row stride ld_y, dtype dt (output)
+ * m_h may be 0 (no head). For AVEY_BF16: m_h, m_t and d multiples of 64; fp32 accumulation
+ * (the residual is added exactly), one rounding to bf16.
+ */
+avey_status avey_fuse(const void* z, avey_dtype dt, int64_t M, int64_t m_h, int64_t ld_z, const void* c,
+                      int64_t m_t, int64_t ld_c, const void* O, int64_t d, const void* x, int64_t ld_x,
+                      void* y, int64_t ld_y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

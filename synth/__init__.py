@@ -11,5 +11,6 @@ from .inputs import (  # noqa: F401
     f32_to_bf16_bits,
     layer_params,
     make_inputs,
+    processor_params,
     n_splits,
 )

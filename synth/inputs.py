@@ -227,3 +227,20 @@ def layer_params(inp: Inputs) -> tuple[np.ndarray, np.ndarray]:
     mu, sd = float(sample.mean()), float(sample.std())
     bias = (sd * r_b.standard_normal(S) - mu).astype(np.float32)
     return V, bias
+
+
+def processor_params(cfg: Config, m: int, u_std: float | None = None, o_std: float | None = None,
+                     b_std: float = 0.5, seed: int | None = None):
+    """Weights of the enricher and fuser around the contextualizer: U [d, m] and O [m, d] drawn
+    N(0, std^2) (defaults 1/sqrt(d) and 1/sqrt(m), so that X U and [Z_h || c] O are of order
+    one, as with the N(0, 0.02^2) initialisation at the bf16 workloads' widths they are not),
+    b [m] float32 N(0, b_std^2). U and O are stored as ``x`` is. Drawn from the seed's stream 8."""
+    d = cfg.d
+    s = cfg.seed if seed is None else seed
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence(s).spawn(9)[8]))
+    u_std = (1.0 / np.sqrt(d)) if u_std is None else u_std
+    o_std = (1.0 / np.sqrt(m)) if o_std is None else o_std
+    U = _store(cfg, (np.float32(u_std) * r.standard_normal((d, m), dtype=np.float32)))
+    O = _store(cfg, (np.float32(o_std) * r.standard_normal((m, d), dtype=np.float32)))
+    b = (b_std * r.standard_normal(m)).astype(np.float32)
+    return U, b, O

@@ -173,3 +173,32 @@ def test_static_layer_validation(lib):
     assert f(P16, 1, 1, 1024, 64, 64, 32, P16, None, 0, P16, 64, None) == UNSUP     # bf16 S % 64
     assert f(P16, 1, 1, 1024, 64, 32, 64, P16, None, 0, P16, 64, None) == SHAPE     # ld_z < m_t
     assert f(P16, 1, 1, 1024, 64, 64, 0, P16, None, 0, P16, 64, None) == SHAPE      # S < 1
+
+
+def test_enrich_validation(lib):
+    f = lib.avey_enrich
+    # (x, dt, M, d, ld_x, U, m, b, z, ld_z, stream)
+    assert f(None, 1, 0, 64, 64, None, 128, None, None, 128, None) == OK
+    assert f(P16, 1, 100, 64, 64, None, 128, None, P16, 128, None) == NULL      # U
+    assert f(P16, 1, 100, 64, 64, P16, 128, None, None, 128, None) == NULL      # z
+    assert f(P16, 1, 100, 96, 96, P16, 128, None, P16, 128, None) == UNSUP      # bf16 d % 64
+    assert f(P16, 1, 100, 64, 64, P16 + 8, 128, None, P16, 128, None) == ALIGN  # bf16 U 16-aligned
+    assert f(P16, 1, 100, 64, 64, P16, 128, P16 + 2, P16, 128, None) == ALIGN   # b 4-aligned
+    assert f(P16, 1, 100, 64, 64, P16, 8192, P16, P16, 8192, None) == UNSUP     # bf16 m > 4096 with b
+    assert f(P16, 1, 100, 64, 32, P16, 128, None, P16, 128, None) == SHAPE      # ld_x < d
+    assert f(P16, 1, -1, 64, 64, P16, 128, None, P16, 128, None) == SHAPE
+    assert f(P16, 7, 100, 64, 64, P16, 128, None, P16, 128, None) == DTYPE
+
+
+def test_fuse_validation(lib):
+    f = lib.avey_fuse
+    # (z, dt, M, m_h, ld_z, c, m_t, ld_c, O, d, x, ld_x, y, ld_y, stream)
+    assert f(None, 1, 0, 64, 128, None, 64, 64, None, 64, None, 64, None, 64, None) == OK
+    assert f(P16, 1, 10, 64, 128, P16, 64, 64, None, 64, P16, 64, P16, 64, None) == NULL    # O
+    assert f(None, 1, 10, 64, 128, P16, 64, 64, P16, 64, P16, 64, P16, 64, None) == NULL    # z with a head
+    assert f(None, 1, 10, 0, 0, P16, 64, 64, P16 + 8, 64, P16, 64, P16, 64, None) == ALIGN  # no head: z unused
+    assert f(P16, 1, 10, 32, 128, P16, 64, 64, P16, 64, P16, 64, P16, 64, None) == UNSUP    # bf16 m_h % 64
+    assert f(P16, 1, 10, -64, 128, P16, 64, 64, P16, 64, P16, 64, P16, 64, None) == SHAPE
+    assert f(P16, 1, 10, 64, 128, P16, 64, 64, P16 + 8, 64, P16, 64, P16, 64, None) == ALIGN
+    assert f(P16, 1, 10, 64, 128, P16, 64, 64, P16, 64, P16, 32, P16, 64, None) == SHAPE    # ld_x < d
+    assert f(P16, 0, 10, 64, 128, P16, 64, 64, P16 + 2, 64, P16, 64, P16, 64, None) == ALIGN
