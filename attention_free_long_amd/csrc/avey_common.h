@@ -106,6 +106,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// The same over a base address the compiler cannot prove wave-uniform (one computed from
+// values that went through the vector unit): the address and size are read from the first
+// lane, so the descriptor lives in scalar registers. A descriptor the compiler takes as per-lane
+// turns every load through it into a loop over its distinct values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
+
 // An offset past every descriptor this library builds (all are < 2^31 bytes): reads as zero.
 constexpr uint32_t OOB = 0x80000000u;
 

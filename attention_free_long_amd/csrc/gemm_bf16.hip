@@ -122,8 +122,10 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
       const int64_t ld = first ? a.lda1 : a.lda2;
       const int kk = first ? k0 : k0 - a.k1;
       const bool ok = valid && !res && tok < a.M;
+      // the K offset rides in the (uniform) scalar offset; a lane out of range gets an offset
+      // past the buffer in its vector offset
       dma16(first ? a1r : a2r, st + XS + r0 * PB, ok ? (uint32_t)(tok * ld * 2) + 16u * piece : OOB,
-            ok ? (uint32_t)kk * 2u : 0u);
+            res ? 0u : (uint32_t)kk * 2u);
     }
   };
   auto dma = [&](int kc, uint8_t* st, bool valid) {

@@ -140,12 +140,14 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 
   // Copy addressing: a descriptor over the unit's sequence and the byte offsets of its two
   // blocks in chunk 0; chunk kc is kc * S * 64 bytes further.
-  __amdgpu_buffer_rsrc_t xr;
+  const uint16_t* xbase = a.xp;   // the copy unit's sequence
+  uint32_t xbytes = 0;
   int limA = 0, limB = 0;      // valid (non-padding) rows of the unit's blocks
   uint32_t pbA = 0, pbB = 0;
   auto set_unit = [&](const Unit& u) {
     const int64_t seq = (int64_t)a.n_s * a.S * a.d;
-    xr = make_rsrc(a.xp + u.b * seq, (uint32_t)(seq * 2));
+    xbase = a.xp + u.b * seq;
+    xbytes = (uint32_t)(seq * 2);
     limA = (int)min((int64_t)min(a.S - u.ua * T, T), a.N - ((int64_t)u.i * a.S + u.ua * T));
     limB = (int)min((int64_t)min(a.S - u.ub * T, T), a.N - ((int64_t)u.j * a.S + u.ub * T));
     pbA = (uint32_t)((int64_t)u.i * a.S * a.d * 2 + u.ua * T * RB);
@@ -165,6 +167,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int r0 = wave * 32 + n * 16;
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
       dma16(xr, st + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
       dma16(xr, st + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
     }
@@ -196,6 +199,9 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     const uint32_t laneA = pbA + c, laneB = pbB + c;
     auto copy = [&](int ks, int h) {
       const int r0 = wave * 32 + ks * 16;
+      // the descriptor is rebuilt from the first lane at each copy: carried across the loop it
+      // is taken as per-lane, and every copy through it became a loop over distinct values
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
       if (h == 0) dma16(xr, dst + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
       else dma16(xr, dst + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
     };
