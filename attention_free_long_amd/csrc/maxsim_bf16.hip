@@ -191,7 +191,10 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   // One chunk from stage st whose k-step-0 fragments are already in ra0 / rb0; the 4 copies of
   // chunk kc into dst go between the MFMA groups. With next != nullptr the next chunk's wait
   // and barrier come before the last MFMA group, and its k-step-0 fragments are read under it.
-  auto compute_pipe = [&](const uint8_t* st, int kc, uint8_t* dst, bool valid, const uint8_t* next) {
+  // FIRST: the unit's first chunk, whose k-step-0 MFMAs start the accumulators from zero (an
+  // inline constant) instead of reading them, so that nothing has to clear them.
+  const f32x16 zero16 = {};
+  auto compute_pipe = [&](auto FIRST, const uint8_t* st, int kc, uint8_t* dst, bool valid, const uint8_t* next) {
     int sub = lane >> 2;
     asm volatile("" : "+v"(sub));
     const uint32_t kb = (uint32_t)kc * (uint32_t)a.S * RB;
@@ -208,14 +211,16 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     fetch1(st);
     copy(0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     copy(0, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -268,33 +273,43 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     const int cLimA = limA, cLimB = limB;
     const bool valid = own < (is_row ? cLimA : cLimB);
 
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
     // ---- K loop. Every copy is issued unconditionally (a control-flow join around a copy
     // makes the compiler drain all copies before the next LDS read) and every chunk is exactly
     // 4 copies per wave, so WAIT_KEEP(8) at a chunk boundary (WAIT_KEEP(7) before the last MFMA
     // group, with 3 of the current chunk's copies issued) leaves exactly the newer copies in
     // flight.
+    // The unit's first chunk starts the accumulators (FIRST) when there are more than four
+    // chunks; with four, the last group is the first one and they are cleared beforehand.
+    const std::integral_constant<bool, true> kFirst;
+    const std::integral_constant<bool, false> kNext;
+    if (nk4 == 4) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
+    }
     WAIT_KEEP(8);
     fetch0(st0);
-    for (int kc = 0; kc + 4 < nk4; kc += 4) {
-      compute_pipe(st0, kc + 3, st3, kc + 3 < nk, st1);
-      compute_pipe(st1, kc + 4, st0, kc + 4 < nk, st2);
-      compute_pipe(st2, kc + 5, st1, kc + 5 < nk, st3);
-      compute_pipe(st3, kc + 6, st2, kc + 6 < nk, st0);
+    if (nk4 > 4) {
+      compute_pipe(kFirst, st0, 3, st3, 3 < nk, st1);
+      compute_pipe(kNext, st1, 4, st0, 4 < nk, st2);
+      compute_pipe(kNext, st2, 5, st1, 5 < nk, st3);
+      compute_pipe(kNext, st3, 6, st2, 6 < nk, st0);
+      for (int kc = 4; kc + 4 < nk4; kc += 4) {
+        compute_pipe(kNext, st0, kc + 3, st3, kc + 3 < nk, st1);
+        compute_pipe(kNext, st1, kc + 4, st0, kc + 4 < nk, st2);
+        compute_pipe(kNext, st2, kc + 5, st1, kc + 5 < nk, st3);
+        compute_pipe(kNext, st3, kc + 6, st2, kc + 6 < nk, st0);
+      }
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
-      compute_pipe(st0, kc + 3, st3, kc + 3 < nk, st1);
+      compute_pipe(kNext, st0, kc + 3, st3, kc + 3 < nk, st1);
       if (has_next) set_unit(nx);
-      compute_pipe(st1, 0, st0, has_next, st2);
-      compute_pipe(st2, 1, st1, has_next && 1 < nk, st3);
-      compute_pipe(st3, 2, st2, has_next && 2 < nk, nullptr);
+      compute_pipe(kNext, st1, 0, st0, has_next, st2);
+      compute_pipe(kNext, st2, 1, st1, has_next && 1 < nk, st3);
+      compute_pipe(kNext, st3, 2, st2, has_next && 2 < nk, nullptr);
     }
 
     // ---- epilogue (the next unit's first three chunks are in flight into stages 0-2)
