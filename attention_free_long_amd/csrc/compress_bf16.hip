@@ -542,7 +542,10 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   // copies of chunk kc of the copy unit into dst go between the MFMA groups; with next, the
   // next chunk's wait and barrier come before the last group and its first fragments are read
   // under it.
-  auto compute_pipe = [&](auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
+  const f32x16 zero16 = {};
+  // FIRST: the unit's first chunk, whose k-step-0 MFMAs start the accumulators from zero (an
+  // inline constant) instead of reading them, so that nothing has to clear them.
+  auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
                           const uint8_t* next) {
     const int tok0 = chunk_tok0(kc);
     const float wt = wt_of(c);
@@ -550,7 +553,8 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
+            mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     fetchA(st, 1, ra1);
     fetchB(st, 1, wt, rb1);
     copy(kc, dst, valid, 0, tok0);
@@ -558,7 +562,8 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
 #pragma unroll
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
+            mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     copy(kc, dst, valid, 1, tok0);
     __builtin_amdgcn_sched_barrier(0);
     res_mfma(POS, ron, ra0, 0);
@@ -594,17 +599,21 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   dma(2, st2, 2 < nk);
 
   const bool relu = a.epi.act != 0;
+  const std::integral_constant<bool, true> kFirst;
+  const std::integral_constant<bool, false> kNext;
   for (;;) {
     const bool has_next = t + Gx < cnt;
     UnitPos nx = cur;
     if (has_next) nx = unit_pos(t + Gx);
     cur_su = cur.su;
+    // The unit's first chunk starts the accumulators (FIRST) when there are more than four
+    // chunks; with four, the last group is the first one and they are cleared beforehand.
+    if (nk4 == 4) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
+    }
 
     // Every chunk is exactly 4 copies per wave and every copy is issued unconditionally, so
     // WAIT_KEEP(8) at a chunk boundary leaves exactly the two newer chunks in flight (any
@@ -619,20 +628,26 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     }
     fetchA(st0, 0, ra0);
     fetchB(st0, 0, wt_of(0), rb0);
-    for (int kc = 0; kc + 4 < nk4; kc += 4) {
-      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
-      compute_pipe(Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
-      compute_pipe(Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
-      compute_pipe(Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+    if (nk4 > 4) {
+      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1);
+      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2);
+      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3);
+      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0);
+      for (int kc = 4; kc + 4 < nk4; kc += 4) {
+        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
+        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
+        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+      }
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
-      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
       if (has_next) set_copy_unit(nx, bf ^ 1);
-      compute_pipe(Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
-      compute_pipe(Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
-      compute_pipe(Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
+      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
+      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
+      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
     }
 
     // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)

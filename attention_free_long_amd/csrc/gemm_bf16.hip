@@ -185,20 +185,25 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
 
   // One chunk c from stage st at pipeline position POS (k-step-0 fragments already in ra0 /
   // rb0); the 4 copies of chunk kc of the copy unit into dst go between the MFMA groups.
-  auto compute_pipe = [&](auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
+  const f32x16 zero16 = {};
+  // FIRST: the unit's first chunk, whose k-step-0 MFMAs start the accumulators from zero (an
+  // inline constant) instead of reading them, so that nothing has to clear them.
+  auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
                           const uint8_t* next) {
     const bool ron = has_res && (c == nreg + 2 * wn || c == nreg + 2 * wn + 1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
+            mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     fetch(st, 1, ra1, rb1);
     copy(kc, dst, valid, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), acc[mb][nb]);
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
+            mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     copy(kc, dst, valid, 1);
     __builtin_amdgcn_sched_barrier(0);
     res_mfma(POS, ron, ra0, 0);
@@ -228,37 +233,47 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   dma(2, st2, 2 < nk);
 
   const bool relu2 = a.relu2 != 0;
+  const std::integral_constant<bool, true> kFirst;
+  const std::integral_constant<bool, false> kNext;
   for (;;) {
     const bool has_next = t + Gx < cnt;
     const int64_t Lc = xs + t;
     const int f0 = (int)(Lc % a.f_tiles) * TF;
     const int64_t t0 = (Lc / a.f_tiles) * TT;
+    // The unit's first chunk starts the accumulators (FIRST) when there are more than four
+    // chunks; with four, the last group is the first one and they are cleared beforehand.
+    if (nk4 == 4) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
+    }
 
     // Every chunk is exactly 4 copies per wave, issued unconditionally, so WAIT_KEEP(8) at a
     // chunk boundary leaves exactly the two newer chunks in flight (older epilogue stores only
     // make the wait stricter).
     WAIT_KEEP(8);
     fetch(st0, 0, ra0, rb0);
-    for (int kc = 0; kc + 4 < nk4; kc += 4) {
-      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
-      compute_pipe(Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
-      compute_pipe(Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
-      compute_pipe(Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+    if (nk4 > 4) {
+      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1);
+      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2);
+      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3);
+      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0);
+      for (int kc = 4; kc + 4 < nk4; kc += 4) {
+        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
+        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
+        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+      }
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
-      compute_pipe(Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
       if (has_next) set_copy_unit(t + Gx);
-      compute_pipe(Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
-      compute_pipe(Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
-      compute_pipe(Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
+      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
+      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
+      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
     }
 
     // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)
