@@ -513,13 +513,7 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
       offZ[fb] = row + (uint32_t)(((2 * fb + g1) ^ (2 * s2x)) << 5) + 8u * (lane & 3);
   }
   f32x16 acc2[8];
-  auto zero2 = [&]() {
-#pragma unroll
-    for (int fb = 0; fb < 8; ++fb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc2[fb][v] = 0.f;
-  };
-  zero2();
+  const f32x16 zero16 = {};
   auto compute2 = [&](const uint8_t* st, auto qc_tag, int cnext, uint8_t* dst) {
     // cnext: phase-2 chunk index of the copies issued meanwhile
     constexpr int qc = decltype(qc_tag)::value;
@@ -535,8 +529,10 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
         ra[fb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
       const uint4 gb = gfrag[2 * qc + qbl][s2];
+      // the tile's first k-step starts the accumulators from an inline zero
+      const bool first = qc == 0 && ks == 0;
 #pragma unroll
-      for (int fb = 0; fb < 8; ++fb) acc2[fb] = mfma32(as_bf16x8(ra[fb]), as_bf16x8(gb), acc2[fb]);
+      for (int fb = 0; fb < 8; ++fb) acc2[fb] = mfma32(as_bf16x8(ra[fb]), as_bf16x8(gb), first ? zero16 : acc2[fb]);
       copy2(cnext, dst, true, ks);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -587,7 +583,6 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     DYN_WAIT_KEEP(8);
     compute2(st3, std::integral_constant<int, 3>{}, c0 + 6, st2);
     epilogue(ft);
-    zero2();
   }
   wait_vmem();   // the zero-filled copies issued past the last chunk land before the exit
 }
