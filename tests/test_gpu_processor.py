@@ -113,3 +113,24 @@ def test_enrich_fuse_full_size_sampled(gpu_ok):
         ey = rows_err(host_f64(y[bb, toks]), O.fuse(host_f64(z[bb, toks]), m_h, host_f64(c[bb, toks]), O64, xs))
         assert ey <= tol, f"fuse b={bb}: {ey:.3e}"
     say(f"long: {len(toks)} sampled tokens per sequence within {tol}")
+
+
+def test_gemm_edges(gpu_ok):
+    """One partial token tile (100 tokens), the narrowest widths (d = m_h = m_t = 64), no bias;
+    and empty inputs, which enqueue nothing."""
+    cfg = Config("edge", B=1, N=100, d=64, S=64, k=1, m_t=64, m=64, dtype="bf16", z_kind="relu2_x")
+    m, m_h = 128, 64
+    inp = make_inputs(cfg)
+    U, _, Ow = processor_params(cfg, m)
+    say("gemm edges: 100 tokens, d = 64, m = 128, no bias")
+    x = dev_tensor(inp.x, cfg.dtype)
+    z = A.avey_enrich(x, dev_tensor(U, cfg.dtype))
+    c = z[..., m_h:].contiguous()
+    y = A.avey_fuse(z, m_h, c, dev_tensor(Ow, cfg.dtype), x)
+    torch.cuda.synchronize()
+    x64 = inp.x_f64()
+    z_g = host_f64(z)
+    assert rows_err(z_g, O.enrich(x64, as64(U, cfg.dtype), np.zeros(m))) <= TOL["bf16"]["out"]
+    assert rows_err(host_f64(y), O.fuse(z_g, m_h, host_f64(c), as64(Ow, cfg.dtype), x64)) <= TOL["bf16"]["out"]
+    e = torch.empty((1, 0, 64), device="cuda", dtype=torch.bfloat16)
+    assert A.avey_enrich(e, dev_tensor(U, cfg.dtype)).shape == (1, 0, m)
