@@ -21,7 +21,11 @@
 // so pointing lane j at token (j >> 2), features 4 (j & 3) .. + 3 hands lane i four consecutive
 // tokens of feature i.
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid over a 256-feature x 128-token output tile,
+// Two kernels share this scheme: a persistent one (namespace unit, below) for problems with at
+// least one 256-feature x 256-token unit per CU, and the tiled one described here for smaller
+// problems, where its smaller tiles keep more CUs busy.
+//
+// Tiled kernel: 256 threads = 4 waves in a 2 x 2 grid over a 256-feature x 128-token output tile,
 // each wave 128 features x 64 tokens (8 MFMA 32x32x16 blocks), with a 3-stage ring of 24 KiB
 // stages, so that two workgroups share a CU: one's epilogue (residual loads and stores) then
 // overlaps the other's MFMAs.
