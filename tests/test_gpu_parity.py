@@ -315,6 +315,12 @@ PERSISTENT = {
                     x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
     "s64": (Config("p64", B=4, N=16374, d=64, S=64, k=2, m_t=64, m=64, dtype="bf16",
                    x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+    # 384 units: per XCD one full round of 32 workgroups and 16 units left over
+    "tail16": (Config("ptail16", B=1, N=32668, d=768, S=256, k=3, m_t=768, m=768, dtype="bf16",
+                         x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+    # 448 units: per XCD one full round and 24 units left over
+    "tail24": (Config("ptail24", B=1, N=57294, d=512, S=256, k=3, m_t=512, m=512, dtype="bf16",
+                         x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
 }
 
 
