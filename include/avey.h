@@ -55,7 +55,7 @@ typedef enum {
   AVEY_ERR_SHAPE = -2,       /* a size or leading dimension is out of range            */
   AVEY_ERR_DTYPE = -3,       /* unknown dtype                                          */
   AVEY_ERR_ALIGN = -4,       /* a pointer or leading dimension is misaligned           */
-  AVEY_ERR_UNSUPPORTED = -5, /* valid request that this build does not implement       */
+  AVEY_ERR_UNSUPPORTED = -5, /* valid request that this library does not implement     */
   AVEY_ERR_HIP = -6          /* the HIP runtime reported an error at launch            */
 } avey_status;
 
