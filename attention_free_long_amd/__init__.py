@@ -42,6 +42,9 @@ EXPORTS = (
     "avey_static_layer",
     "avey_enrich",
     "avey_fuse",
+    "avey_probe_mfma_flops",
+    "avey_probe_mfma_bf16",
+    "avey_probe_copy",
 )
 
 
@@ -94,6 +97,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_fuse.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.avey_static_layer.restype = i32
     lib.avey_static_layer.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp, i32, vp, i64, vp]
+    lib.avey_probe_mfma_flops.restype = i64
+    lib.avey_probe_mfma_flops.argtypes = [i64]
+    lib.avey_probe_mfma_bf16.restype = i32
+    lib.avey_probe_mfma_bf16.argtypes = [i64, i32, vp, vp]
+    lib.avey_probe_copy.restype = i32
+    lib.avey_probe_copy.argtypes = [vp, vp, i64, vp]
     ver = lib.avey_abi_version()
     if ver != AVEY_ABI_VERSION:
         raise AveyError("load_library", -101, f"ABI version {ver}, expected {AVEY_ABI_VERSION}")
@@ -345,3 +354,36 @@ def avey_fuse(z, m_h: int, c, O, x, out=None):
         z.data_ptr(), _dtype_code(x), B * N, m_h, ld_z, c.data_ptr(), m_t, ld_c, O.data_ptr(), d,
         x.data_ptr(), ld_x, out.data_ptr(), ld_y, _stream(x)))
     return out
+
+
+# ---- peak micro-benchmarks (include/avey_probe.h): the measured ceilings, not the hot path
+
+def avey_probe_mfma_flops(iters: int) -> int:
+    """bf16 FLOPs one avey_probe_mfma_bf16 launch of `iters` iterations performs on this device."""
+    n = load_library().avey_probe_mfma_flops(int(iters))
+    if n < 0:
+        _check("avey_probe_mfma_flops", int(n))
+    return int(n)
+
+
+def avey_probe_mfma_bf16(iters: int, changing: bool, sink=None):
+    """Enqueue the matrix-core probe on the current stream (register operands, no memory traffic;
+    `changing` replaces the operands every iteration). Returns the sink buffer it was given or
+    allocated (one float per compute unit)."""
+    import torch
+    if sink is None:
+        sink = torch.zeros(4096, device="cuda", dtype=torch.float32)
+    st = torch.cuda.current_stream().cuda_stream
+    _check("avey_probe_mfma_bf16",
+           load_library().avey_probe_mfma_bf16(int(iters), 1 if changing else 0, sink.data_ptr(), st))
+    return sink
+
+
+def avey_probe_copy(src, dst) -> None:
+    """Enqueue dst <- src (same number of bytes, contiguous, 16-byte aligned) on the current stream."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_contiguous() and dst.is_contiguous()) or dst.numel() * dst.element_size() != nbytes:
+        raise AveyError("avey_probe_copy", -2, "src and dst must be contiguous and of the same size in bytes")
+    st = torch.cuda.current_stream().cuda_stream
+    _check("avey_probe_copy", load_library().avey_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, st))

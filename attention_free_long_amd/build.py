@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libavey.so")
 
 ARCH = "gfx950"
-SOURCES = ["abi.hip", "prepare.hip", "maxsim_bf16.hip", "topk.hip", "compress_bf16.hip", "dyn_bf16.hip", "gemm_bf16.hip", "simt_f32.hip"]
+SOURCES = ["abi.hip", "prepare.hip", "maxsim_bf16.hip", "topk.hip", "compress_bf16.hip", "dyn_bf16.hip", "gemm_bf16.hip", "simt_f32.hip", "peak_probe.hip"]
 
 # Packed fp32 instructions are kept out of all device code (the host pass warns that it does not
 # know the feature; that warning is harmless).

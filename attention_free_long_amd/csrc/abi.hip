@@ -1,5 +1,6 @@
 // C ABI of libavey.so: argument checks and kernel launches. See include/avey.h for the contract.
 #include "avey.h"
+#include "avey_probe.h"
 
 #include <stdint.h>
 
@@ -363,6 +364,33 @@ avey_status avey_fuse(const void* z, avey_dtype dt, int64_t M, int64_t m_h, int6
   return hip_status(launch_fuse_f32(static_cast<const float*>(z), M, (int)m_h, ld_z, static_cast<const float*>(c),
                                     (int)m_t, ld_c, static_cast<const float*>(O), (int)d,
                                     static_cast<const float*>(x), ld_x, static_cast<float*>(y), ld_y, st));
+}
+
+int64_t avey_probe_mfma_flops(int64_t iters) {
+  if (iters < 1) return AVEY_ERR_SHAPE;
+  const int cus = probe_cus();
+  if (cus < 0) return AVEY_ERR_HIP;
+  // per iteration and wave: 16 MFMAs of 32 x 32 x 16 multiply-adds
+  return (int64_t)cus * 8 * iters * 16 * (2 * 32 * 32 * 16);
+}
+
+avey_status avey_probe_mfma_bf16(int64_t iters, int32_t changing, float* sink, void* stream) {
+  if (iters < 1) return AVEY_ERR_SHAPE;
+  if (!sink) return AVEY_ERR_NULL;
+  if (!aligned(sink, 4)) return AVEY_ERR_ALIGN;
+  const int cus = probe_cus();
+  if (cus < 0) return AVEY_ERR_HIP;
+  return hip_status(launch_mfma_probe(iters, changing != 0, sink, cus, static_cast<hipStream_t>(stream)));
+}
+
+avey_status avey_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16) return AVEY_ERR_SHAPE;
+  if (bytes == 0) return AVEY_OK;
+  if (!src || !dst) return AVEY_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return AVEY_ERR_ALIGN;
+  const int cus = probe_cus();
+  if (cus < 0) return AVEY_ERR_HIP;
+  return hip_status(launch_copy_probe(src, dst, bytes, cus, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

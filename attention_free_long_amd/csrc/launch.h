@@ -52,4 +52,9 @@ hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int6
 hipError_t launch_dyn_f32(const float* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps, float* out,
                           int64_t ld_out, hipStream_t stream, LayerEpi epi = {});
 
+// Peak micro-benchmarks (peak_probe.hip).
+int probe_cus();   // compute units of the current device, or -1
+hipError_t launch_mfma_probe(int64_t iters, int changing, float* sink, int cus, hipStream_t stream);
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int cus, hipStream_t stream);
+
 }  // namespace avey

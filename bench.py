@@ -35,8 +35,8 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("8d126d048c5c1965", "long"): {"fetch_kib": 1216846.6, "fetch_scale": 1.99995,
-                                           "write_kib": 252.5, "write_scale": 1.0},
+            ("baf884bcbc72d556", "long"): {"fetch_kib": 1216465.3, "fetch_scale": 1.99995,
+                                           "write_kib": 252.6, "write_scale": 1.0},
         },
     },
 }
@@ -206,6 +206,43 @@ def time_compress_cold(call, work_bytes: float, reps: int = 10):
             "flush": "512 MiB written before each launch"}
 
 
+def measured_peaks(A, reps: int = 10):
+    """The two ceilings measured on this device (include/avey_probe.h), medians of `reps` launches
+    timed with HIP events: the bf16 matrix-core rate on register operands that stay fixed or
+    change every iteration (as data streamed from memory does), and a 1 GiB device copy."""
+    import numpy as np
+    import torch
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    iters = 2000
+    flops = A.avey_probe_mfma_flops(iters)
+    sink = A.avey_probe_mfma_bf16(1, False)
+    fixed = flops / timed(lambda: A.avey_probe_mfma_bf16(iters, False, sink)) / 1e12
+    changing = flops / timed(lambda: A.avey_probe_mfma_bf16(iters, True, sink)) / 1e12
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * n / timed(lambda: A.avey_probe_copy(src, dst)) / 1e9
+    del src, dst
+    return {"mfma_bf16_tflops_fixed_operands": round(fixed, 1),
+            "mfma_bf16_tflops_changing_operands": round(changing, 1),
+            "copy_gbs": round(copy_gbs, 1),
+            "method": f"avey_probe_mfma_bf16 ({iters} iterations, one 8-wave workgroup per CU) and "
+                      f"avey_probe_copy (1 GiB, read + written), median of {reps} launches"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +375,12 @@ def main(argv=None):
         "kernels": {n: {kk: round(v, 3) for kk, v in e.items()} for n, e in kern.items()},
     }
     result["compress_cold"] = time_compress_cold(calls[3], work["compress"]["bytes"])
+    if cfg.dtype == "bf16":
+        mp = measured_peaks(A)
+        result["measured_peaks"] = mp
+        roofline["measured_peak"] = mp["mfma_bf16_tflops_changing_operands"]
+        roofline["frac_measured"] = round(achieved / mp["mfma_bf16_tflops_changing_operands"], 4)
+        result["compress_hbm_frac_measured"] = round(work["compress"]["bytes"] / comp_t / 1e9 / mp["copy_gbs"], 4)
     if not args.no_layers:
         result["layers"] = time_layers(A, cfg, inp, z_tail, work, max(10, args.steps // 2), peak)
     if not args.no_cpu_baseline:

@@ -1,4 +1,4 @@
-"""libavey.so loads on the host, exports every function include/avey.h declares, and rejects bad
+"""libavey.so loads on the host, exports every function include/*.h declares, and rejects bad
 arguments before any HIP call (CPU only: every call here fails validation or is empty work)."""
 import ctypes
 import os
@@ -9,7 +9,8 @@ import pytest
 import attention_free_long_amd as A
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "avey.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP = 0, -1, -2, -3, -4, -5
 P16 = 0x10000          # fake, 16-byte aligned device address: never dereferenced by these calls
@@ -17,7 +18,7 @@ P4 = 0x10004           # 4-byte aligned, not 16-byte aligned
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(avey_[a-z_0-9]+)\s*\(", src)))
 
@@ -202,3 +203,21 @@ def test_fuse_validation(lib):
     assert f(P16, 1, 10, 64, 128, P16, 64, 64, P16 + 8, 64, P16, 64, P16, 64, None) == ALIGN
     assert f(P16, 1, 10, 64, 128, P16, 64, 64, P16, 64, P16, 32, P16, 64, None) == SHAPE    # ld_x < d
     assert f(P16, 0, 10, 64, 128, P16, 64, 64, P16 + 2, 64, P16, 64, P16, 64, None) == ALIGN
+
+
+def test_probe_validation(lib):
+    f = lib.avey_probe_mfma_flops
+    assert f(0) == SHAPE
+    m = lib.avey_probe_mfma_bf16
+    # (iters, changing, sink, stream)
+    assert m(0, 0, P16, None) == SHAPE
+    assert m(10, 0, None, None) == NULL
+    assert m(10, 1, P16 + 2, None) == ALIGN
+    c = lib.avey_probe_copy
+    # (src, dst, bytes, stream)
+    assert c(P16, P16 + 4096, 0, None) == OK            # nothing to copy
+    assert c(P16, P16 + 4096, -16, None) == SHAPE
+    assert c(P16, P16 + 4096, 24, None) == SHAPE         # not a multiple of 16
+    assert c(None, P16, 32, None) == NULL
+    assert c(P4, P16, 32, None) == ALIGN
+    assert c(P16, P4, 32, None) == ALIGN
