@@ -337,10 +337,16 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
 //     4-feature groups into a [256 tokens][64 features] bf16 tile, then 8 lanes per token store
 //     whole 128-byte rows (scattered 8-byte stores would cost a write request per lane).
 //   * Source splits and weights of the next unit are read with scalar loads into a second LDS
-//     table, so that the copies stay the only vector-memory operations of the K loop.
+//     table, so that the copies stay the only vector-memory operations of the K loop. When the
+//     copies move on to a unit, its block table is loaded once into one VGPR (lane r: block r's
+//     first token); each chunk then takes its token base with a lane read, with no LDS load
+//     (whose wait would also drain the fragment reads in flight).
+//   * The per-chunk bookkeeping is kept to scalar integer work without divisions (chunk ->
+//     block by a multiply-shift) and the copy offsets to 32-bit arithmetic without branches.
 namespace unit {
 
 constexpr int TU = 256;                 // output tokens per unit
+constexpr int kMaxBlocks = 64;          // k + 1: one lane of a VGPR per block of the unit's table
 constexpr int USTAGE = XS + TU * PB;    // 32 KiB: 32 X rows of 256 features + 256 P rows
 
 struct UnitPos {
@@ -377,6 +383,9 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   const int cpb = a.S / KH;               // chunks per block
   const int nk = KP / KH;
   const int nk4 = (nk + 3) / 4 * 4;       // padded with zero chunks: every unit starts on stage 0
+  // floor(c / cpb) as (c * cpb_magic) >> 20: exact while c * (cpb_magic * cpb - 2^20) < 2^20,
+  // i.e. for c < 2^16 with cpb <= 16, far above any chunk index here
+  const uint32_t cpb_magic = ((1u << 20) + (uint32_t)cpb - 1u) / (uint32_t)cpb;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((int64_t)a.S * KP * 2));
 
   auto unit_pos = [&](int64_t tl) {
@@ -412,26 +421,30 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
 
   // ---- copy side: the unit whose chunks are being copied (the next one near a unit's end)
   __amdgpu_buffer_rsrc_t xr;
-  int c_bf = 0, c_su = 0, c_fb = 0;
+  int c_su = 0, c_fb = 0;
+  int vtok = 0;   // lane r: first token of block r of the copy unit (the launcher ensures k + 1 <= 64)
   auto set_copy_unit = [&](const UnitPos& u, int bf) {
     xr = make_rsrc(a.x + u.b * a.N * a.ld_x, (uint32_t)(a.N * a.ld_x * 2));
-    c_bf = bf;
     c_su = u.su;
     c_fb = u.f_base;
+    vtok = lane <= a.k ? s_tok0[bf][lane] : 0;
   };
   // Chunk c covers block (c / cpb + 1) mod (k + 1): blocks 1..k, then block 0.
   auto chunk_block = [&](int c, int& r, int& j) {
-    const int q = c / cpb;
+    const int q = (int)(((uint32_t)c * cpb_magic) >> 20);
     r = q < a.k ? q + 1 : 0;
     j = c - q * cpb;
   };
+  // one lane read per chunk instead of an LDS load, whose wait would also drain the fragment reads
   auto chunk_tok0 = [&](int kc) {
     int r, j;
     chunk_block(kc, r, j);
-    return uniform(s_tok0[c_bf][r]) + j * KH;
+    return __builtin_amdgcn_readlane(vtok, r) + j * KH;
   };
   // Copy n of chunk kc into stage st: n = 0, 1 are X rows 4 w + 2 n, + 1 (1 KiB), n = 2, 3 are
-  // P rows 32 w + 16 (n - 2) .. + 15. Tokens past N, features past d and rows past S load zeros.
+  // P rows 32 w + 16 (n - 2) .. + 15. Tokens past N, features past d and rows past S load zeros:
+  // their offset gets the high bit, past the descriptor's range (a sequence and P are < 2^31
+  // bytes), so that the offsets are plain 32-bit arithmetic without a branch.
   auto copy = [&](int kc, uint8_t* st, bool valid, int n, int tok0) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -439,10 +452,11 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       const int tr = wave * 4 + n * 2 + (ln >> 5);
       const int p = ln & 31;
       const int c = (p >> 1) ^ (2 * (tr & 3));
-      const int f = c_fb + c * 16 + (p & 1) * 8;
-      const int64_t tok = (int64_t)tok0 + tr;
-      const bool ok = valid && tok >= 0 && tok < a.N && f < a.d;
-      dma16(xr, st + (wave * 4 + n * 2) * XB, ok ? (uint32_t)((tok * a.ld_x + f) * 2) : OOB, 0);
+      const int fl = c * 16 + (p & 1) * 8;                 // feature within the tile
+      const uint32_t tok = (uint32_t)(tok0 + tr);          // an empty block's tokens wrap above N
+      const bool ok = valid & (tok < (uint32_t)a.N) & (fl < a.d - c_fb);
+      const uint32_t off = (tok * (uint32_t)a.ld_x + (uint32_t)(c_fb + fl)) * 2u;
+      dma16(xr, st + (wave * 4 + n * 2) * XB, off | ((uint32_t)!ok << 31), 0);
     } else {
       const int r0 = wave * 32 + (n - 2) * 16;
       const int row = r0 + (ln >> 2);
@@ -451,8 +465,9 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       int r, j;
       chunk_block(kc, r, j);
       const int kk0 = r * a.S + j * KH;
-      const bool ok = valid && s < a.S;
-      dma16(pr, st + XS + r0 * PB, ok ? (uint32_t)s * (uint32_t)KP * 2u + 16u * piece : OOB, (uint32_t)kk0 * 2u);
+      const bool ok = valid & (s < a.S);
+      dma16(pr, st + XS + r0 * PB, ((uint32_t)s * (uint32_t)KP * 2u + 16u * piece) | ((uint32_t)!ok << 31),
+            (uint32_t)kk0 * 2u);
     }
   };
   auto dma = [&](int kc, uint8_t* st, bool valid) {
@@ -476,6 +491,9 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     const int rb = wn * 64 + (lane & 31);
     offB[ks] = (uint32_t)XS + (uint32_t)rb * PB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(rb)) << 4);
   }
+  int bf = 0, cur_su = 0;
+  bool slow = false;
+  int rc0 = -1, rc1 = -1;   // the chunks of the current unit that add the residual (token blocks 0, 1)
   f32x16 acc[4][2];
   uint4 ra0[4], rb0[2], ra1[4], rb1[2];
   auto fetchA = [&](const uint8_t* st, int ks, uint4 (&ra)[4]) {
@@ -490,13 +508,11 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const uint4 v = lds_read16(st, offB[ks] + nb * 32 * PB);
-      rb[nb] = wt == 1.f ? v : scale8(v, wt);
+      rb[nb] = slow ? scale8(v, wt) : v;
     }
   };
 
   // ---- compute side: the unit being multiplied
-  int bf = 0, cur_su = 0;
-  bool slow = false;
   auto wt_of = [&](int c) {   // weight applied to chunk c's P fragments (slow path only)
     if (!slow || c >= nk) return 1.f;
     int r, j;
@@ -506,10 +522,10 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   // After chunk c: at the last chunk of a retrieved block r, multiply the accumulator by
   // w_r / w_{r+1} (by w_k after block k).
   auto post = [&](int c) {
-    if (slow || c >= nk || (c + 1) % cpb) return;
+    if (slow || c >= nk) return;
     int r, j;
     chunk_block(c, r, j);
-    if (r == 0) return;
+    if (j != cpb - 1 || r == 0) return;
     const float f = r < a.k ? s_wt[bf][r] / s_wt[bf][r + 1] : s_wt[bf][r];
     if (f == 1.f) return;
 #pragma unroll
@@ -553,7 +569,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
                           const uint8_t* next) {
     const int tok0 = chunk_tok0(kc);
     const float wt = wt_of(c);
-    const bool ron = a.residual && (c == res_chunk(0) || c == res_chunk(1));
+    const bool ron = (c == rc0) | (c == rc1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -610,6 +626,8 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     UnitPos nx = cur;
     if (has_next) nx = unit_pos(t + Gx);
     cur_su = cur.su;
+    rc0 = a.residual ? res_chunk(0) : -1;
+    rc1 = a.residual ? res_chunk(1) : -1;
     // The unit's first chunk starts the accumulators (FIRST) when there are more than four
     // chunks; with four, the last group is the first one and they are cleared beforehand.
     if (nk4 == 4) {
@@ -718,9 +736,10 @@ hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, 
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   // At least one 256 x 256 unit per CU: the persistent kernel; otherwise the tiled one, whose
-  // smaller tiles keep more CUs busy.
+  // smaller tiles keep more CUs busy. The persistent kernel keeps a unit's block table in one
+  // lane per block, so it takes k + 1 <= 64 (the tiled kernel any k).
   const int64_t units = B * p.n_s * ((S + unit::TU - 1) / unit::TU) * p.f_tiles;
-  if (units >= cus) {
+  if (units >= cus && k + 1 <= unit::kMaxBlocks) {
     p.s_tiles = (S + unit::TU - 1) / unit::TU;
     p.tiles = units;
     hipLaunchKernelGGL(unit::compress_unit_kernel, dim3((unsigned)cus), dim3(512), 0, stream, p);

@@ -321,6 +321,10 @@ PERSISTENT = {
     # 448 units: per XCD one full round and 24 units left over
     "tail24": (Config("ptail24", B=1, N=57294, d=512, S=256, k=3, m_t=512, m=512, dtype="bf16",
                          x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+    # 320 units but k + 1 = 71 blocks, more than the persistent kernel's table holds: the tiled
+    # kernel takes it
+    "k70": (Config("pk70", B=4, N=5100, d=64, S=64, k=70, m_t=64, m=64, dtype="bf16",
+                   x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
 }
 
 
