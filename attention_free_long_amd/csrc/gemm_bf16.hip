@@ -104,27 +104,29 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const bool res = kc >= nreg;
+    // Offsets are 32-bit (every operand is below 2^31 bytes); a lane out of range gets the high
+    // bit, past the descriptor's range, so that no branch is needed.
     if (n < 2) {
       const int tr = wave * 4 + n * 2 + (ln >> 5);
       const int p = ln & 31;
       const int c = (p >> 1) ^ (2 * (tr & 3));
-      const int f = c_f0 + c * 16 + (p & 1) * 8;
-      const int64_t row = res ? c_t0 + (int64_t)(kc - nreg) * KH + tr : (int64_t)kc * KH + tr;
-      const int64_t ld = res ? a.ldr : a.ldw;
-      const bool ok = valid && f < a.F && (!res || row < a.M);
-      dma16(res ? rr : wr, st + (wave * 4 + n * 2) * XB, ok ? (uint32_t)((row * ld + f) * 2) : OOB, 0);
+      const int fl = c * 16 + (p & 1) * 8;                  // feature within the tile
+      const uint32_t row = res ? (uint32_t)c_t0 + (uint32_t)((kc - nreg) * KH + tr) : (uint32_t)(kc * KH + tr);
+      const uint32_t ld = res ? (uint32_t)a.ldr : (uint32_t)a.ldw;
+      const bool ok = valid & (fl < a.F - c_f0) & (!res | (row < (uint32_t)a.M));
+      const uint32_t off = (row * ld + (uint32_t)(c_f0 + fl)) * 2u;
+      dma16(res ? rr : wr, st + (wave * 4 + n * 2) * XB, off | ((uint32_t)!ok << 31), 0);
     } else {
       const int r0 = wave * 32 + (n - 2) * 16;
-      const int64_t tok = c_t0 + r0 + (ln >> 2);
+      const uint32_t tok = (uint32_t)c_t0 + (uint32_t)(r0 + (ln >> 2));
       const uint32_t piece = (uint32_t)((ln & 3) ^ (int)sw4(r0 + (ln >> 2)));
       const int k0 = kc * KH;
       const bool first = k0 < a.k1;
-      const int64_t ld = first ? a.lda1 : a.lda2;
+      const uint32_t ld = first ? (uint32_t)a.lda1 : (uint32_t)a.lda2;
       const int kk = first ? k0 : k0 - a.k1;
-      const bool ok = valid && !res && tok < a.M;
-      // the K offset rides in the (uniform) scalar offset; a lane out of range gets an offset
-      // past the buffer in its vector offset
-      dma16(first ? a1r : a2r, st + XS + r0 * PB, ok ? (uint32_t)(tok * ld * 2) + 16u * piece : OOB,
+      const bool ok = valid & !res & (tok < (uint32_t)a.M);
+      // the K offset rides in the (uniform) scalar offset
+      dma16(first ? a1r : a2r, st + XS + r0 * PB, (tok * ld * 2u + 16u * piece) | ((uint32_t)!ok << 31),
             res ? 0u : (uint32_t)kk * 2u);
     }
   };
