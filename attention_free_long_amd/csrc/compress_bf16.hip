@@ -5,12 +5,14 @@
 // scores per 方法详解/整体框架; residual to the split's own tokens per the paperlayer.ai
 // "Avey-B" summary, appendix H). X_cat is never materialised: the K dimension of the GEMM,
 // (k+1)S, walks the gathered splits through idx, one 32-token chunk at a time, the retrieved
-// blocks 1..k first and the split's own block 0 last. The weights are applied to the fp32
-// accumulator between blocks: after block r it is multiplied by w_r / w_{r+1}, after block k
-// by w_k, so that it ends as sum_r w_r (P_r X_r) + P_0 X_0. This holds whenever every weight is
-// a positive normal number in [2^-60, 2^60] (top-k weights are, unless a score is zero or
-// negative); otherwise each P fragment of block r is multiplied by w_r as it is read (rounded
-// to bf16), using (w P_r) X = P_r (w X).
+// blocks first and the split's own block last. The weights are applied to the fp32 accumulator
+// between blocks: with the retrieved blocks taken in ascending order of |w| as w_1..w_k, after
+// block r it is multiplied by w_r / w_{r+1}, after block k by w_k, so that it ends as
+// sum_r w_r (P_r X_r) + P_0 X_0 (P_r: the columns of P for the block's rank in the selection).
+// Every factor lies in [-1, 1] except the last, which cannot overflow a finite result; a factor
+// that underflows to zero drops a block whose term is below 2^-149 of a later one. Blocks that
+// add nothing (an empty block, a zero weight) come after the others with factor 1; a NaN or
+// infinite weight comes last and makes the split's outputs non-finite, as it makes w X.
 //
 // The product is computed transposed, C[f][s] = sum_kk X_cat[kk][f] P[s][kk], so that each lane
 // of the result owns one output token and four consecutive features (8-byte stores). Both
@@ -57,14 +59,14 @@ __device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* base, uint32_t off)
   return __builtin_bit_cast(uint2, v);
 }
 
-// Eight bf16 values times w, rounded to bf16 (round to nearest even).
-__device__ __forceinline__ uint4 scale8(uint4 v, float w) {
-  uint4 o;
-  o.x = pack_bf16(bf16lo(v.x) * w, bf16hi(v.x) * w);
-  o.y = pack_bf16(bf16lo(v.y) * w, bf16hi(v.y) * w);
-  o.z = pack_bf16(bf16lo(v.z) * w, bf16hi(v.z) * w);
-  o.w = pack_bf16(bf16lo(v.w) * w, bf16hi(v.w) * w);
-  return o;
+// Order of a retrieved block (index src, weight w) in the K loop: ascending |w| (the bits of a
+// finite |w| order as the values do), then the blocks that contribute nothing (an empty block,
+// negative index; a zero weight), then those with a non-finite weight.
+constexpr uint32_t kKeyNone = 0x7F800000u;
+__device__ __forceinline__ uint32_t block_key(int src, float w) {
+  if (src < 0 || w == 0.f) return kKeyNone;
+  const uint32_t m = __float_as_uint(w) & 0x7FFFFFFFu;
+  return m < kKeyNone ? m : kKeyNone + 1u;
 }
 
 struct CompressParams {
@@ -87,9 +89,9 @@ constexpr int kEmptyBlock = -(1 << 30);      // first token of an empty block: e
 __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE];
   __shared__ int s_tok0[MAXBLK];     // first token of block r's source split
-  __shared__ float s_wt[MAXBLK];     // weight applied to block r's P fragments
+  __shared__ int s_col0[MAXBLK];     // first column of P that multiplies block r
+  __shared__ float s_wt[MAXBLK];     // weight of block r
   __shared__ float s_ps[MAXBLK];     // accumulator factor after block r's last chunk
-  __shared__ int s_slow;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6), wm = wave >> 1, wn = wave & 1;
@@ -112,43 +114,41 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   const int nk3 = (nk + 2) / 3 * 3;
   const int f_base = ft * TF;
 
-  // Source split and weights of every block, staged in LDS before any copy is issued: inside
-  // the K loop only the copies may count as vector-memory operations, so that the copy waits
-  // count exactly 4 per chunk.
-  if (tid == 0) s_slow = 0;
+  // Block table, staged in LDS before any copy is issued: inside the K loop only the copies may
+  // count as vector-memory operations, so that the copy waits count whole chunks. Slot 0
+  // is the split's own block; the retrieved blocks follow in block_key order, so that every
+  // accumulator factor w_r / w_(r+1) lies in [-1, 1]. The sort keys sit in s_ps until the
+  // factors replace them.
+  uint32_t* s_key = reinterpret_cast<uint32_t*>(s_ps);
+  for (int r = tid + 1; r <= a.k; r += 256) s_key[r] = block_key(idx_i[r - 1], w_i[r - 1]);
   __syncthreads();
   for (int r = tid; r <= a.k; r += 256) {
-    const int src = r ? idx_i[r - 1] : i;
-    // a negative index is an empty block (zero rows, as the unidirectional ranker pads its
-    // selection): its copies load zeros and its weight is taken as 1, which changes nothing
-    s_tok0[r] = src < 0 ? kEmptyBlock : min(src, a.n_s - 1) * a.S;
-    const float wr = (r && src >= 0) ? w_i[r - 1] : 1.f;
-    s_wt[r] = wr;
-    if (!(wr >= 0x1p-60f && wr <= 0x1p60f)) s_slow = 1;   // also catches NaN
+    if (r == 0) {
+      s_tok0[0] = i * a.S;
+      s_col0[0] = 0;
+      s_wt[0] = 1.f;
+      continue;
+    }
+    const uint32_t key = s_key[r];
+    int pos = 1;   // 1 + the number of retrieved blocks ordered before this one
+    for (int j = 1; j <= a.k; ++j) pos += (s_key[j] < key || (s_key[j] == key && j < r)) ? 1 : 0;
+    const bool none = key == kKeyNone;
+    // an empty block (zero rows, as the unidirectional ranker pads its selection) or a zero
+    // weight: its copies load zeros and its factor is 1
+    s_tok0[pos] = none ? kEmptyBlock : min(idx_i[r - 1], a.n_s - 1) * a.S;
+    s_col0[pos] = r * a.S;   // P keeps the rank order of the selection
+    s_wt[pos] = none ? 1.f : w_i[r - 1];
   }
   __syncthreads();
-  const bool slow = s_slow != 0;
-  for (int r = tid; r <= a.k; r += 256) {
-    const float wr = s_wt[r];
-    float ps = 1.f;
-    if (!slow && r >= 1) ps = r < a.k ? wr / s_wt[r + 1] : wr;
-    s_ps[r] = ps;
-    if (!slow) s_wt[r] = 1.f;
-  }
+  for (int r = tid; r <= a.k; r += 256) s_ps[r] = r == 0 ? 1.f : r < a.k ? s_wt[r] / s_wt[r + 1] : s_wt[r];
   __syncthreads();
-  // Chunk c of the K loop covers block (c / cpb + 1) mod (k + 1): blocks 1..k, then block 0.
+  // Chunk c of the K loop covers slot (c / cpb + 1) mod (k + 1): slots 1..k, then slot 0; j is
+  // its offset within the block.
   const int cpb = a.S / KH;
-  auto chunk_block = [&](int c, int& r, int& kk0) {
+  auto chunk_block = [&](int c, int& r, int& j) {
     const int q = c / cpb;
     r = q < a.k ? q + 1 : 0;
-    kk0 = r * a.S + (c - q * cpb) * KH;
-  };
-  // Source tokens and fragment weight of chunk c.
-  auto chunk_src = [&](int c, int& tok0, float& wt) {
-    int r, kk0;
-    chunk_block(c, r, kk0);
-    tok0 = s_tok0[r] + (kk0 - r * a.S);
-    wt = s_wt[r];
+    j = (c - q * cpb) * KH;
   };
 
   // Chunk kc into stage st, 6 copies per wave: X tokens 8w .. 8w + 7 (n = 0..3, 2 tokens per
@@ -158,10 +158,10 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   auto copy_chunk = [&](int kc, uint8_t* st, bool valid, int n) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    int r, j;
+    chunk_block(kc, r, j);
     if (n < 4) {
-      int tok0 = 0;
-      float wt_unused;
-      chunk_src(kc, tok0, wt_unused);
+      const int tok0 = s_tok0[r] + j;
       const int t = wave * 8 + n * 2 + (ln >> 5);                  // row in the stage
       const int p = ln & 31;                                       // 16-byte position in the row
       const int c = (p >> 1) ^ (2 * (t & 3));                      // logical 32-byte piece
@@ -176,10 +176,8 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
       const int s = stl * TS + row;
       const uint32_t piece = (uint32_t)((ln & 3) ^ (int)sw4(row));
       const bool ok = valid && s < a.S;
-      int r, kk0;
-      chunk_block(kc, r, kk0);
       dma16(pr, st + XS + r0 * PB, ok ? (uint32_t)s * (uint32_t)KP * 2u + 16u * piece : OOB,
-            (uint32_t)kk0 * 2u);
+            (uint32_t)(s_col0[r] + j) * 2u);
     }
   };
 
@@ -209,9 +207,9 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
 
-  // One chunk of MFMAs from stage st (weight wt of its block), with the 6 copies of chunk nkc
-  // into stage dst spread between its MFMA groups.
-  auto compute_copy = [&](const uint8_t* st, float wt, int nkc, uint8_t* dst, bool valid) {
+  // One chunk of MFMAs from stage st, with the 6 copies of chunk nkc into stage dst spread
+  // between its MFMA groups.
+  auto compute_copy = [&](const uint8_t* st, int nkc, uint8_t* dst, bool valid) {
     uint4 ra[2][4], rb[2][2];
     auto fetch = [&](int ks) {
 #pragma unroll
@@ -222,8 +220,7 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const uint4 v = lds_read16(st, offB[ks] + nb * 32 * PB);
-        rb[ks][nb] = wt == 1.f ? v : scale8(v, wt);
+        rb[ks][nb] = lds_read16(st, offB[ks] + nb * 32 * PB);
       }
     };
     fetch(0);
@@ -244,17 +241,11 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
       }
     }
   };
-  auto weight = [&](int kc) {
-    int t0;
-    float wt = 1.f;
-    if (kc < nk) chunk_src(kc, t0, wt);
-    return wt;
-  };
   // After chunk c: at the last chunk of a block, multiply the accumulator by the block's factor.
   auto post = [&](int c) {
     if (c >= nk || (c + 1) % cpb) return;
-    int r, kk0;
-    chunk_block(c, r, kk0);
+    int r, j;
+    chunk_block(c, r, j);
     const float f = s_ps[r];
     if (f == 1.f) return;
 #pragma unroll
@@ -268,13 +259,13 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   // Every chunk is exactly 6 copies per wave: WAIT_KEEP(6) leaves the next chunk in flight.
   for (int kc = 0; kc < nk3; kc += 3) {
     WAIT_KEEP(6);
-    compute_copy(st0, weight(kc), kc + 2, st2, kc + 2 < nk);
+    compute_copy(st0, kc + 2, st2, kc + 2 < nk);
     post(kc);
     WAIT_KEEP(6);
-    compute_copy(st1, weight(kc + 1), kc + 3, st0, kc + 3 < nk);
+    compute_copy(st1, kc + 3, st0, kc + 3 < nk);
     post(kc + 1);
     WAIT_KEEP(6);
-    compute_copy(st2, weight(kc + 2), kc + 4, st1, kc + 4 < nk);
+    compute_copy(st2, kc + 4, st1, kc + 4 < nk);
     post(kc + 2);
   }
   wait_vmem();   // the zero-filled copies issued past the last chunk land before the exit
@@ -361,11 +352,13 @@ typedef const __attribute__((address_space(4))) float* sc_f32;
 template <int P>
 using Pos = std::integral_constant<int, P>;
 
+// CPB: chunks per block (S / 32) as a compile-time constant, or 0 for any S.
+template <int CPB>
 __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a) {
   __shared__ __align__(16) uint8_t st0[USTAGE], st1[USTAGE], st2[USTAGE], st3[USTAGE];
   __shared__ int s_tok0[2][MAXBLK];   // per unit (two tables): first token of block r's split
   __shared__ float s_wt[2][MAXBLK];   // weight of block r
-  __shared__ int s_slow[2][8];        // per wave: a weight outside [2^-60, 2^60]
+  __shared__ int s_col0[2][MAXBLK];   // first column of P that multiplies block r
   __shared__ float s_bias[512];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -380,7 +373,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   if (t >= cnt) return;
 
   const int KP = (a.k + 1) * a.S;
-  const int cpb = a.S / KH;               // chunks per block
+  const int cpb = CPB ? CPB : a.S / KH;   // chunks per block
   const int nk = KP / KH;
   const int nk4 = (nk + 3) / 4 * 4;       // padded with zero chunks: every unit starts on stage 0
   // floor(c / cpb) as (c * cpb_magic) >> 20: exact while c * (cpb_magic * cpb - 2^20) < 2^20,
@@ -400,52 +393,65 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     u.f_base = ft * TF;
     return u;
   };
+  // Block table of a unit: slot 0 is the split's own block (weight 1), the retrieved blocks
+  // follow in block_key order, so that every factor w_r / w_(r+1) the accumulator is multiplied
+  // by lies in [-1, 1].
   auto fill_table = [&](const UnitPos& u, int bf) {
     const int64_t row = (u.b * a.n_s + u.i) * (int64_t)a.k;
-    int slow = 0;
     for (int r = wave; r <= a.k; r += 8) {
-      int src = u.i;
-      float wr = 1.f;
-      if (r) {
-        src = ((sc_i32)a.idx)[row + r - 1];
-        if (src >= 0) wr = ((sc_f32)a.w)[row + r - 1];
+      if (r == 0) {
+        s_tok0[bf][0] = u.i * a.S;
+        s_wt[bf][0] = 1.f;
+        s_col0[bf][0] = 0;
+        continue;
       }
-      // a negative index is an empty block: its copies load zeros, its weight is taken as 1
-      s_tok0[bf][r] = src < 0 ? kEmptyBlock : min(src, a.n_s - 1) * a.S;
-      s_wt[bf][r] = wr;
-      if (!(wr >= 0x1p-60f && wr <= 0x1p60f)) slow = 1;   // also catches NaN
+      const int src = ((sc_i32)a.idx)[row + r - 1];
+      const float wr = ((sc_f32)a.w)[row + r - 1];
+      const uint32_t key = block_key(src, wr);
+      int pos = 1;   // 1 + the number of retrieved blocks ordered before this one
+      for (int j = 1; j <= a.k; ++j) {
+        const uint32_t kj = block_key(((sc_i32)a.idx)[row + j - 1], ((sc_f32)a.w)[row + j - 1]);
+        pos += (kj < key || (kj == key && j < r)) ? 1 : 0;
+      }
+      const bool none = key == kKeyNone;
+      s_tok0[bf][pos] = none ? kEmptyBlock : min(src, a.n_s - 1) * a.S;
+      s_wt[bf][pos] = none ? 1.f : wr;
+      s_col0[bf][pos] = r * a.S;   // P keeps the rank order of the selection
     }
-    s_slow[bf][wave] = slow;
   };
   s_bias[tid] = (a.epi.bias && tid < a.S) ? a.epi.bias[tid] : 0.f;
 
   // ---- copy side: the unit whose chunks are being copied (the next one near a unit's end)
   __amdgpu_buffer_rsrc_t xr;
   int c_su = 0, c_fb = 0;
-  int vtok = 0;   // lane r: first token of block r of the copy unit (the launcher ensures k + 1 <= 64)
+  // lane r: first token of block r of the copy unit, and its first column of P (the launcher
+  // ensures k + 1 <= 64)
+  int vtok = 0, vcol = 0;
   auto set_copy_unit = [&](const UnitPos& u, int bf) {
     xr = make_rsrc(a.x + u.b * a.N * a.ld_x, (uint32_t)(a.N * a.ld_x * 2));
     c_su = u.su;
     c_fb = u.f_base;
     vtok = lane <= a.k ? s_tok0[bf][lane] : 0;
+    vcol = lane <= a.k ? s_col0[bf][lane] : 0;
   };
   // Chunk c covers block (c / cpb + 1) mod (k + 1): blocks 1..k, then block 0.
   auto chunk_block = [&](int c, int& r, int& j) {
-    const int q = (int)(((uint32_t)c * cpb_magic) >> 20);
+    const int q = CPB ? c / CPB : (int)(((uint32_t)c * cpb_magic) >> 20);
     r = q < a.k ? q + 1 : 0;
     j = c - q * cpb;
   };
-  // one lane read per chunk instead of an LDS load, whose wait would also drain the fragment reads
-  auto chunk_tok0 = [&](int kc) {
+  // First token (x) and first column of P (y) of chunk kc: lane reads instead of LDS loads, whose
+  // wait would also drain the fragment reads.
+  auto chunk_src = [&](int kc) {
     int r, j;
     chunk_block(kc, r, j);
-    return __builtin_amdgcn_readlane(vtok, r) + j * KH;
+    return make_int2(__builtin_amdgcn_readlane(vtok, r) + j * KH, __builtin_amdgcn_readlane(vcol, r) + j * KH);
   };
   // Copy n of chunk kc into stage st: n = 0, 1 are X rows 4 w + 2 n, + 1 (1 KiB), n = 2, 3 are
   // P rows 32 w + 16 (n - 2) .. + 15. Tokens past N, features past d and rows past S load zeros:
   // their offset gets the high bit, past the descriptor's range (a sequence and P are < 2^31
   // bytes), so that the offsets are plain 32-bit arithmetic without a branch.
-  auto copy = [&](int kc, uint8_t* st, bool valid, int n, int tok0) {
+  auto copy = [&](uint8_t* st, bool valid, int n, int2 src) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     if (n < 2) {
@@ -453,7 +459,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       const int p = ln & 31;
       const int c = (p >> 1) ^ (2 * (tr & 3));
       const int fl = c * 16 + (p & 1) * 8;                 // feature within the tile
-      const uint32_t tok = (uint32_t)(tok0 + tr);          // an empty block's tokens wrap above N
+      const uint32_t tok = (uint32_t)(src.x + tr);         // an empty block's tokens wrap above N
       const bool ok = valid & (tok < (uint32_t)a.N) & (fl < a.d - c_fb);
       const uint32_t off = (tok * (uint32_t)a.ld_x + (uint32_t)(c_fb + fl)) * 2u;
       dma16(xr, st + (wave * 4 + n * 2) * XB, off | ((uint32_t)!ok << 31), 0);
@@ -462,18 +468,15 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       const int row = r0 + (ln >> 2);
       const int s = c_su * TU + row;
       const uint32_t piece = (uint32_t)((ln & 3) ^ (int)sw4(row));
-      int r, j;
-      chunk_block(kc, r, j);
-      const int kk0 = r * a.S + j * KH;
       const bool ok = valid & (s < a.S);
       dma16(pr, st + XS + r0 * PB, ((uint32_t)s * (uint32_t)KP * 2u + 16u * piece) | ((uint32_t)!ok << 31),
-            (uint32_t)kk0 * 2u);
+            (uint32_t)src.y * 2u);
     }
   };
   auto dma = [&](int kc, uint8_t* st, bool valid) {
-    const int tok0 = chunk_tok0(kc);
+    const int2 src = chunk_src(kc);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) copy(kc, st, valid, n, tok0);
+    for (int n = 0; n < 4; ++n) copy(st, valid, n, src);
   };
 
   // ---- fragments (transpose reads of X for A, P rows for B), feature blocks 64 mb + 32 wm
@@ -492,7 +495,6 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     offB[ks] = (uint32_t)XS + (uint32_t)rb * PB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(rb)) << 4);
   }
   int bf = 0, cur_su = 0;
-  bool slow = false;
   int rc0 = -1, rc1 = -1;   // the chunks of the current unit that add the residual (token blocks 0, 1)
   f32x16 acc[4][2];
   uint4 ra0[4], rb0[2], ra1[4], rb1[2];
@@ -504,25 +506,16 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       ra[mb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
-  auto fetchB = [&](const uint8_t* st, int ks, float wt, uint4 (&rb)[2]) {
+  auto fetchB = [&](const uint8_t* st, int ks, uint4 (&rb)[2]) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint4 v = lds_read16(st, offB[ks] + nb * 32 * PB);
-      rb[nb] = slow ? scale8(v, wt) : v;
-    }
+    for (int nb = 0; nb < 2; ++nb) rb[nb] = lds_read16(st, offB[ks] + nb * 32 * PB);
   };
 
   // ---- compute side: the unit being multiplied
-  auto wt_of = [&](int c) {   // weight applied to chunk c's P fragments (slow path only)
-    if (!slow || c >= nk) return 1.f;
-    int r, j;
-    chunk_block(c, r, j);
-    return s_wt[bf][r];
-  };
   // After chunk c: at the last chunk of a retrieved block r, multiply the accumulator by
   // w_r / w_{r+1} (by w_k after block k).
   auto post = [&](int c) {
-    if (slow || c >= nk) return;
+    if (c >= nk) return;
     int r, j;
     chunk_block(c, r, j);
     if (j != cpb - 1 || r == 0) return;
@@ -567,8 +560,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   // inline constant) instead of reading them, so that nothing has to clear them.
   auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
                           const uint8_t* next) {
-    const int tok0 = chunk_tok0(kc);
-    const float wt = wt_of(c);
+    const int2 src = chunk_src(kc);
     const bool ron = (c == rc0) | (c == rc1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -576,35 +568,34 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
             mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     fetchA(st, 1, ra1);
-    fetchB(st, 1, wt, rb1);
-    copy(kc, dst, valid, 0, tok0);
+    fetchB(st, 1, rb1);
+    copy(dst, valid, 0, src);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
             mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
-    copy(kc, dst, valid, 1, tok0);
+    copy(dst, valid, 1, src);
     __builtin_amdgcn_sched_barrier(0);
     res_mfma(POS, ron, ra0, 0);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
-    copy(kc, dst, valid, 2, tok0);
+    copy(dst, valid, 2, src);
     __builtin_amdgcn_sched_barrier(0);
     if (next) {
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
       WAIT_KEEP(7);
-      const float wnx = wt_of(c + 1);
       fetchA(next, 0, ra0);
-      fetchB(next, 0, wnx, rb0);
+      fetchB(next, 0, rb0);
     }
 #pragma unroll
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
-    copy(kc, dst, valid, 3, tok0);
+    copy(dst, valid, 3, src);
     __builtin_amdgcn_sched_barrier(0);
     res_mfma(POS, ron, ra1, 1);
     post(c);
@@ -642,14 +633,8 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     // epilogue stores of the previous unit are older and only make the wait stricter).
     WAIT_KEEP(8);
     if (has_next) fill_table(nx, bf ^ 1);   // its readers come after later barriers
-    {
-      int sl = 0;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) sl |= s_slow[bf][w];
-      slow = sl != 0;
-    }
     fetchA(st0, 0, ra0);
-    fetchB(st0, 0, wt_of(0), rb0);
+    fetchB(st0, 0, rb0);
     if (nk4 > 4) {
       compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1);
       compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2);
@@ -742,7 +727,13 @@ hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, 
   if (units >= cus && k + 1 <= unit::kMaxBlocks) {
     p.s_tiles = (S + unit::TU - 1) / unit::TU;
     p.tiles = units;
-    hipLaunchKernelGGL(unit::compress_unit_kernel, dim3((unsigned)cus), dim3(512), 0, stream, p);
+    // chunks per block as a constant for the common split lengths
+    if (S == 256)
+      hipLaunchKernelGGL(unit::compress_unit_kernel<8>, dim3((unsigned)cus), dim3(512), 0, stream, p);
+    else if (S == 512)
+      hipLaunchKernelGGL(unit::compress_unit_kernel<16>, dim3((unsigned)cus), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL(unit::compress_unit_kernel<0>, dim3((unsigned)cus), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
   p.tiles = B * p.n_s * p.s_tiles * p.f_tiles;

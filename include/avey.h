@@ -174,8 +174,9 @@ avey_status avey_split_rank_preceding(const void* x, avey_dtype dt, int64_t B, i
  *   residual 0 or 1
  *   xhat     [B, N, d] row stride ld_out, dtype dt (output)
  * Requires k >= 1 (and k + 1 <= 512 for AVEY_BF16). For AVEY_BF16 the weights scale the fp32
- * accumulator between blocks when every weight is a positive normal number in [2^-60, 2^60];
- * otherwise block r's rows of P are multiplied by w_r and rounded to bf16 as they are read.
+ * accumulator between blocks, the retrieved blocks taken in ascending order of |w|; any finite
+ * weight is accepted (negative, zero, above 1). A block whose |w| is below 2^-149 times the next
+ * larger one's may be dropped. A NaN or infinite weight makes that split's outputs non-finite.
  * The result is rounded to bf16.
  */
 avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,

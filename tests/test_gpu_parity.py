@@ -204,10 +204,36 @@ def test_prepare_normalises_and_pads(gpu_ok, dtype):
         assert np.all(np.abs(got[b, : cfg.N] - ref) <= rel * np.abs(ref) + 1e-7)
 
 
-@pytest.mark.parametrize("weights", ["positive", "zero_and_negative"])
+def edge_weights(w, nan_split):
+    """Caller-given weights the ranker does not produce but the call accepts: all negative in
+    one split, |w| over 50 decades in another, and a NaN at nan_split (that split's outputs must
+    be non-finite, as w X is)."""
+    B, n_s, k = w.shape
+    w[0, 3, :] = -w[0, 3, :]
+    w[B - 1, 2, 0] = 1e-30
+    w[B - 1, 2, 1:] *= 1e20
+    w[nan_split] = np.nan
+    return w
+
+
+def compare_splits(got, ref, N, S, nan_split=None):
+    worst = 0.0
+    for (b, i), rows in ref.items():
+        g = got[b, split_rows_of(N, S, i)]
+        if (b, i) == nan_split:
+            assert not np.isfinite(g).any(), f"split {(b, i)} with a NaN weight has finite outputs"
+            continue
+        err = row_rel_err(g, rows)
+        assert err <= TOL["bf16"]["out"], f"xhat split {(b, i)}: {err:.3e}"
+        worst = max(worst, err)
+    return worst
+
+
+@pytest.mark.parametrize("weights", ["positive", "zero_and_negative", "edge"])
 def test_compress_given_weights(gpu_ok, weights):
     """select_compress on caller-given idx / w, including a zero and a negative weight (divide-
-    by-max of non-positive scores, read as written) and weights above 1."""
+    by-max of non-positive scores, read as written), weights above 1, and (edge) all-negative,
+    widely spread and NaN weights."""
     cfg = SMALL["small_bf16"]
     inp = make_inputs(cfg)
     say(f"select_compress given weights ({weights})")
@@ -219,15 +245,14 @@ def test_compress_given_weights(gpu_ok, weights):
     if weights == "zero_and_negative":
         w[0, 1, 1] = 0.0
         w[1, 2, 0] = -0.75
+    nan_split = (0, 5, 1) if weights == "edge" else None
+    if nan_split:
+        w = edge_weights(w, nan_split)
     g = A.avey_select_compress(x, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), P, cfg.S)
     torch.cuda.synchronize()
     got = host_f64(g)
     ref = O.select_compress(inp.x_f64(), cfg.S, idx, w.astype(np.float64), inp.P_f64(), residual=True)
-    worst = 0.0
-    for (b, i), rows in ref.items():
-        err = row_rel_err(got[b, split_rows_of(cfg.N, cfg.S, i)], rows)
-        assert err <= TOL["bf16"]["out"], f"xhat split {(b, i)}: {err:.3e}"
-        worst = max(worst, err)
+    worst = compare_splits(got, ref, cfg.N, cfg.S, nan_split[:2] if nan_split else None)
     say(f"given weights ({weights}): worst xhat error {worst:.2e}")
 
 
@@ -330,8 +355,8 @@ PERSISTENT = {
 
 @pytest.mark.parametrize("name", list(PERSISTENT))
 def test_compress_persistent_kernel(gpu_ok, name):
-    """Every split against the oracle on caller-given idx / w, with an empty block (index -1),
-    a zero weight (per-fragment weighting in that unit) and a ragged last split."""
+    """Every split against the oracle on caller-given idx / w in random order of |w|, with an
+    empty block (index -1), a zero weight, the edge weights above and a ragged last split."""
     cfg, residual = PERSISTENT[name]
     inp = make_inputs(cfg)
     say(f"persistent compress {name}: B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S} k={cfg.k} residual={residual}")
@@ -343,14 +368,11 @@ def test_compress_persistent_kernel(gpu_ok, name):
     idx[0, 5, k - 1] = -1
     w[0, 5, k - 1] = 0.0
     w[B - 1, n_s - 1, 0] = 0.0
+    w = edge_weights(w, (0, 11, k - 1))
     g = A.avey_select_compress(x, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), P, cfg.S,
                                residual=residual)
     torch.cuda.synchronize()
     got = host_f64(g)
     ref = O.select_compress(inp.x_f64(), cfg.S, idx, w.astype(np.float64), inp.P_f64(), residual=residual)
-    worst = 0.0
-    for (b, i), rows in ref.items():
-        err = row_rel_err(got[b, split_rows_of(cfg.N, cfg.S, i)], rows)
-        assert err <= TOL["bf16"]["out"], f"xhat split {(b, i)}: {err:.3e}"
-        worst = max(worst, err)
+    worst = compare_splits(got, ref, cfg.N, cfg.S, (0, 11))
     say(f"persistent compress {name}: worst xhat error {worst:.2e}")
