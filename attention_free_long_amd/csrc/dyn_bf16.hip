@@ -10,14 +10,12 @@
 //     is exactly the B-operand layout the second GEMM needs along its K = q axis (up to a
 //     fixed permutation of q inside each 16-row group, applied identically to both operands).
 //     Token norms come from LDS fragments the waves read anyway where possible.
-//  2. O[f][p] = sum_q Z^T[f][q] G[q][p]: Z^T tiles (128 features x 64 tokens) are staged
-//     feature-major through a register transpose that also applies the q permutation; the
-//     result lane owns token p and four consecutive features (8-byte stores), scaled by
-//     1 / (r_p + eps). G is rounded to bf16 for this product and r_p is summed from the
-//     rounded values, so the applied weights sum to r_p / (r_p + eps).
-//
-// Template: NQB = q blocks of 32 covering the split (8 for S <= 256, 16 for S <= 512); NPB = p
-// blocks per wave (2 or 1), so one workgroup covers 4 * NPB * 32 tokens p.
+//  2. O^T[f][p] = sum_q Z^T[f][q] G[q][p]: Z^T is read from LDS tiles of [64 q][256 f] by the
+//     LDS transpose read, in the same q order; each result lane owns token p and four
+//     consecutive features, scaled by 1 / (r_p + eps). G is rounded to bf16 for this product
+//     and r_p is summed from the rounded values, so the applied weights sum to r_p / (r_p + eps).
+// Two kernels below: one 8-wave workgroup per split for S <= 256, four 4-wave workgroups per
+// split (128 tokens p each) for S <= 512.
 #include "avey_common.h"
 #include "launch.h"
 
@@ -74,265 +72,6 @@ __device__ __forceinline__ float layer_out(float v, float scale, float bv, bool 
   const float y = fmaf(v, scale, bv);
   return relu ? fmaxf(y, 0.f) : y;
 }
-
-template <int NQB, int NPB>
-__global__ void __launch_bounds__(256, 1) dyn_bf16_kernel(DynParams a) {
-  constexpr int QROWS = NQB * 32;
-  constexpr int PWG = 4 * NPB * 32;
-  constexpr int LROWS = QROWS / 4;       // Z rows copied per wave in GEMM 1
-  constexpr int LN = LROWS / 8;          // copy instructions per wave per chunk
-  // Norms of the q rows: when this workgroup's p rows are all the split's rows, each wave sums
-  // its own p fragments; otherwise every wave also reads the fragments of 128 q rows of its own.
-  constexpr bool kNormFromP = (PWG == QROWS);
-  constexpr int NNB = kNormFromP ? NPB : 4;   // norm fragments per k-step
-  __shared__ __align__(16) uint8_t sZ0[QROWS * ROWB], sZ1[QROWS * ROWB];
-  __shared__ float s_sq[QROWS];
-  __shared__ __align__(16) float s_rn[QROWS];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-
-  const int64_t L = xcd_remap(blockIdx.x, a.tiles);
-  const int pg = (int)(L % a.pgroups);
-  const int64_t split = L / a.pgroups;
-  const int64_t b = split / a.n_s;
-  const int i = (int)(split % a.n_s);
-  const int64_t base = (int64_t)i * a.S;
-  const int nvalid = (int)min((int64_t)a.S, a.N - base);   // valid tokens of the split
-  const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
-  const int nk = a.m_t / KC;
-
-  // ------------------------------------------------------------------ GEMM 1
-  const int ld_sub = lane >> 3, ld_pos = lane & 7;
-  uint32_t offZ[LN];
-#pragma unroll
-  for (int n = 0; n < LN; ++n) {
-    const int row = wave * LROWS + n * 8 + ld_sub;
-    const uint32_t c = (uint32_t)(ld_pos ^ (int)swz<SWZ_ROW>(row));
-    const bool v = row < a.S && base + row < a.N;
-    offZ[n] = v ? (uint32_t)((base + row) * a.ld_z * 2) + 16u * c : OOB;
-  }
-  const int prow0 = pg * PWG + wave * NPB * 32;   // this wave's first p (split-local)
-  const int nrow0 = kNormFromP ? prow0 : wave * 128;
-  const bool relu = a.epi.act != 0;
-  float bv[NPB];
-#pragma unroll
-  for (int nb = 0; nb < NPB; ++nb) {
-    const int p = prow0 + nb * 32 + (lane & 31);
-    bv[nb] = layer_bias(a.epi, p, p < a.S && base + p < a.N);
-  }
-  uint32_t fq[4], fp[4], fn[4];
-  frag_offsets<SWZ_ROW>(fq, 0, lane);
-  frag_offsets<SWZ_ROW>(fp, prow0, lane);
-  frag_offsets<SWZ_ROW>(fn, nrow0, lane);
-
-  f32x16 acc1[NQB][NPB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-    for (int nb = 0; nb < NPB; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc1[qb][nb][v] = 0.f;
-  float sq[NNB];
-#pragma unroll
-  for (int j = 0; j < NNB; ++j) sq[j] = 0.f;
-
-  auto dma1 = [&](int kc, uint8_t* dst) {
-#pragma unroll
-    for (int n = 0; n < LN; ++n) dma16(zr, dst + (wave * LROWS + n * 8) * ROWB, offZ[n], (uint32_t)kc * KC * 2);
-  };
-  auto compute1 = [&](const uint8_t* s) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 rb[NPB];
-#pragma unroll
-      for (int nb = 0; nb < NPB; ++nb) rb[nb] = lds_read16(s, fp[ks] + nb * 32 * ROWB);
-      if constexpr (kNormFromP) {
-#pragma unroll
-        for (int nb = 0; nb < NPB; ++nb) sq[nb] = sumsq8(rb[nb], sq[nb]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NNB; ++j) sq[j] = sumsq8(lds_read16(s, fn[ks] + j * 32 * ROWB), sq[j]);
-      }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const uint4 ra = lds_read16(s, fq[ks] + qb * 32 * ROWB);
-#pragma unroll
-        for (int nb = 0; nb < NPB; ++nb) acc1[qb][nb] = mfma32(as_bf16x8(ra), as_bf16x8(rb[nb]), acc1[qb][nb]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  dma1(0, sZ0);
-  wait_vmem();
-  __syncthreads();
-  int kc = 0;
-  for (; kc + 2 <= nk; kc += 2) {
-    dma1(kc + 1, sZ1);
-    compute1(sZ0);
-    wait_vmem();
-    __syncthreads();
-    if (kc + 2 < nk) dma1(kc + 2, sZ0);
-    compute1(sZ1);
-    wait_vmem();
-    __syncthreads();
-  }
-  if (kc < nk) {
-    compute1(sZ0);
-    __syncthreads();
-  }
-
-  // token norms (lane halves hold the two k-halves)
-#pragma unroll
-  for (int j = 0; j < NNB; ++j) {
-    const float t = sq[j] + __shfl_xor(sq[j], 32);
-    if (lane < 32) s_sq[nrow0 + j * 32 + lane] = t;
-  }
-  __syncthreads();
-  for (int q = tid; q < QROWS; q += 256) {
-    const float ss = s_sq[q];
-    const bool v = q < a.S && base + q < a.N;
-    s_rn[q] = (v && ss > 0.f) ? 1.0f / sqrtf(ss) : 0.f;
-  }
-  __syncthreads();
-
-  // G (bf16) as GEMM-2 B fragments, and r_p from the rounded values
-  uint4 gfrag[NQB][2][NPB];
-  float inv[NPB];
-#pragma unroll
-  for (int nb = 0; nb < NPB; ++nb) {
-    const float rnp = s_rn[prow0 + nb * 32 + (lane & 31)];
-    float r = 0.f;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int q0 = qb * 32 + s2 * 16 + h * 8 + (lane >> 5) * 4;   // rows of v = 8*s2 + 4*h + 0..3
-          const float4 rq = *reinterpret_cast<const float4*>(&s_rn[q0]);
-          const int v0 = s2 * 8 + h * 4;
-          g_weights(acc1[qb][nb][v0 + 0] * rq.x * rnp, acc1[qb][nb][v0 + 1] * rq.y * rnp,
-                    acc1[qb][nb][v0 + 2] * rq.z * rnp, acc1[qb][nb][v0 + 3] * rq.w * rnp, q0, nvalid, a.epi.norm,
-                    pk[2 * h + 0], pk[2 * h + 1], r);
-        }
-        gfrag[qb][s2][nb] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      }
-    }
-    r += __shfl_xor(r, 32);
-    inv[nb] = row_scale(a.epi.norm, r, a.eps, nvalid);
-  }
-
-  // ------------------------------------------------------------------ GEMM 2
-  constexpr int FT = 128;                 // features per output tile
-  constexpr int NQC = QROWS / KC;         // 64-token chunks along K = q
-  const int nft = (a.m_t + FT - 1) / FT;
-  const int total = nft * NQC;
-  // staging role: 4 features x 8 tokens; the 8 tokens are the ones a lane half feeds to
-  // one k-step: 16g + 4h + {0..3} and 16g + 8 + 4h + {0..3} (g = tg >> 1, h = tg & 1)
-  const int fg = tid & 31, tg = tid >> 5;
-  const int qoff = 16 * (tg >> 1) + 4 * (tg & 1);
-  uint32_t fz[4];
-  frag_offsets<SWZ_DIAG>(fz, 0, lane);
-  uint2 st2[8];
-  auto gload2 = [&](int c) {
-    const int ft = c / NQC, qc = c % NQC;
-    const int f0 = ft * FT + fg * 4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int q = qc * KC + qoff + (e & 3) + ((e >> 2) << 3);
-      const bool v = f0 < a.m_t && q < a.S && base + q < a.N;
-      st2[e] = buf_load8(zr, v ? (uint32_t)(((base + q) * a.ld_z + f0) * 2) : OOB, 0);
-    }
-  };
-  auto put2 = [&](uint8_t* dst) {
-#pragma unroll
-    for (int ff = 0; ff < 4; ++ff) {
-      uint32_t o[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t lo = (ff >> 1) ? st2[2 * m].y : st2[2 * m].x;
-        const uint32_t hi = (ff >> 1) ? st2[2 * m + 1].y : st2[2 * m + 1].x;
-        o[m] = pick16(lo, hi, ff & 1);
-      }
-      lds_write16(dst, lds_off<SWZ_DIAG>(fg * 4 + ff, tg), make_uint4(o[0], o[1], o[2], o[3]));
-    }
-  };
-
-  f32x16 acc2[4][NPB];
-  auto zero2 = [&]() {
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-      for (int nb = 0; nb < NPB; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc2[fb][nb][v] = 0.f;
-  };
-  zero2();
-  auto compute2 = [&](const uint8_t* s, auto qc_tag) {
-    constexpr int qc = decltype(qc_tag)::value;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 ra[4];
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb) ra[fb] = lds_read16(s, fz[frag_ks<SWZ_DIAG>(ks, fb)] + fb * 32 * ROWB);
-      const int qb = qc * 2 + (ks >> 1);
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int nb = 0; nb < NPB; ++nb)
-          acc2[fb][nb] = mfma32(as_bf16x8(ra[fb]), as_bf16x8(gfrag[qb][ks & 1][nb]), acc2[fb][nb]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  uint16_t* ob = a.out + b * a.N * a.ld_out;
-  auto epilogue = [&](int ft) {
-#pragma unroll
-    for (int nb = 0; nb < NPB; ++nb) {
-      const int p = prow0 + nb * 32 + (lane & 31);
-      const int64_t tok = base + p;
-      if (p >= a.S || tok >= a.N) continue;
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = ft * FT + fb * 32 + g * 8 + (lane >> 5) * 4;
-          if (f >= a.m_t) continue;
-          const float sc = inv[nb], bb = bv[nb];
-          const uint32_t lo = pack_bf16(layer_out(acc2[fb][nb][g * 4 + 0], sc, bb, relu),
-                                        layer_out(acc2[fb][nb][g * 4 + 1], sc, bb, relu));
-          const uint32_t hi = pack_bf16(layer_out(acc2[fb][nb][g * 4 + 2], sc, bb, relu),
-                                        layer_out(acc2[fb][nb][g * 4 + 3], sc, bb, relu));
-          *reinterpret_cast<uint2*>(ob + tok * a.ld_out + f) = make_uint2(lo, hi);
-        }
-    }
-  };
-
-  // Chunk c = ft * NQC + qc; NQC is even, so chunk parity = qc parity and the stage buffer of
-  // every chunk is known at compile time.
-  static_assert(NQC % 2 == 0, "q chunks per feature tile must be even");
-  gload2(0);
-  put2(sZ0);
-  __syncthreads();
-  if (total > 1) gload2(1);
-  for (int ft = 0; ft < nft; ++ft) {
-    static_for<NQC>([&](auto qc_tag) {
-      constexpr int qc = decltype(qc_tag)::value;
-      const int c = ft * NQC + qc;
-      compute2(qc % 2 == 0 ? sZ0 : sZ1, qc_tag);
-      if (c + 1 < total) {
-        put2(qc % 2 == 0 ? sZ1 : sZ0);
-        if (c + 2 < total) gload2(c + 2);
-      }
-      __syncthreads();
-    });
-    epilogue(ft);
-    zero2();
-  }
-}
-
 
 // ---------------------------------------------------------------------------------------------
 // S <= 256: one 8-wave workgroup per split, both GEMMs fed by one 4-stage ring of 32 KiB
@@ -587,16 +326,279 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   wait_vmem();   // the zero-filled copies issued past the last chunk land before the exit
 }
 
-}  // namespace ring
+// ---------------------------------------------------------------------------------------------
+// 256 < S <= 512: a split's G row block for 128 tokens p, over all 512 q, fills the register
+// file of a wave per 32 p (16 accumulator blocks), so a workgroup of 4 waves (one per SIMD)
+// takes 128 p and a split takes 4 workgroups, each reading the whole split.
+//   Phase 1, chunk kc: Z rows q = 0..511 x features 64 kc .. +63, as two halves of 256 rows in
+//   separate LDS objects (two stages of 64 KiB, one chunk in flight).
+//   Phase 2: the 4-stage ring of the S <= 256 kernel, chunk (ft, qc) = Z rows 64 qc .. +63 x
+//   features 256 ft .. +255 (8 chunks per feature tile, 8 copies per wave per chunk), read as
+//   Z^T fragments by the LDS transpose read against the G fragments the wave holds.
+constexpr int QR5 = 512;
+constexpr int HALF = 256 * ROWB;        // 32 KiB: 256 rows of a phase-1 chunk, or a phase-2 stage
 
-template <int NQB, int NPB>
-hipError_t launch_dyn_t(DynParams p, hipStream_t stream) {
-  constexpr int PWG = 4 * NPB * 32;
-  p.pgroups = (p.S + PWG - 1) / PWG;
-  p.tiles = (int64_t)p.pgroups * p.tiles;   // tiles held B * n_s on entry
-  hipLaunchKernelGGL((dyn_bf16_kernel<NQB, NPB>), dim3((unsigned)p.tiles), dim3(256), 0, stream, p);
-  return hipGetLastError();
+__global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
+  __shared__ __align__(16) uint8_t st0[HALF], st1[HALF], st2[HALF], st3[HALF];
+  __shared__ float s_sq[QR5];
+  __shared__ __align__(16) float s_rn[QR5];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+
+  const int64_t L = xcd_remap(blockIdx.x, a.tiles);
+  const int pg = (int)(L % a.pgroups);
+  const int64_t split = L / a.pgroups;
+  const int64_t b = split / a.n_s;
+  const int i = (int)(split % a.n_s);
+  const int64_t base = (int64_t)i * a.S;
+  const int nvalid = (int)min((int64_t)a.S, a.N - base);   // valid tokens of the split
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
+  const int nk = a.m_t / KC;
+
+  // ---- phase 1: C1[q][p] for all 512 q and this wave's 32 p. Wave w copies rows 64 w .. +63 of
+  // each half of a chunk (8 copies of 8 rows per half), so that every copy has a fixed LDS
+  // object as its destination (with a selected one, the compiler would wait for the copies in
+  // flight before reading either half).
+  const int prow0 = pg * 128 + wave * 32;          // this wave's first p (split-local)
+  const int p = prow0 + (lane & 31);               // this lane's output token
+  const bool relu = a.epi.act != 0;
+  const float bv = layer_bias(a.epi, p, p < nvalid);
+  uint32_t offZ[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const int row = (n >> 3) * 256 + wave * 64 + (n & 7) * 8 + (lane >> 3);
+    const uint32_t c = (uint32_t)((lane & 7) ^ (int)swz<SWZ_ROW>(row));
+    offZ[n] = row < nvalid ? (uint32_t)((base + row) * a.ld_z * 2) + 16u * c : OOB;
+  }
+  // fragment offsets within a 256-row half (the swizzle repeats every 16 rows)
+  uint32_t fq[4], fp[4], fn[4];
+  frag_offsets<SWZ_ROW>(fq, 0, lane);
+  frag_offsets<SWZ_ROW>(fp, prow0 & 255, lane);
+  frag_offsets<SWZ_ROW>(fn, wave * 64, lane);
+  const bool p_hi = prow0 >= 256;
+
+  f32x16 acc1[16];
+#pragma unroll
+  for (int qb = 0; qb < 16; ++qb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc1[qb][v] = 0.f;
+  // squared norms (k-halves) of rows 256 (j >> 1) + 64 w + 32 (j & 1) + (l & 31)
+  float sq[4] = {0.f, 0.f, 0.f, 0.f};
+
+  auto dma1 = [&](int kc, uint8_t* lo, uint8_t* hi) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) dma16(zr, lo + (wave * 64 + n * 8) * ROWB, offZ[n], (uint32_t)kc * KC * 2);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) dma16(zr, hi + (wave * 64 + n * 8) * ROWB, offZ[8 + n], (uint32_t)kc * KC * 2);
+  };
+  // Every LDS read names its object (a read through a selected pointer would also wait for
+  // the copies in flight): the p fragment is read from both halves and selected. The next
+  // k-step's fragments are read before this one's MFMAs.
+  struct Frags1 {
+    uint4 q[16], p;
+  };
+  auto fetch1 = [&](const uint8_t* lo, const uint8_t* hi, int ks, Frags1& f) {
+    const uint4 rlo = lds_read16(lo, fp[ks]), rhi = lds_read16(hi, fp[ks]);
+    f.p = p_hi ? rhi : rlo;
+#pragma unroll
+    for (int qb = 0; qb < 16; ++qb) f.q[qb] = lds_read16(qb < 8 ? lo : hi, fq[ks] + (qb & 7) * 32 * ROWB);
+  };
+  auto compute1 = [&](const uint8_t* lo, const uint8_t* hi) {
+    Frags1 f0, f1;
+    fetch1(lo, hi, 0, f0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      Frags1& cur = (ks & 1) ? f1 : f0;
+      Frags1& nxt = (ks & 1) ? f0 : f1;
+      if (ks < 3) fetch1(lo, hi, ks + 1, nxt);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sq[j] = sumsq8(lds_read16(j < 2 ? lo : hi, fn[ks] + (j & 1) * 32 * ROWB), sq[j]);
+#pragma unroll
+      for (int qb = 0; qb < 16; ++qb) acc1[qb] = mfma32(as_bf16x8(cur.q[qb]), as_bf16x8(cur.p), acc1[qb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  dma1(0, st0, st1);
+  wait_vmem();
+  __syncthreads();
+  int kc = 0;
+  for (; kc + 2 <= nk; kc += 2) {
+    dma1(kc + 1, st2, st3);
+    compute1(st0, st1);
+    wait_vmem();
+    __syncthreads();
+    if (kc + 2 < nk) dma1(kc + 2, st0, st1);
+    compute1(st2, st3);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (kc < nk) {
+    compute1(st0, st1);
+    __syncthreads();
+  }
+
+  // ---- norms, G (bf16) as phase-2 B fragments, r_p from the rounded values
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float t = sq[j] + __shfl_xor(sq[j], 32);   // the two lane halves hold the two k-halves
+    if (lane < 32) s_sq[(j >> 1) * 256 + wave * 64 + (j & 1) * 32 + lane] = t;
+  }
+  __syncthreads();
+  for (int q = tid; q < QR5; q += 256) {
+    const float ss = s_sq[q];
+    s_rn[q] = (q < nvalid && ss > 0.f) ? 1.0f / sqrtf(ss) : 0.f;
+  }
+  __syncthreads();
+  uint4 gfrag[16][2];
+  float inv;
+  {
+    const float rnp = s_rn[p];
+    float r = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < 16; ++qb) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int q0 = qb * 32 + s2 * 16 + h * 8 + (lane >> 5) * 4;   // rows of v = 8 s2 + 4 h + 0..3
+          const float4 rq = *reinterpret_cast<const float4*>(&s_rn[q0]);
+          const int v0 = s2 * 8 + h * 4;
+          g_weights(acc1[qb][v0 + 0] * rq.x * rnp, acc1[qb][v0 + 1] * rq.y * rnp, acc1[qb][v0 + 2] * rq.z * rnp,
+                    acc1[qb][v0 + 3] * rq.w * rnp, q0, nvalid, a.epi.norm, pk[2 * h + 0], pk[2 * h + 1], r);
+        }
+        gfrag[qb][s2] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
+    }
+    r += __shfl_xor(r, 32);
+    inv = row_scale(a.epi.norm, r, a.eps, nvalid);
+  }
+
+  // ---- phase 2
+  const int nft = (a.m_t + FT - 1) / FT;
+  const int total = 8 * nft;
+  // copy n (0..7) of chunk c2 into stage st: rows 16 w + 2 n, + 1 (512 bytes each); 32-byte
+  // piece (p >> 1) ^ 2 (t & 3) of row t
+  auto copy2 = [&](int c2, uint8_t* st, int n) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int ft = c2 >> 3, qc = c2 & 7;
+    const int t = wave * 16 + n * 2 + (ln >> 5);
+    const int q = qc * 64 + t;
+    const int pp = ln & 31;
+    const int pc = (pp >> 1) ^ (2 * (t & 3));
+    const int f = ft * FT + pc * 16 + (pp & 1) * 8;
+    const bool ok = c2 < total && q < nvalid && f < a.m_t;
+    dma16(zr, st + (wave * 16 + n * 2) * ZB, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
+  };
+  uint32_t offZ2[8];
+  {
+    const int s2x = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
+    const uint32_t row = (uint32_t)(4 * (lane >> 5) + ((lane & 15) >> 2)) * ZB;
+#pragma unroll
+    for (int fb = 0; fb < 8; ++fb)
+      offZ2[fb] = row + (uint32_t)(((2 * fb + g1) ^ (2 * s2x)) << 5) + 8u * (lane & 3);
+  }
+  f32x16 acc2[8];
+  const f32x16 zero16 = {};
+  // Z^T fragments of k-step ks (q = 32 (ks >> 1) + 16 (ks & 1) + the G fragment's order)
+  auto fetch2 = [&](const uint8_t* st, int ks, uint4 (&ra)[8]) {
+    const uint32_t tok = (uint32_t)(32 * (ks >> 1) + 16 * (ks & 1)) * ZB;
+#pragma unroll
+    for (int fb = 0; fb < 8; ++fb) {
+      const uint2 lo = lds_read_tr8(st, offZ2[fb] + tok);
+      const uint2 hi = lds_read_tr8(st, offZ2[fb] + tok + 8 * ZB);
+      ra[fb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
+  // Chunk qc of a feature tile from stage st; the 8 copies of chunk cnext go into dst meanwhile.
+  // With one wave per SIMD nothing else hides the fragment reads, so the next k-step's are
+  // issued before this one's MFMAs.
+  auto compute2 = [&](const uint8_t* st, auto qc_tag, int cnext, uint8_t* dst) {
+    constexpr int qc = decltype(qc_tag)::value;
+    uint4 ra0[8], ra1[8];
+    fetch2(st, 0, ra0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 (&cur)[8] = (ks & 1) ? ra1 : ra0;
+      uint4 (&nxt)[8] = (ks & 1) ? ra0 : ra1;
+      if (ks < 3) fetch2(st, ks + 1, nxt);
+      const uint4 gb = gfrag[2 * qc + (ks >> 1)][ks & 1];
+      const bool first = qc == 0 && ks == 0;   // the tile's first k-step starts from zero
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) acc2[fb] = mfma32(as_bf16x8(cur[fb]), as_bf16x8(gb), first ? zero16 : acc2[fb]);
+      copy2(cnext, dst, 2 * ks);
+      copy2(cnext, dst, 2 * ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Epilogue of feature tile ft through stage 3 in four rounds of 64 features ([128 tokens][64
+  // features] bf16, 16-byte piece c of row t at c ^ ((t >> 1) & 7)), stored as whole 128-byte
+  // row pieces by 8 lanes per token.
+  uint16_t* ob = a.out + b * a.N * a.ld_out;
+  const int pl = wave * 32 + (lane & 31);          // this lane's token within the workgroup
+  auto epilogue = [&](int ft) {
+    lds_sync();   // every wave is done reading stage 3
+    const uint32_t rowo = (uint32_t)pl * 128u + 8u * (uint32_t)(lane >> 5);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+      for (int fh = 0; fh < 2; ++fh) {
+        const int fb = 2 * rr + fh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = pack_bf16(layer_out(acc2[fb][g * 4 + 0], inv, bv, relu),
+                                        layer_out(acc2[fb][g * 4 + 1], inv, bv, relu));
+          const uint32_t hi = pack_bf16(layer_out(acc2[fb][g * 4 + 2], inv, bv, relu),
+                                        layer_out(acc2[fb][g * 4 + 3], inv, bv, relu));
+          const uint32_t pc = (uint32_t)(4 * fh + g) ^ (uint32_t)((pl >> 1) & 7);
+          *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(lo, hi);
+        }
+      }
+      lds_sync();
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int t = wave * 32 + it * 8 + (lane >> 3);
+        const int pp = lane & 7;
+        const uint4 v = lds_read16(st3, (uint32_t)t * 128u + ((uint32_t)(pp ^ ((t >> 1) & 7)) << 4));
+        const int f = ft * FT + rr * 64 + pp * 8;
+        const int tp = pg * 128 + t;
+        if (tp < nvalid && f < a.m_t) *reinterpret_cast<uint4*>(ob + (base + tp) * a.ld_out + f) = v;
+      }
+      if (rr < 3) lds_sync();
+    }
+  };
+  // The phase-1 stages are free (the barriers above); chunks 0..2 go into stages 0..2. Before
+  // chunk c: its 8 copies are complete in every wave (the 16 newer ones may stay in flight).
+  for (int n = 0; n < 8; ++n) copy2(0, st0, n);
+  for (int n = 0; n < 8; ++n) copy2(1, st1, n);
+  for (int n = 0; n < 8; ++n) copy2(2, st2, n);
+  for (int ft = 0; ft < nft; ++ft) {
+    const int c0 = 8 * ft;
+    DYN_WAIT_KEEP(16);
+    compute2(st0, std::integral_constant<int, 0>{}, c0 + 3, st3);
+    DYN_WAIT_KEEP(16);
+    compute2(st1, std::integral_constant<int, 1>{}, c0 + 4, st0);
+    DYN_WAIT_KEEP(16);
+    compute2(st2, std::integral_constant<int, 2>{}, c0 + 5, st1);
+    DYN_WAIT_KEEP(16);
+    compute2(st3, std::integral_constant<int, 3>{}, c0 + 6, st2);
+    DYN_WAIT_KEEP(16);
+    compute2(st0, std::integral_constant<int, 4>{}, c0 + 7, st3);
+    DYN_WAIT_KEEP(16);
+    compute2(st1, std::integral_constant<int, 5>{}, c0 + 8, st0);
+    DYN_WAIT_KEEP(16);
+    compute2(st2, std::integral_constant<int, 6>{}, c0 + 9, st1);
+    DYN_WAIT_KEEP(16);
+    compute2(st3, std::integral_constant<int, 7>{}, c0 + 10, st2);
+    epilogue(ft);
+  }
+  wait_vmem();   // the zero-filled copies issued past the last chunk land before the exit
 }
+
+}  // namespace ring
 
 }  // namespace
 
@@ -614,7 +616,10 @@ hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int
     hipLaunchKernelGGL(ring::dyn_ring_kernel, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
-  return launch_dyn_t<16, 1>(p, stream);
+  p.pgroups = (S + 127) / 128;   // workgroups of 128 tokens p per split
+  p.tiles *= p.pgroups;
+  hipLaunchKernelGGL(ring::dyn512_kernel, dim3((unsigned)p.tiles), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace avey
