@@ -27,6 +27,11 @@ SMALL = {
     # S = 512: 2 x 2 quadrants per split pair, last split 40 tokens
     "s512_bf16": Config("s512_bf16", B=2, N=2600, d=128, S=512, k=2, m_t=128, m=256, dtype="bf16",
                         x_dist="mixture", n_centroids=16),
+    # S = 448: the dynamic core's 4 workgroups of 128 tokens per split end with a half-full one,
+    # the last split (108 tokens) leaves three of them empty; m_t = 320 ends on a partial
+    # 256-feature tile
+    "s448_bf16": Config("s448_bf16", B=1, N=1900, d=128, S=448, k=2, m_t=320, m=384, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
     # S = 64 < tile: heavy masking inside every tile
     "s64_bf16": Config("s64_bf16", B=1, N=700, d=64, S=64, k=2, m_t=64, m=128, dtype="bf16",
                        x_dist="mixture", n_centroids=8),
