@@ -60,6 +60,13 @@ struct GemmParams {
 template <int P>
 using Pos = std::integral_constant<int, P>;
 
+// 16-byte global store with the non-temporal hint (the output stream then takes less of the
+// caches' room from the operands still to be read)
+__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
 __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   __shared__ __align__(16) float s_bias[kMaxF];
@@ -310,7 +317,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
         const uint4 v = lds_read16(st3, (uint32_t)sl * 128u + ((uint32_t)(p ^ ((sl >> 1) & 7)) << 4));
         const int64_t tok = t0 + sl;
         const int f = f0 + mb * 64 + p * 8;
-        if (tok < a.M && f < a.F) *reinterpret_cast<uint4*>(a.C + tok * a.ldc + f) = v;
+        if (tok < a.M && f < a.F) store16_nt(a.C + tok * a.ldc + f, v);
       }
       if (mb < 3) lds_sync();
     }
