@@ -139,6 +139,34 @@ def _rows(t, name: str):
     return B, N, w, ld
 
 
+def _arg(t, fn: str, name: str, like, dtype, shape=None):
+    """Check a tensor argument before any launch: a contiguous device tensor on `like`'s device,
+    of dtype `dtype` and (when given) exactly `shape`; raises AveyError otherwise."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise AveyError(fn, -1, f"{name} must be a torch tensor")
+    if not t.is_cuda or t.device != like.device:
+        raise AveyError(fn, -1, f"{name} must be a device tensor on {like.device}, got {t.device}")
+    if t.dtype != dtype:
+        raise AveyError(fn, -3, f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise AveyError(fn, -2, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise AveyError(fn, -2, f"{name} must be contiguous")
+    return t
+
+
+def _out_rows(t, fn: str, name: str, like, shape):
+    """An output [B, N, width] tensor (any row stride): device and dtype of `like`, exact shape."""
+    if not t.is_cuda or t.device != like.device:
+        raise AveyError(fn, -1, f"{name} must be a device tensor on {like.device}, got {t.device}")
+    if t.dtype != like.dtype:
+        raise AveyError(fn, -3, f"{name} must have dtype {like.dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise AveyError(fn, -2, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return _rows(t, name)
+
+
 def _stream(t) -> int:
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -164,11 +192,42 @@ def rank_workspace(x, S: int):
     return torch.empty((max(n, 16),), device=x.device, dtype=torch.uint8)
 
 
+def _workspace_arg(fn: str, workspace, x, S: int):
+    """The caller's ranker workspace: a contiguous uint8 device tensor on x's device, at least
+    avey_rank_workspace_bytes(...) bytes long."""
+    import torch
+    B, N, d, _ = _rows(x, "x")
+    need = avey_rank_workspace_bytes(_dtype_code(x), B, N, d, S)
+    _arg(workspace, fn, "workspace", x, torch.uint8)
+    if workspace.numel() < need:
+        raise AveyError(fn, -2, f"workspace holds {workspace.numel()} bytes, {need} needed")
+    return workspace
+
+
+def _scores_arg(fn: str, scores, x, B: int, n_s: int):
+    import torch
+    if scores is None:
+        return torch.empty((B, n_s, n_s), device=x.device, dtype=torch.float32)
+    return _arg(scores, fn, "scores", x, torch.float32, (B, n_s, n_s))
+
+
+def _topk_args(fn: str, idx, w, like, B: int, n_s: int, k: int):
+    import torch
+    if idx is None:
+        idx = torch.empty((B, n_s, k), device=like.device, dtype=torch.int32)
+    if w is None:
+        w = torch.empty((B, n_s, k), device=like.device, dtype=torch.float32)
+    _arg(idx, fn, "idx", like, torch.int32, (B, n_s, k))
+    _arg(w, fn, "w", like, torch.float32, (B, n_s, k))
+    return idx, w
+
+
 def avey_maxsim_prepare(x, S: int, workspace=None):
     """Fill (and return) the ranker workspace from x [B, N, d]."""
     B, N, d, ld = _rows(x, "x")
     if workspace is None:
         workspace = rank_workspace(x, S)
+    _workspace_arg("avey_maxsim_prepare", workspace, x, S)
     _check("avey_maxsim_prepare", load_library().avey_maxsim_prepare(
         x.data_ptr(), _dtype_code(x), B, N, d, ld, S, workspace.data_ptr(), _stream(x)))
     return workspace
@@ -177,11 +236,10 @@ def avey_maxsim_prepare(x, S: int, workspace=None):
 def avey_maxsim_scores(workspace, x, S: int, scores=None):
     """All-pairs MaxSim scores [B, n_s, n_s] (fp32, diagonal -inf) from a workspace that
     avey_maxsim_prepare filled for x (x supplies the shape and dtype only)."""
-    import torch
     B, N, d, _ = _rows(x, "x")
     n_s = n_splits(N, S)
-    if scores is None:
-        scores = torch.empty((B, n_s, n_s), device=x.device, dtype=torch.float32)
+    _workspace_arg("avey_maxsim_scores", workspace, x, S)
+    scores = _scores_arg("avey_maxsim_scores", scores, x, B, n_s)
     _check("avey_maxsim_scores", load_library().avey_maxsim_scores(
         workspace.data_ptr(), _dtype_code(x), B, N, d, S, scores.data_ptr(), _stream(x)))
     return scores
@@ -192,11 +250,11 @@ def avey_topk_norm(scores, k: int, idx=None, w=None, preceding: bool = False):
 
     preceding=True: candidates of row i are the splits j < i; short rows end with (-1, 0)."""
     import torch
+    if not isinstance(scores, torch.Tensor) or scores.dim() != 3 or scores.shape[1] != scores.shape[2]:
+        raise AveyError("avey_topk_norm", -2, "scores must be a [B, n_s, n_s] tensor")
     B, n_s, _ = scores.shape
-    if idx is None:
-        idx = torch.empty((B, n_s, k), device=scores.device, dtype=torch.int32)
-    if w is None:
-        w = torch.empty((B, n_s, k), device=scores.device, dtype=torch.float32)
+    _arg(scores, "avey_topk_norm", "scores", scores, torch.float32)
+    idx, w = _topk_args("avey_topk_norm", idx, w, scores, B, n_s, k)
     lib = load_library()
     fn = lib.avey_topk_norm_preceding if preceding else lib.avey_topk_norm
     _check("avey_topk_norm", fn(scores.data_ptr(), B, n_s, k, idx.data_ptr(), w.data_ptr(), _stream(scores)))
@@ -206,21 +264,17 @@ def avey_topk_norm(scores, k: int, idx=None, w=None, preceding: bool = False):
 def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, workspace=None, preceding: bool = False):
     """(scores, idx, w) of the ranker for x [B, N, d]: bidirectional (every other split is a
     candidate), or with preceding=True unidirectional (only earlier splits)."""
-    import torch
     B, N, d, ld = _rows(x, "x")
     n_s = n_splits(N, S)
-    dev = x.device
+    fn_name = "avey_split_rank_preceding" if preceding else "avey_split_rank"
     if workspace is None:
         workspace = rank_workspace(x, S)
-    if scores is None:
-        scores = torch.empty((B, n_s, n_s), device=dev, dtype=torch.float32)
-    if idx is None:
-        idx = torch.empty((B, n_s, k), device=dev, dtype=torch.int32)
-    if w is None:
-        w = torch.empty((B, n_s, k), device=dev, dtype=torch.float32)
+    _workspace_arg(fn_name, workspace, x, S)
+    scores = _scores_arg(fn_name, scores, x, B, n_s)
+    idx, w = _topk_args(fn_name, idx, w, x, B, n_s, k)
     lib = load_library()
     fn = lib.avey_split_rank_preceding if preceding else lib.avey_split_rank
-    _check("avey_split_rank", fn(
+    _check(fn_name, fn(
         x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, workspace.data_ptr(), scores.data_ptr(), idx.data_ptr(),
         w.data_ptr(), _stream(x)))
     return scores, idx, w
@@ -229,20 +283,19 @@ def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, workspace=
 def avey_select_compress(x, idx, w, P, S: int, residual: bool = True, out=None):
     """Xhat [B, N, d] = P X_cat (+ X_i) per split, X_cat gathered through idx and weighted by w."""
     import torch
+    fn = "avey_select_compress"
     B, N, d, ld = _rows(x, "x")
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 3:
+        raise AveyError(fn, -2, "idx must be a [B, n_s, k] tensor")
     k = idx.shape[-1]
+    n_s = n_splits(N, S)
+    _arg(idx, fn, "idx", x, torch.int32, (B, n_s, k))
+    _arg(w, fn, "w", x, torch.float32, (B, n_s, k))
+    _arg(P, fn, "P", x, x.dtype, (S, (k + 1) * S))
     if out is None:
         out = torch.empty((B, N, d), device=x.device, dtype=x.dtype)
-    _, _, _, ld_out = _rows(out, "out")
-    if P.dtype != x.dtype or out.dtype != x.dtype:
-        raise AveyError("avey_select_compress", -3, "x, P and out must share one dtype")
-    if idx.dtype != torch.int32 or w.dtype != torch.float32:
-        raise AveyError("avey_select_compress", -3, "idx must be int32 and w float32")
-    if not (idx.is_contiguous() and w.is_contiguous() and P.is_contiguous()):
-        raise AveyError("avey_select_compress", -2, "idx, w and P must be contiguous")
-    if tuple(P.shape) != (S, (k + 1) * S):
-        raise AveyError("avey_select_compress", -2, f"P must be [S, (k+1)S] = [{S}, {(k + 1) * S}]")
-    _check("avey_select_compress", load_library().avey_select_compress(
+    _, _, _, ld_out = _out_rows(out, fn, "out", x, (B, N, d))
+    _check(fn, load_library().avey_select_compress(
         x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, idx.data_ptr(), w.data_ptr(), P.data_ptr(),
         1 if residual else 0, out.data_ptr(), ld_out, _stream(x)))
     return out
@@ -254,9 +307,7 @@ def avey_dyn_context(z_tail, S: int, eps: float, out=None):
     B, N, m_t, ld = _rows(z_tail, "z_tail")
     if out is None:
         out = torch.empty((B, N, m_t), device=z_tail.device, dtype=z_tail.dtype)
-    if out.dtype != z_tail.dtype:
-        raise AveyError("avey_dyn_context", -3, "out must have the dtype of z_tail")
-    _, _, _, ld_out = _rows(out, "out")
+    _, _, _, ld_out = _out_rows(out, "avey_dyn_context", "out", z_tail, (B, N, m_t))
     _check("avey_dyn_context", load_library().avey_dyn_context(
         z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, float(eps), out.data_ptr(), ld_out,
         _stream(z_tail)))
@@ -270,10 +321,7 @@ def _layer_args(fn: str, z_tail, S: int, bias, act: str):
         raise AveyError(fn, -2, f"act must be one of {sorted(AVEY_ACT)}")
     if bias is None:
         return 0, AVEY_ACT[act]
-    if bias.dtype != torch.float32 or not bias.is_contiguous() or tuple(bias.shape) != (S,):
-        raise AveyError(fn, -2, f"bias must be a contiguous float32 [S] = [{S}] tensor")
-    if bias.device != z_tail.device:
-        raise AveyError(fn, -1, "bias must be on the device of z_tail")
+    _arg(bias, fn, "bias", z_tail, torch.float32, (S,))
     return bias.data_ptr(), AVEY_ACT[act]
 
 
@@ -281,16 +329,15 @@ def avey_dyn_layer(z_tail, S: int, eps: float, bias=None, act: str = "identity",
     """act(S~ Z_t + bias[slot]) per split: the dynamic layer with its bias and activation; norm
     selects the row normalisation of the cosine matrix ("sum", "softmax", "rms" or "none")."""
     import torch
+    fn = "avey_dyn_layer"
     B, N, m_t, ld = _rows(z_tail, "z_tail")
-    bptr, code = _layer_args("avey_dyn_layer", z_tail, S, bias, act)
+    bptr, code = _layer_args(fn, z_tail, S, bias, act)
     if norm not in AVEY_NORM:
-        raise AveyError("avey_dyn_layer", -2, f"norm must be one of {sorted(AVEY_NORM)}")
+        raise AveyError(fn, -2, f"norm must be one of {sorted(AVEY_NORM)}")
     if out is None:
         out = torch.empty((B, N, m_t), device=z_tail.device, dtype=z_tail.dtype)
-    if out.dtype != z_tail.dtype:
-        raise AveyError("avey_dyn_layer", -3, "out must have the dtype of z_tail")
-    _, _, _, ld_out = _rows(out, "out")
-    _check("avey_dyn_layer", load_library().avey_dyn_layer(
+    _, _, _, ld_out = _out_rows(out, fn, "out", z_tail, (B, N, m_t))
+    _check(fn, load_library().avey_dyn_layer(
         z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, float(eps), AVEY_NORM[norm], bptr, code,
         out.data_ptr(), ld_out, _stream(z_tail)))
     return out
@@ -299,16 +346,14 @@ def avey_dyn_layer(z_tail, S: int, eps: float, bias=None, act: str = "identity",
 def avey_static_layer(z_tail, V, S: int, bias=None, act: str = "identity", out=None):
     """act(V Z_t + bias[slot]) per split, V [S, S] mixing the split's token positions."""
     import torch
+    fn = "avey_static_layer"
     B, N, m_t, ld = _rows(z_tail, "z_tail")
-    bptr, code = _layer_args("avey_static_layer", z_tail, S, bias, act)
-    if V.dtype != z_tail.dtype or not V.is_contiguous() or tuple(V.shape) != (S, S):
-        raise AveyError("avey_static_layer", -2, f"V must be a contiguous [S, S] = [{S}, {S}] tensor of z_tail's dtype")
+    bptr, code = _layer_args(fn, z_tail, S, bias, act)
+    _arg(V, fn, "V", z_tail, z_tail.dtype, (S, S))
     if out is None:
         out = torch.empty((B, N, m_t), device=z_tail.device, dtype=z_tail.dtype)
-    if out.dtype != z_tail.dtype:
-        raise AveyError("avey_static_layer", -3, "out must have the dtype of z_tail")
-    _, _, _, ld_out = _rows(out, "out")
-    _check("avey_static_layer", load_library().avey_static_layer(
+    _, _, _, ld_out = _out_rows(out, fn, "out", z_tail, (B, N, m_t))
+    _check(fn, load_library().avey_static_layer(
         z_tail.data_ptr(), _dtype_code(z_tail), B, N, m_t, ld, S, V.data_ptr(), bptr, code, out.data_ptr(),
         ld_out, _stream(z_tail)))
     return out
@@ -317,18 +362,18 @@ def avey_static_layer(z_tail, V, S: int, bias=None, act: str = "identity", out=N
 def avey_enrich(x, U, b=None, out=None):
     """Z [B, N, m] = ReLU(X U + b)^2 for x [B, N, d], U [d, m], b [m] float32 (or None)."""
     import torch
+    fn = "avey_enrich"
     B, N, d, ld = _rows(x, "x")
-    if U.dtype != x.dtype or not U.is_contiguous() or U.dim() != 2 or U.shape[0] != d:
-        raise AveyError("avey_enrich", -2, f"U must be a contiguous [d, m] tensor of x's dtype (d = {d})")
+    if not isinstance(U, torch.Tensor) or U.dim() != 2:
+        raise AveyError(fn, -2, "U must be a [d, m] tensor")
     m = U.shape[1]
-    if b is not None and (b.dtype != torch.float32 or not b.is_contiguous() or tuple(b.shape) != (m,)):
-        raise AveyError("avey_enrich", -2, f"b must be a contiguous float32 [{m}] tensor")
+    _arg(U, fn, "U", x, x.dtype, (d, m))
+    if b is not None:
+        _arg(b, fn, "b", x, torch.float32, (m,))
     if out is None:
         out = torch.empty((B, N, m), device=x.device, dtype=x.dtype)
-    if out.dtype != x.dtype:
-        raise AveyError("avey_enrich", -3, "out must have x's dtype")
-    _, _, _, ld_out = _rows(out, "out")
-    _check("avey_enrich", load_library().avey_enrich(
+    _, _, _, ld_out = _out_rows(out, fn, "out", x, (B, N, m))
+    _check(fn, load_library().avey_enrich(
         x.data_ptr(), _dtype_code(x), B * N, d, ld, U.data_ptr(), m, b.data_ptr() if b is not None else 0,
         out.data_ptr(), ld_out, _stream(x)))
     return out
@@ -338,19 +383,23 @@ def avey_fuse(z, m_h: int, c, O, x, out=None):
     """Y [B, N, d] = [Z_h || C] O + X: z [B, N, >= m_h] (head = its first m_h columns), c [B, N, m_t],
     O [m_h + m_t, d], x [B, N, d] the layer's input."""
     import torch
+    fn = "avey_fuse"
     B, N, d, ld_x = _rows(x, "x")
     _, _, m_t, ld_c = _rows(c, "c")
     _, _, wz, ld_z = _rows(z, "z")
+    if tuple(c.shape[:2]) != (B, N) or tuple(z.shape[:2]) != (B, N):
+        raise AveyError(fn, -2, f"z and c must have the leading shape [B, N] = [{B}, {N}] of x")
+    if z.device != x.device or c.device != x.device:
+        raise AveyError(fn, -1, "z, c and x must be on one device")
     if wz < m_h:
-        raise AveyError("avey_fuse", -2, f"z has {wz} columns, fewer than m_h = {m_h}")
-    if O.dtype != x.dtype or not O.is_contiguous() or tuple(O.shape) != (m_h + m_t, d):
-        raise AveyError("avey_fuse", -2, f"O must be a contiguous [{m_h + m_t}, {d}] tensor of x's dtype")
+        raise AveyError(fn, -2, f"z has {wz} columns, fewer than m_h = {m_h}")
     if z.dtype != x.dtype or c.dtype != x.dtype:
-        raise AveyError("avey_fuse", -3, "z, c, O and x must share one dtype")
+        raise AveyError(fn, -3, "z, c, O and x must share one dtype")
+    _arg(O, fn, "O", x, x.dtype, (m_h + m_t, d))
     if out is None:
         out = torch.empty((B, N, d), device=x.device, dtype=x.dtype)
-    _, _, _, ld_y = _rows(out, "out")
-    _check("avey_fuse", load_library().avey_fuse(
+    _, _, _, ld_y = _out_rows(out, fn, "out", x, (B, N, d))
+    _check(fn, load_library().avey_fuse(
         z.data_ptr(), _dtype_code(x), B * N, m_h, ld_z, c.data_ptr(), m_t, ld_c, O.data_ptr(), d,
         x.data_ptr(), ld_x, out.data_ptr(), ld_y, _stream(x)))
     return out
@@ -373,6 +422,8 @@ def avey_probe_mfma_bf16(iters: int, changing: bool, sink=None):
     import torch
     if sink is None:
         sink = torch.zeros(4096, device="cuda", dtype=torch.float32)
+    if not sink.is_cuda or sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < 4096:
+        raise AveyError("avey_probe_mfma_bf16", -2, "sink must be a contiguous float32 device tensor of >= 4096 values")
     st = torch.cuda.current_stream().cuda_stream
     _check("avey_probe_mfma_bf16",
            load_library().avey_probe_mfma_bf16(int(iters), 1 if changing else 0, sink.data_ptr(), st))
@@ -383,6 +434,8 @@ def avey_probe_copy(src, dst) -> None:
     """Enqueue dst <- src (same number of bytes, contiguous, 16-byte aligned) on the current stream."""
     import torch
     nbytes = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda and src.device == dst.device):
+        raise AveyError("avey_probe_copy", -1, "src and dst must be device tensors on one device")
     if not (src.is_contiguous() and dst.is_contiguous()) or dst.numel() * dst.element_size() != nbytes:
         raise AveyError("avey_probe_copy", -2, "src and dst must be contiguous and of the same size in bytes")
     st = torch.cuda.current_stream().cuda_stream

@@ -88,49 +88,103 @@ def algorithmic(cfg):
     }
 
 
-def blas_threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
-        if n:
-            return max(n)
-    except Exception:
-        pass
-    return len(os.sched_getaffinity(0))
+def pipeline_roofline(cfg, value: float, peak_tflops: float) -> dict:
+    """The step against the rooflines of the hot path's own work (all-pairs MaxSim, gather +
+    compress, dynamic layer; top-k's few KiB are left out): tokens/s the step would reach if every
+    kernel ran at its bound, max(FLOP / MFMA peak, bytes / HBM peak) per kernel, and the two
+    single-resource figures B N peak / sum(FLOP) and B N BW / sum(bytes). The normalised operand
+    copy of the explicit-workspace ranker is an implementation choice, not work of the method: it
+    is not counted."""
+    work = algorithmic(cfg)
+    names = ("maxsim", "compress", "dyn")
+    flop = sum(work[n]["flop"] for n in names)
+    byts = sum(work[n]["bytes"] for n in names)
+    t_roof = sum(max(work[n]["flop"] / (peak_tflops * 1e12), work[n]["bytes"] / (PEAK_HBM_GBS * 1e9))
+                 for n in names)
+    tokens = cfg.B * cfg.N
+    roof = tokens / t_roof
+    mfma = tokens * peak_tflops * 1e12 / flop
+    hbm = tokens * PEAK_HBM_GBS * 1e9 / byts
+    return {"tokens_per_s": round(roof, 1), "frac": round(value / roof, 4),
+            "mfma_tokens_per_s": round(mfma, 1), "mfma_frac": round(value / mfma, 4),
+            "hbm_tokens_per_s": round(hbm, 1), "hbm_frac": round(value / hbm, 4),
+            "flop_per_step": flop, "bytes_per_step": byts,
+            "basis": "sum over maxsim, compress, dyn of max(FLOP/peak, bytes/8 TB/s)"}
+
+
+def gap_histogram(scores, k: int, edges=(0.0, 1e-6, 1e-4, 1e-3, 1e-2, 1e-1)) -> dict:
+    """Histogram of the relative gap between the k-th and (k+1)-th best score of every row of the
+    score matrix the GPU computed (the diagonal left out): how close the workload's top-k
+    selections are to a tie. Counts per bin [e_i, e_{i+1}), the last bin open-ended."""
+    import numpy as np
+    s = scores.reshape(-1, scores.shape[-1]).astype(np.float64)
+    s = -np.sort(-s, axis=1)   # descending; the diagonal's -inf comes last
+    kth, nxt = s[:, k - 1], s[:, k]
+    gap = (kth - nxt) / np.abs(kth)
+    out = {}
+    for lo, hi in zip(edges, list(edges[1:]) + [float("inf")]):
+        out[f"[{lo:g},{hi:g})"] = int(((gap >= lo) & (gap < hi)).sum())
+    return {"rows": int(len(gap)), "bins": out, "min_gap": float(gap.min()),
+            "source": "the GPU's own score matrix of this run"}
+
+
+def _oracle_worker(args):
+    """One process of the CPU baseline: whole target splits of its share, in order, until the
+    deadline; the float64 oracle as it stands, with single-threaded BLAS."""
+    shard, deadline = args
+    from threadpoolctl import threadpool_limits
+    from oracle import avey_oracle as O
+    inp, xs, Ps = _CPU_STATE
+    cfg = inp.cfg
+    done = tok = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        for b, i in shard:
+            if time.time() >= deadline:
+                break
+            row = O.score_row(xs[b], cfg.S, i)
+            idx, w, _, _ = O.top_k(row, i, cfg.k)
+            O.compress_split(xs[b], cfg.S, idx, w, Ps, i)
+            rows = slice(i * cfg.S, min((i + 1) * cfg.S, cfg.N))
+            O.dyn_context_split(inp.z_tail_f64(b, rows), cfg.S, cfg.eps, 0)
+            done += 1
+            tok += rows.stop - rows.start
+    return done, tok, time.perf_counter() - t0
+
+
+_CPU_STATE = None
 
 
 def cpu_baseline(inp, budget_s: float = 12.0):
-    """The float64 oracle, as it stands, on whole target splits of the same workload until the
-    time budget is spent: score row + top-k, compression and dynamic layer of each split."""
-    import numpy as np
-    from oracle import avey_oracle as O
+    """The float64 oracle, as it stands, on whole target splits of the same workload (full score
+    row, top-k, compression and dynamic layer of each split), spread over one single-threaded
+    process per host core of this process's CPU share (at most 16) until the time budget is
+    spent. Runs before anything touches the GPU: the worker processes are forked."""
+    import multiprocessing as mp
+    global _CPU_STATE
     cfg = inp.cfg
     n_s = cfg.n_s
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
     stride = max(1, n_s // 16)
     order = [(b, i) for r in range(stride) for i in range(r, n_s, stride) for b in range(cfg.B)]
-    xs, Ps = {}, inp.P_f64()
-    done, tok = 0, 0
+    _CPU_STATE = (inp, {b: inp.x_f64(b) for b in range(cfg.B)}, inp.P_f64())
+    shards = [order[p::workers] for p in range(workers)]
     t0 = time.perf_counter()
-    for b, i in order:
-        if b not in xs:
-            xs[b] = inp.x_f64(b)
-        row = O.score_row(xs[b], cfg.S, i)
-        idx, w, _, _ = O.top_k(row, i, cfg.k)
-        O.compress_split(xs[b], cfg.S, idx, w, Ps, i)
-        rows = slice(i * cfg.S, min((i + 1) * cfg.S, cfg.N))
-        O.dyn_context_split(inp.z_tail_f64(b, rows), cfg.S, cfg.eps, 0)
-        done += 1
-        tok += rows.stop - rows.start
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
+    deadline = time.time() + budget_s
+    with mp.get_context("fork").Pool(workers) as pool:
+        res = pool.map(_oracle_worker, [(sh, deadline) for sh in shards])
+    wall = time.perf_counter() - t0
+    _CPU_STATE = None
+    done = sum(r[0] for r in res)
+    tok = sum(r[1] for r in res)
     return {
-        "value": tok / el,
+        "value": tok / wall,
         "unit": "tokens/s",
-        "cores": blas_threads(),
+        "cores": workers,
         "kind": "oracle",
         "sample": f"{done} of {cfg.B * n_s} target splits of the {cfg.name} workload (full score row, "
-                  f"top-k, compression and dynamic layer per split), {el:.1f} s, float64 numpy",
+                  f"top-k, compression and dynamic layer per split) in {wall:.1f} s over {workers} "
+                  f"single-threaded processes, float64 numpy",
     }
 
 
@@ -243,47 +297,9 @@ def measured_peaks(A, reps: int = 10):
                       f"avey_probe_copy (1 GiB, read + written), median of {reps} launches"}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="long")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--no-layers", action="store_true",
-                    help="skip the separate timing of the rest of a layer (static, dynamic, enricher, fuser)")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain device-to-device copy of this many MiB three times (the "
-                         "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the hot path here is the single-GPU kernel set; "
-              "run it with --gpus 1", file=sys.stderr)
-        return 2
-
+def upload(cfg, inp):
     import numpy as np
     import torch
-
-    import attention_free_long_amd as A
-    from synth import CONFIGS, make_inputs
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 20
-        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
-        return 0
-    cfg = CONFIGS[args.config]
-    inp = make_inputs(cfg)
-    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def dev(a):
         if cfg.dtype == "bf16":
@@ -291,8 +307,19 @@ def main(argv=None):
         return torch.from_numpy(a).to("cuda")
 
     x, P, z = dev(inp.x), dev(inp.P), dev(inp.z)
-    z_tail = z[..., inp.tail_col:]
+    return x, P, z, z[..., inp.tail_col:]
+
+
+def time_workload(A, cfg, inp, steps: int, warmup: int, peak: float):
+    """Time `steps` steps of the hot path on one workload after `warmup` untimed ones. Every library
+    call enqueues on torch's current stream, on which the events are recorded: each interval
+    brackets exactly one call. Returns the measurements and the device tensors."""
+    import numpy as np
+    import torch
+
+    x, P, z, z_tail = upload(cfg, inp)
     B, N, n_s, S, k = cfg.B, cfg.N, cfg.n_s, cfg.S, cfg.k
+    dt = x.dtype
     scores = torch.empty((B, n_s, n_s), device="cuda", dtype=torch.float32)
     idx = torch.empty((B, n_s, k), device="cuda", dtype=torch.int32)
     w = torch.empty((B, n_s, k), device="cuda", dtype=torch.float32)
@@ -309,8 +336,6 @@ def main(argv=None):
     )
 
     def step(ev=None):
-        # The events are recorded on torch's current stream, which is the stream every call
-        # enqueues its kernels on; each interval brackets exactly one library call.
         for j, call in enumerate(calls):
             if ev is not None:
                 ev[j].record()
@@ -318,74 +343,158 @@ def main(argv=None):
         if ev is not None:
             ev[len(calls)].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
+    for s_ in range(steps):
+        step(events[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: [] for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    per = {n: [ev[j].elapsed_time(ev[j + 1]) * 1e-3 for ev in events] for j, n in enumerate(names)}
     work = algorithmic(cfg)
     kern = {}
     for n in names:
         t = float(np.mean(per[n]))
-        entry = {"avg_us": t * 1e6, "median_us": float(np.median(per[n])) * 1e6, "min_us": float(np.min(per[n])) * 1e6}
+        e = {"avg_us": t * 1e6, "median_us": float(np.median(per[n])) * 1e6, "min_us": float(np.min(per[n])) * 1e6}
         if work[n]["flop"]:
-            entry["tflops"] = work[n]["flop"] / t / 1e12
-        entry["gbs"] = work[n]["bytes"] / t / 1e9
-        kern[n] = entry
-    ms_per_step = wall / args.steps * 1e3
-    value = B * N / (wall / args.steps)
+            e["tflops"] = work[n]["flop"] / t / 1e12
+        e["gbs"] = work[n]["bytes"] / t / 1e9
+        kern[n] = {kk: round(v, 3) for kk, v in e.items()}
+    value = B * N / (wall / steps)
+    ms_t = kern["maxsim"]["avg_us"] * 1e-6
+    comp_t = kern["compress"]["avg_us"] * 1e-6
+    dyn_t = kern["dyn"]["avg_us"] * 1e-6
+    res = {
+        "value": value,
+        "ms_per_step": wall / steps * 1e3,
+        "maxsim_achieved_tflops": work["maxsim"]["flop"] / ms_t / 1e12,
+        "compress_hbm_frac": round(work["compress"]["bytes"] / comp_t / 1e9 / PEAK_HBM_GBS, 4),
+        "compress_mfma_frac": round(work["compress"]["flop"] / comp_t / 1e12 / peak, 4),
+        "dyn_hbm_frac": round(work["dyn"]["bytes"] / dyn_t / 1e9 / PEAK_HBM_GBS, 4),
+        "dyn_mfma_frac": round(work["dyn"]["flop"] / dyn_t / 1e12 / peak, 4),
+        "kernels": kern,
+        "compress_cold": time_compress_cold(calls[3], work["compress"]["bytes"]),
+        "pipeline_roofline": pipeline_roofline(cfg, value, peak),
+        "gap_histogram": gap_histogram(scores.cpu().numpy(), k),
+    }
+    res["compress_cold"]["mfma_frac"] = round(work["compress"]["flop"] / (res["compress_cold"]["median_us"] * 1e-6)
+                                              / 1e12 / peak, 4)
+    return res, (x, z_tail, work)
+
+
+def workload_name(cfg) -> str:
+    return f"{cfg.name}: B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S} k={cfg.k} m_t={cfg.m_t} eps={cfg.eps}"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the separate timing of the rest of a layer (static, dynamic, enricher, fuser)")
+    ap.add_argument("--no-extreme", action="store_true",
+                    help="skip the 96K-token workload timed after the main one")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times (the "
+                         "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path here is the single-GPU kernel set; "
+              "run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    from synth import CONFIGS, make_inputs
+
+    cfg = None if args.copy_probe_mib > 0 else CONFIGS[args.config]
+    inp = None if cfg is None else make_inputs(cfg)
+    # The CPU baseline forks its worker processes: it runs before anything touches the GPU.
+    cpu = None
+    if cfg is not None and not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_budget)
+        cpu["value"] = round(cpu["value"], 2)
+
+    import torch
+
+    import attention_free_long_amd as A
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return 0
 
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-    ms_t = kern["maxsim"]["avg_us"] * 1e-6
-    achieved = work["maxsim"]["flop"] / ms_t / 1e12
+    r, (x, z_tail, work) = time_workload(A, cfg, inp, args.steps, args.warmup, peak)
+    achieved = r["maxsim_achieved_tflops"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_bytes("maxsim", cfg.name),
                 "traffic_unit": "bytes per launch"}
-    comp_t = kern["compress"]["avg_us"] * 1e-6
-    dyn_t = kern["dyn"]["avg_us"] * 1e-6
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(r["value"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: B={B} N={N} d={cfg.d} S={S} k={k} m_t={cfg.m_t} eps={cfg.eps}",
-                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "config": {"workload": workload_name(cfg), "global_batch": cfg.B, "seq_len": cfg.N,
+                   "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "pipeline_roofline": r["pipeline_roofline"],
         "maxsim_mfma_util_pct": round(100 * achieved / peak, 2),
-        "compress_hbm_frac": round(work["compress"]["bytes"] / comp_t / 1e9 / PEAK_HBM_GBS, 4),
-        "dyn_hbm_frac": round(work["dyn"]["bytes"] / dyn_t / 1e9 / PEAK_HBM_GBS, 4),
-        "dyn_mfma_frac": round(work["dyn"]["flop"] / dyn_t / 1e12 / peak, 4),
-        "kernels": {n: {kk: round(v, 3) for kk, v in e.items()} for n, e in kern.items()},
     }
-    result["compress_cold"] = time_compress_cold(calls[3], work["compress"]["bytes"])
+    for key in ("compress_hbm_frac", "compress_mfma_frac", "dyn_hbm_frac", "dyn_mfma_frac", "kernels",
+                "compress_cold", "gap_histogram"):
+        result[key] = r[key]
     if cfg.dtype == "bf16":
-        mp = measured_peaks(A)
-        result["measured_peaks"] = mp
-        roofline["measured_peak"] = mp["mfma_bf16_tflops_changing_operands"]
-        roofline["frac_measured"] = round(achieved / mp["mfma_bf16_tflops_changing_operands"], 4)
-        result["compress_hbm_frac_measured"] = round(work["compress"]["bytes"] / comp_t / 1e9 / mp["copy_gbs"], 4)
+        mp_ = measured_peaks(A)
+        result["measured_peaks"] = mp_
+        roofline["measured_peak"] = mp_["mfma_bf16_tflops_changing_operands"]
+        roofline["frac_measured"] = round(achieved / mp_["mfma_bf16_tflops_changing_operands"], 4)
+        comp_t = r["kernels"]["compress"]["avg_us"] * 1e-6
+        result["compress_hbm_frac_measured"] = round(work["compress"]["bytes"] / comp_t / 1e9 / mp_["copy_gbs"], 4)
     if not args.no_layers:
         result["layers"] = time_layers(A, cfg, inp, z_tail, work, max(10, args.steps // 2), peak)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
-        result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 2)
+    del x, z_tail
+    if not args.no_extreme and cfg.name != "extreme":
+        ecfg = CONFIGS["extreme"]
+        einp = make_inputs(ecfg)
+        e, _ = time_workload(A, ecfg, einp, max(5, args.steps // 5), max(3, args.warmup // 5), PEAK_BF16_TFLOPS)
+        result["extreme"] = {
+            "workload": workload_name(ecfg),
+            "value": round(e["value"], 1), "unit": "tokens/s", "ms_per_step": round(e["ms_per_step"], 4),
+            "steps": max(5, args.steps // 5),
+            "maxsim": {"achieved": round(e["maxsim_achieved_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(e["maxsim_achieved_tflops"] / PEAK_BF16_TFLOPS, 4)},
+            "compress_cold": e["compress_cold"],
+            "compress_hbm_frac": e["compress_hbm_frac"],
+            "dyn_hbm_frac": e["dyn_hbm_frac"], "dyn_mfma_frac": e["dyn_mfma_frac"],
+            "pipeline_roofline": e["pipeline_roofline"],
+            "kernels": e["kernels"],
+            "gap_histogram": e["gap_histogram"],
+        }
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
     return 0
 

@@ -58,19 +58,39 @@ def check_score_row(g_row: np.ndarray, o_row: np.ndarray, i: int, tol: float):
 
 
 def check_topk_row(g_idx, g_w, o_row, o_idx, gap, i, k, tol_w):
+    """Top-k of one row against the oracle under the tie rule. Returns how the row passed:
+    "exact" (gap >= TIE_GAP, identical sets), "band_same" (gap < TIE_GAP, identical sets) or
+    "band_differs" (gap < TIE_GAP, the sets differ only by indices inside the tie band)."""
     g_idx = [int(v) for v in g_idx]
     assert len(set(g_idx)) == k and i not in g_idx and all(0 <= j < len(o_row) for j in g_idx)
     assert g_w[0] == 1.0, f"w0 = {g_w[0]!r}"
+    o_set = set(int(v) for v in o_idx)
     if gap >= TIE_GAP:
-        assert set(g_idx) == set(int(v) for v in o_idx), f"top-k {g_idx} vs oracle {list(o_idx)} (gap {gap:.2e})"
+        assert set(g_idx) == o_set, f"top-k {g_idx} vs oracle {list(o_idx)} (gap {gap:.2e})"
+        how = "exact"
     else:
         kth = o_row[o_idx[-1]]
-        for j in set(g_idx) ^ set(int(v) for v in o_idx):
+        for j in set(g_idx) ^ o_set:
             assert abs(o_row[j] - kth) <= TIE_GAP * abs(kth), f"index {j} outside the tie band"
+        how = "band_same" if set(g_idx) == o_set else "band_differs"
+    # the GPU's ranks are in order of its own scores: non-increasing oracle scores up to the band
+    o_sel = np.array([o_row[j] for j in g_idx])
+    assert np.all(o_sel[1:] <= o_sel[:-1] + TIE_GAP * np.abs(o_sel[:-1])), f"rank order {g_idx}"
     # weights against the oracle's scores at the GPU's own indices
-    ow = np.array([o_row[j] for j in g_idx]) / o_row[g_idx[0]]
+    ow = o_sel / o_row[g_idx[0]]
     rel = np.abs(np.asarray(g_w, dtype=np.float64) - ow) / np.abs(ow)
     assert rel.max() <= tol_w, f"w rel err {rel.max():.3e}"
+    return how
+
+
+def gap_histogram(gaps, edges=(0.0, 1e-6, 1e-4, 1e-3, 1e-2, 1e-1)):
+    """Counts of the oracle's relative k-th vs (k+1)-th score gaps per bin [e_i, e_{i+1}), the last
+    bin open-ended; exact ties (gap 0) fall in the first bin."""
+    g = np.asarray(list(gaps), dtype=np.float64)
+    out = {}
+    for lo, hi in zip(edges, list(edges[1:]) + [math.inf]):
+        out[f"[{lo:g},{hi:g})"] = int(((g >= lo) & (g < hi)).sum())
+    return out
 
 
 def split_rows_of(N: int, S: int, i: int) -> slice:
