@@ -3,7 +3,7 @@
 Thin ctypes binding over libavey.so (see include/avey.h): argument marshalling only, every step
 runs in the library's HIP kernels. torch supplies device memory and the current stream.
 
-    scores, idx, w = avey_split_rank(x, S, k)        # allocates the ranker workspace if not given
+    scores, idx, w = avey_split_rank(x, S, k)        # no workspace: token norms on chip
     xhat = avey_select_compress(x, idx, w, P, S, residual=True)
     out = avey_dyn_context(z_tail, S, eps)
     out = avey_dyn_layer(z_tail, S, eps, bias, act="relu")       # sigma(S~ Z_t + b)
@@ -24,11 +24,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libavey.so"
 AVEY_F32, AVEY_BF16 = 0, 1
 AVEY_ACT = {"identity": 0, "relu": 1}
 AVEY_NORM = {"sum": 0, "softmax": 1, "rms": 2, "none": 3}
-AVEY_ABI_VERSION = 1
+AVEY_ABI_VERSION = 2
 
 EXPORTS = (
     "avey_abi_version",
     "avey_status_str",
+    "avey_maxsim",
     "avey_rank_workspace_bytes",
     "avey_maxsim_prepare",
     "avey_maxsim_scores",
@@ -82,9 +83,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_topk_norm.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.avey_topk_norm_preceding.restype = i32
     lib.avey_topk_norm_preceding.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.avey_maxsim.restype = i32
+    lib.avey_maxsim.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp]
     for fn in (lib.avey_split_rank, lib.avey_split_rank_preceding):
         fn.restype = i32
-        fn.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, vp]
+        fn.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.avey_select_compress.restype = i32
     lib.avey_select_compress.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32, vp, i64, vp]
     lib.avey_dyn_context.restype = i32
@@ -261,22 +264,47 @@ def avey_topk_norm(scores, k: int, idx=None, w=None, preceding: bool = False):
     return idx, w
 
 
-def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, workspace=None, preceding: bool = False):
-    """(scores, idx, w) of the ranker for x [B, N, d]: bidirectional (every other split is a
-    candidate), or with preceding=True unidirectional (only earlier splits)."""
+def avey_maxsim(x, S: int, scores=None):
+    """All-pairs MaxSim scores [B, n_s, n_s] (fp32, diagonal -inf) straight from x [B, N, d], with
+    no workspace (token norms on chip)."""
+    B, N, d, ld = _rows(x, "x")
+    n_s = n_splits(N, S)
+    scores = _scores_arg("avey_maxsim", scores, x, B, n_s)
+    _check("avey_maxsim", load_library().avey_maxsim(
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, scores.data_ptr(), _stream(x)))
+    return scores
+
+
+def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, preceding: bool = False):
+    """(scores, idx, w) of the ranker for x [B, N, d], with no workspace: bidirectional (every
+    other split is a candidate), or with preceding=True unidirectional (only earlier splits)."""
     B, N, d, ld = _rows(x, "x")
     n_s = n_splits(N, S)
     fn_name = "avey_split_rank_preceding" if preceding else "avey_split_rank"
-    if workspace is None:
-        workspace = rank_workspace(x, S)
-    _workspace_arg(fn_name, workspace, x, S)
     scores = _scores_arg(fn_name, scores, x, B, n_s)
     idx, w = _topk_args(fn_name, idx, w, x, B, n_s, k)
     lib = load_library()
     fn = lib.avey_split_rank_preceding if preceding else lib.avey_split_rank
     _check(fn_name, fn(
-        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, workspace.data_ptr(), scores.data_ptr(), idx.data_ptr(),
-        w.data_ptr(), _stream(x)))
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, scores.data_ptr(), idx.data_ptr(), w.data_ptr(),
+        _stream(x)))
+    return scores, idx, w
+
+
+def avey_split_rank_ws(x, S: int, k: int, workspace=None, scores=None, idx=None, w=None, preceding: bool = False):
+    """The same ranker through the explicit-workspace path: avey_maxsim_prepare, avey_maxsim_scores
+    and the top-k call on the current stream (allocates the workspace if not given)."""
+    B, N, d, _ = _rows(x, "x")
+    n_s = n_splits(N, S)
+    fn_name = "avey_split_rank_ws"
+    if workspace is None:
+        workspace = rank_workspace(x, S)
+    _workspace_arg(fn_name, workspace, x, S)
+    scores = _scores_arg(fn_name, scores, x, B, n_s)
+    idx, w = _topk_args(fn_name, idx, w, x, B, n_s, k)
+    avey_maxsim_prepare(x, S, workspace)
+    avey_maxsim_scores(workspace, x, S, scores)
+    avey_topk_norm(scores, k, idx, w, preceding=preceding)
     return scores, idx, w
 
 

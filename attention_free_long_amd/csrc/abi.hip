@@ -28,12 +28,12 @@ avey_status check_common(avey_dtype dt, int64_t B, int64_t N, int32_t S, bool* e
   return AVEY_OK;
 }
 
-// A [B, N, width] operand with row stride ld.
-avey_status check_tensor(const void* p, avey_dtype dt, int64_t N, int64_t width, int64_t ld) {
+// A [B, N, width] operand with row stride ld; bf16 widths must be multiples of `mult`.
+avey_status check_tensor(const void* p, avey_dtype dt, int64_t N, int64_t width, int64_t ld, int64_t mult = 64) {
   if (!p) return AVEY_ERR_NULL;
   if (width < 1 || ld < width) return AVEY_ERR_SHAPE;
   if (dt == AVEY_BF16) {
-    if (width % 64) return AVEY_ERR_UNSUPPORTED;
+    if (width % mult) return AVEY_ERR_UNSUPPORTED;
     if (ld % 8 || !aligned(p, 16)) return AVEY_ERR_ALIGN;
     if (N * ld >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // byte offsets within a sequence stay < 2^31
   } else {
@@ -52,23 +52,26 @@ avey_status check_split_bf16(avey_dtype dt, int32_t S) {
     if (s_ != AVEY_OK) return s_;           \
   } while (0)
 
+// Feature count of the bf16 ranker workspace: d padded with zeros to whole chunks of 32.
+int64_t padded_d(avey_dtype dt, int64_t d) { return dt == AVEY_BF16 ? (d + 31) / 32 * 32 : d; }
+
 // Bytes of the ranker workspace (normalised, padded copy of X), or a negative status.
 int64_t workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S) {
   const int64_t eb = dt == AVEY_BF16 ? 2 : 4;
-  return B * splits(N, S) * S * d * eb;
+  return B * splits(N, S) * S * padded_d(dt, d) * eb;
 }
 
-// Checks of the ranker's first two stages (preparation and scoring) on the shape alone.
+// Checks of the ranker (scoring, and the workspace path's preparation) on the shape alone. bf16
+// takes S a multiple of 16 and d a multiple of 8.
 avey_status check_rank_shape(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S, bool* empty) {
   AVEY_TRY(check_common(dt, B, N, S, empty));
   if (*empty) return AVEY_OK;
   if (d < 1) return AVEY_ERR_SHAPE;
   const int64_t n_s = splits(N, S);
   if (n_s < 2) return AVEY_ERR_SHAPE;
-  AVEY_TRY(check_split_bf16(dt, S));
   if (dt == AVEY_BF16) {
-    if (d % 64) return AVEY_ERR_UNSUPPORTED;
-    if (n_s * S * d >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // workspace byte offsets per sequence < 2^31
+    if (S % 16 || d % 8) return AVEY_ERR_UNSUPPORTED;
+    if (n_s * S * padded_d(dt, d) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // workspace offsets < 2^31
     if (n_s * (n_s - 1) / 2 > kI32) return AVEY_ERR_UNSUPPORTED;
   } else {
     if (B * n_s * n_s > kI32) return AVEY_ERR_UNSUPPORTED;
@@ -77,12 +80,20 @@ avey_status check_rank_shape(avey_dtype dt, int64_t B, int64_t N, int64_t d, int
   return AVEY_OK;
 }
 
+// The workspace-free scoring's reads of X: the kernel's byte offsets per sequence, up to the rows
+// of a whole last unit past N (which it reads as zeros), stay below 2^31.
+avey_status check_rank_rows(const void* x, avey_dtype dt, int64_t N, int64_t d, int64_t ld_x) {
+  AVEY_TRY(check_tensor(x, dt, N, d, ld_x, 8));
+  if (dt == AVEY_BF16 && (N + 512) * ld_x >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;
+  return AVEY_OK;
+}
+
 avey_status check_prepare(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
                           const void* ws, bool* empty) {
   AVEY_TRY(check_rank_shape(dt, B, N, d, S, empty));
   if (*empty) return AVEY_OK;
   if (!ws) return AVEY_ERR_NULL;
-  AVEY_TRY(check_tensor(x, dt, N, d, ld_x));
+  AVEY_TRY(check_tensor(x, dt, N, d, ld_x, 8));
   if (!aligned(ws, 16)) return AVEY_ERR_ALIGN;
   return AVEY_OK;
 }
@@ -173,20 +184,35 @@ avey_status avey_topk_norm_preceding(const float* scores, int64_t B, int64_t n_s
 }  // extern "C"
 
 namespace {
+// MaxSim straight from X (no workspace): every check before the launch.
+avey_status check_maxsim_rows(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
+                              int32_t S, const float* scores, bool* empty) {
+  AVEY_TRY(check_rank_shape(dt, B, N, d, S, empty));
+  if (*empty) return AVEY_OK;
+  if (!scores) return AVEY_ERR_NULL;
+  AVEY_TRY(check_rank_rows(x, dt, N, d, ld_x));
+  if (!aligned(scores, 4)) return AVEY_ERR_ALIGN;
+  return AVEY_OK;
+}
+
+avey_status launch_maxsim_rows(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
+                               int32_t S, float* scores, hipStream_t st) {
+  if (dt == AVEY_BF16)
+    return hip_status(launch_maxsim_rows_bf16(static_cast<const uint16_t*>(x), B, N, (int)d, ld_x, S, scores, st));
+  return hip_status(launch_maxsim_rows_f32(static_cast<const float*>(x), B, N, (int)d, ld_x, S, scores, st));
+}
+
 avey_status split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
-                       int32_t k, void* workspace, float* scores, int32_t* idx, float* w, bool preceding,
-                       void* stream) {
-  // Every check of the three stages runs before the first launch.
+                       int32_t k, float* scores, int32_t* idx, float* w, bool preceding, void* stream) {
+  // Every check of both stages runs before the first launch.
   bool empty = false;
-  AVEY_TRY(check_prepare(x, dt, B, N, d, ld_x, S, workspace, &empty));
+  AVEY_TRY(check_maxsim_rows(x, dt, B, N, d, ld_x, S, scores, &empty));
   if (empty) return AVEY_OK;
-  AVEY_TRY(check_scores(workspace, dt, B, N, d, S, scores, &empty));
   const int64_t n_s = splits(N, S);
   AVEY_TRY(check_topk(scores, B, n_s, k, idx, w, &empty));
-  AVEY_TRY(avey_maxsim_prepare(x, dt, B, N, d, ld_x, S, workspace, stream));
-  AVEY_TRY(avey_maxsim_scores(workspace, dt, B, N, d, S, scores, stream));
-  return preceding ? avey_topk_norm_preceding(scores, B, n_s, k, idx, w, stream)
-                   : avey_topk_norm(scores, B, n_s, k, idx, w, stream);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  AVEY_TRY(launch_maxsim_rows(x, dt, B, N, d, ld_x, S, scores, st));
+  return hip_status(launch_topk_norm(scores, B, n_s, k, preceding, idx, w, st));
 }
 // Row-wise (position-wise) entry points: a [M, width] operand set.
 avey_status check_rows(avey_dtype dt, int64_t M, bool* empty) {
@@ -229,15 +255,22 @@ avey_status dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, i
 
 extern "C" {
 
+avey_status avey_maxsim(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
+                        float* scores, void* stream) {
+  bool empty = false;
+  AVEY_TRY(check_maxsim_rows(x, dt, B, N, d, ld_x, S, scores, &empty));
+  if (empty) return AVEY_OK;
+  return launch_maxsim_rows(x, dt, B, N, d, ld_x, S, scores, reinterpret_cast<hipStream_t>(stream));
+}
+
 avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x, int32_t S,
-                            int32_t k, void* workspace, float* scores, int32_t* idx, float* w, void* stream) {
-  return split_rank(x, dt, B, N, d, ld_x, S, k, workspace, scores, idx, w, false, stream);
+                            int32_t k, float* scores, int32_t* idx, float* w, void* stream) {
+  return split_rank(x, dt, B, N, d, ld_x, S, k, scores, idx, w, false, stream);
 }
 
 avey_status avey_split_rank_preceding(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
-                                      int32_t S, int32_t k, void* workspace, float* scores, int32_t* idx, float* w,
-                                      void* stream) {
-  return split_rank(x, dt, B, N, d, ld_x, S, k, workspace, scores, idx, w, true, stream);
+                                      int32_t S, int32_t k, float* scores, int32_t* idx, float* w, void* stream) {
+  return split_rank(x, dt, B, N, d, ld_x, S, k, scores, idx, w, true, stream);
 }
 
 avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,

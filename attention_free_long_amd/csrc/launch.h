@@ -8,8 +8,12 @@ namespace avey {
 
 hipError_t launch_prepare(const void* x, bool bf16, int64_t B, int64_t N, int d, int64_t ld, int S, void* ws,
                           hipStream_t stream);
+// MaxSim from the packed, normalised workspace that launch_prepare wrote (d padded to whole chunks
+// of 32 features), and straight from the caller's row-major X (norms on chip).
 hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
                               hipStream_t stream);
+hipError_t launch_maxsim_rows_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld, int S, float* scores,
+                                   hipStream_t stream);
 hipError_t launch_topk_norm(const float* scores, int64_t B, int64_t n_s, int k, bool preceding, int32_t* idx,
                             float* w, hipStream_t stream);
 
@@ -46,6 +50,8 @@ hipError_t launch_fuse_f32(const float* z, int64_t M, int m_h, int64_t ld_z, con
                            hipStream_t stream);
 
 hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S, float* scores, hipStream_t stream);
+hipError_t launch_maxsim_rows_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld, int S, float* scores,
+                                  hipStream_t stream);
 hipError_t launch_compress_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld_x, int S, int k,
                                const int32_t* idx, const float* w, const float* P, int residual, float* xhat,
                                int64_t ld_out, hipStream_t stream, LayerEpi epi = {});

@@ -2,15 +2,25 @@
 //
 // MaxSim relevance of candidate split j to target split i is the sum over the tokens t of i of
 // the largest cosine between x_t and any token u of j (paperlayer.ai "Avey-B" summary,
-// section 3; papernotes.org Avey-B note, 方法详解/整体框架). The operands are the L2-normalised
-// tokens n_t = N(x_t) (papernotes.org Avey-B note, 关键设计 2), prepared once per call in a
-// split-packed bf16 copy (prepare.hip), so that an MFMA tile C = N(X_i) N(X_j)^T holds the
-// cosines themselves and both directions of the pair come from it:
-//   score(i <- j) = sum_t max_u C_tu          (row direction)
-//   score(j <- i) = sum_u max_t C_tu          (column direction)
+// section 3; papernotes.org Avey-B note, 方法详解/整体框架). With n_t = N(x_t) the L2-normalised
+// token (papernotes.org Avey-B note, 关键设计 2) and C = X_i X_j^T the tile of dot products,
+// cos(x_t, x_u) = C_tu rn_t rn_u with rn = 1 / |x| (0 for a zero token), and both directions of
+// the pair come from one tile:
+//   score(i <- j) = sum_t rn_t max_u C_tu rn_u          (row direction)
+//   score(j <- i) = sum_u rn_u max_t C_tu rn_t          (column direction)
 // Each unordered pair i < j is computed once, and no token-by-token similarity leaves the chip.
 //
-// Units are 256 target rows x 256 candidate rows (one per pair at S = 256, four at S = 512).
+// Two operand sources, one kernel template:
+//   * row-major (kRow): the caller's X as it is ([B, N, d], row stride ld). Every wave sums the
+//     squares of one 32-row block of each operand from the MFMA fragments it reads anyway, so
+//     the norms of the unit's 512 tokens are on chip when the K loop ends, and the epilogue
+//     scales each direction's candidates before taking maxima. Nothing but the scores is
+//     written to memory.
+//   * packed: a copy of N(x) that prepare.hip wrote split by split in chunk planes of 32
+//     features ([B][n_s][nk][S][32] bf16): the tile holds the cosines themselves, and every copy
+//     instruction reads 1 KiB of contiguous memory.
+//
+// Units are 256 target rows x 256 candidate rows (one per pair at S <= 256, four at S <= 512).
 // One workgroup of 8 waves per CU (2 per SIMD), in a 2 x 4 grid: each wave owns 128 x 64 of the
 // fp32 accumulator (8 MFMA 32x32x16 blocks). Features stream through a 4-stage LDS ring in
 // chunks of 32 by direct global -> LDS copies, three chunks in flight while one is multiplied
@@ -18,7 +28,7 @@
 // the wait for the next chunk comes before the last group, whose MFMAs hide the next chunk's
 // first fragment reads);
 // the next unit's first three chunks are copied while the current one finishes and during its
-// epilogue. The packed layout makes every copy instruction read 1 KiB of contiguous memory.
+// epilogue.
 //
 // Persistent grid: workgroups are dealt to the 8 XCDs round-robin; each XCD owns one contiguous
 // range of pair tiles, walked in bands of 4 target splits, so that the target operands of the
@@ -39,9 +49,11 @@ constexpr int RB = 64;    // bytes per LDS row (one chunk of one token)
 __device__ __forceinline__ uint32_t sw4(int r) { return (uint32_t)((r >> 2) & 3); }
 
 struct MaxsimParams {
-  const uint16_t* xp;   // packed N(x): [B][n_s][d / 32][S][32] bf16, padding tokens zero
+  const uint16_t* x;    // kRow: X [B, N, d] row stride ld; packed: N(x) [B][n_s][nk][S][32]
+  int64_t ld;           // kRow: row stride of X in elements
   int64_t N;
   int d, S, n_s;
+  int nk;               // chunks of 32 features (the last one partial when d % 32 != 0)
   int q;                // 256-row blocks per split
   int pairs;            // unordered pairs per sequence
   int64_t tiles;        // B * pairs
@@ -96,13 +108,17 @@ struct Unit {
 // every wave's older copies have landed in LDS and every wave is done with the previous stage.
 #define WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+template <bool kRow, bool kTail>
 __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   // One LDS object per stage (target block, then candidate block): the compiler tracks copies
   // per object, so reads of one stage do not wait for copies into another. Stage 3 doubles as
   // the epilogue's row-max scratch.
   __shared__ __align__(16) uint8_t st0[2 * T * RB], st1[2 * T * RB], st2[2 * T * RB], st3[2 * T * RB];
   __shared__ __align__(16) float s_biA[T];   // per target row: 0, or -inf for a padding token
-  __shared__ float s_biB[T];                 // per candidate row
+  __shared__ __align__(16) float s_biB[T];   // per candidate row
+  __shared__ __align__(16) float s_rnA[T];   // kRow: per target row 1 / |x_t| (0 for a zero token)
+  __shared__ __align__(16) float s_rnB[T];   // kRow: per candidate row
+  __shared__ float s_ssA[2 * T], s_ssB[2 * T];   // kRow: running sums of squares, [k-half][row]
   __shared__ float s_cm[2][T];               // column maxima of the two row halves
   __shared__ float s_colmax[2 * T];          // running column maxima over target blocks (S = 512)
   __shared__ float s_red[8];
@@ -119,75 +135,154 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   int64_t t = l;
   if (t >= cnt) return;
 
-  const int nk = a.d / KH;
-  uint32_t fa[2], fb[2];   // fragment offsets of the two k-steps of a chunk
+  const int nk = a.nk;
+  // Accumulator slot s of the wave holds its target-row block blkA(s) (32 rows), slot u its
+  // candidate-row block blkB(u). kRow rotates the slots so that slot 0 is the block whose token
+  // norms this wave sums: target block wn of its row half, candidate block wm of its column
+  // quarter; the eight waves cover each operand's 256 rows once.
+  const int rotA = kRow ? wn : 0, rotB = kRow ? wm : 0;
+  auto blkA = [&](int s_) { return (s_ + rotA) & 3; };
+  auto blkB = [&](int u_) { return (u_ + rotB) & 1; };
+  uint32_t fa[2], fb[2];   // fragment offsets of the two k-steps of a chunk, block 0
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int ra = wm * 128 + (lane & 31), rb = wn * 64 + (lane & 31);
     fa[ks] = (uint32_t)ra * RB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(ra)) << 4);
     fb[ks] = (uint32_t)rb * RB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(rb)) << 4);
   }
+  // Fragment offset of slot s at k-step ks. The rotated offsets are rebuilt at each read (the
+  // base laundered through an empty asm): held, they would take 8 more long-lived registers.
+  auto offA = [&](int ks, int s_) {
+    uint32_t o = fa[ks];
+    if (kRow) asm volatile("" : "+v"(o));
+    return o + (uint32_t)blkA(s_) * 32 * RB;
+  };
+  auto offB = [&](int ks, int u_) {
+    uint32_t o = fb[ks];
+    if (kRow) asm volatile("" : "+v"(o));
+    return o + (uint32_t)blkB(u_) * 32 * RB;
+  };
 
+  // The pair decode runs on the vector unit (double-precision square root); its results are
+  // wave-uniform and are moved to scalar registers, so that everything derived from them (block
+  // offsets, limits, the descriptor base) stays out of the vector register file.
   auto tile_unit = [&](int64_t tl) {
     Unit u;
     const int64_t L = xs + tl;
     u.b = L / a.pairs;
-    decode_pair((int)(L % a.pairs), a.n_s, u.i, u.j);
+    int i, j;
+    decode_pair((int)(L % a.pairs), a.n_s, i, j);
+    u.i = uniform(i);
+    u.j = uniform(j);
     u.ua = 0;
     u.ub = 0;
     return u;
   };
 
-  // Copy addressing: a descriptor over the unit's sequence and the byte offsets of its two
-  // blocks in chunk 0; chunk kc is kc * S * 64 bytes further.
-  const uint16_t* xbase = a.xp;   // the copy unit's sequence
+  // Copy addressing: a descriptor over the unit's sequence, the byte offsets of its two blocks'
+  // first rows in chunk 0, the bytes from one token row to the next (rowB) and from one chunk to
+  // the next (chunkB). Packed: rows are 64 bytes apart inside a chunk plane of S rows; kRow:
+  // rows are ld * 2 bytes apart and a chunk is the next 64 bytes of the row.
+  const uint16_t* xbase = a.x;   // the copy unit's sequence
   uint32_t xbytes = 0;
-  int limA = 0, limB = 0;      // valid (non-padding) rows of the unit's blocks
+  int limA = 0, limB = 0;        // valid (non-padding) rows of the unit's blocks
   uint32_t pbA = 0, pbB = 0;
+  const uint32_t rowB = kRow ? (uint32_t)(a.ld * 2) : (uint32_t)RB;
+  const uint32_t chunkB = kRow ? (uint32_t)RB : (uint32_t)a.S * RB;
   auto set_unit = [&](const Unit& u) {
-    const int64_t seq = (int64_t)a.n_s * a.S * a.d;
-    xbase = a.xp + u.b * seq;
+    const int64_t seq = kRow ? a.N * a.ld : (int64_t)a.n_s * a.nk * a.S * KH;
+    xbase = a.x + u.b * seq;
     xbytes = (uint32_t)(seq * 2);
     limA = (int)min((int64_t)min(a.S - u.ua * T, T), a.N - ((int64_t)u.i * a.S + u.ua * T));
     limB = (int)min((int64_t)min(a.S - u.ub * T, T), a.N - ((int64_t)u.j * a.S + u.ub * T));
-    pbA = (uint32_t)((int64_t)u.i * a.S * a.d * 2 + u.ua * T * RB);
-    pbB = (uint32_t)((int64_t)u.j * a.S * a.d * 2 + u.ub * T * RB);
+    if (kRow) {
+      pbA = (uint32_t)(((int64_t)u.i * a.S + u.ua * T) * rowB);
+      pbB = (uint32_t)(((int64_t)u.j * a.S + u.ub * T) * rowB);
+    } else {
+      pbA = (uint32_t)((int64_t)u.i * a.nk * a.S * RB + u.ua * T * RB);
+      pbB = (uint32_t)((int64_t)u.j * a.nk * a.S * RB + u.ub * T * RB);
+    }
+  };
+  // Lane l of a copy lands at LDS row r0 + (l >> 2), position l & 3, so it fetches the logical
+  // 16-byte piece pc = (l & 3) ^ sw4(row) of its row: features 8 pc .. 8 pc + 7 of the chunk.
+  // kRow: an LDS row past the block's valid rows is filled from the block's last valid row, so
+  // that padding rows repeat a real token (neither maximum changes; the sums skip them) and no
+  // row t >= N is read; with d % 32 != 0 (kTail) the pieces past d load zeros. Lane terms are
+  // recomputed per copy (laundered through an empty asm so they are not hoisted into long-lived
+  // registers).
+  auto src_off = [&](uint32_t pb, int lim, int r0, int sub, int pc) {
+    const int r = kRow ? min(r0 + sub, lim - 1) : r0 + sub;
+    return pb + (uint32_t)r * rowB + 16u * (uint32_t)pc;
+  };
+  auto lane_terms = [&](int& sub, int& pc) {
+    sub = lane >> 2;
+    asm volatile("" : "+v"(sub));
+    pc = (lane & 3) ^ ((sub >> 2) & 3);
+  };
+  auto live = [&](int kc, int pc, bool valid) {
+    return kTail ? (valid && 8 * pc < a.d - kc * KH) : valid;
   };
   // Chunk kc of the current copy unit into stage st: wave w copies rows [32w, 32w + 32) of both
-  // blocks, 16 rows (1 KiB) per instruction, 4 instructions. Lane l lands at LDS row l >> 2,
-  // position l & 3, so it fetches the logical piece (l & 3) ^ sw4(row). Lane terms are
-  // recomputed per copy (laundered through an empty asm so they are not hoisted into long-lived
-  // registers). With valid == false every lane loads zeros.
+  // blocks, 16 rows per instruction, 4 instructions. With valid == false every lane loads zeros.
   auto dma = [&](int kc, uint8_t* st, bool valid) {
-    int sub = lane >> 2;
-    asm volatile("" : "+v"(sub));
-    const uint32_t kb = (uint32_t)kc * (uint32_t)a.S * RB;
-    const uint32_t c = (uint32_t)sub * RB + 16u * (uint32_t)((lane & 3) ^ ((sub >> 2) & 3));
-    const uint32_t laneA = pbA + c, laneB = pbB + c;
+    int sub, pc;
+    lane_terms(sub, pc);
+    const bool ok = live(kc, pc, valid);
+    const uint32_t kb = (uint32_t)kc * chunkB;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int r0 = wave * 32 + n * 16;
       const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
-      dma16(xr, st + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
-      dma16(xr, st + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
+      dma16(xr, st + r0 * RB, ok ? src_off(pbA, limA, r0, sub, pc) : OOB, kb);
+      dma16(xr, st + T * RB + r0 * RB, ok ? src_off(pbB, limB, r0, sub, pc) : OOB, kb);
     }
   };
 
   f32x16 acc[4][2];
-  // Fragments of k-step 0 (ra0, rb0) and 1 (ra1, rb1) of the chunk being multiplied.
+  // Fragments of k-step 0 (ra0, rb0) and 1 (ra1, rb1) of the chunk being multiplied, by slot.
   uint4 ra0[4], rb0[2], ra1[4], rb1[2];
   auto fetch0 = [&](const uint8_t* st) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) ra0[mb] = lds_read16(st, fa[0] + mb * 32 * RB);
+    for (int s_ = 0; s_ < 4; ++s_) ra0[s_] = lds_read16(st, offA(0, s_));
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) rb0[nb] = lds_read16(st + T * RB, fb[0] + nb * 32 * RB);
+    for (int u_ = 0; u_ < 2; ++u_) rb0[u_] = lds_read16(st + T * RB, offB(0, u_));
   };
   auto fetch1 = [&](const uint8_t* st) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) ra1[mb] = lds_read16(st, fa[1] + mb * 32 * RB);
+    for (int s_ = 0; s_ < 4; ++s_) ra1[s_] = lds_read16(st, offA(1, s_));
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) rb1[nb] = lds_read16(st + T * RB, fb[1] + nb * 32 * RB);
+    for (int u_ = 0; u_ < 2; ++u_) rb1[u_] = lds_read16(st + T * RB, offB(1, u_));
   };
+  // kRow reads each k-step's fragments in two halves, target blocks 0-1 with the candidate
+  // blocks, then target blocks 2-3 once the previous k-step's MFMAs that read those registers
+  // are issued: at most 32 fragment registers are live instead of 40, which leaves room for the
+  // norm sums and the scale registers of the epilogue.
+  auto fetch_lo = [&](uint4 (&ra)[4], uint4 (&rb)[2], int ks, const uint8_t* st) {
+#pragma unroll
+    for (int s_ = 0; s_ < 2; ++s_) ra[s_] = lds_read16(st, offA(ks, s_));
+#pragma unroll
+    for (int u_ = 0; u_ < 2; ++u_) rb[u_] = lds_read16(st + T * RB, offB(ks, u_));
+  };
+  auto fetch_hi = [&](uint4 (&ra)[4], int ks, const uint8_t* st) {
+#pragma unroll
+    for (int s_ = 2; s_ < 4; ++s_) ra[s_] = lds_read16(st, offA(ks, s_));
+  };
+  // kRow: sums of squares of this wave's norm rows (slot 0 of each operand). Per chunk each lane
+  // sums the 8 features of its k-half over both k-steps into tA / tB, then adds that to its
+  // running sum in LDS, s_ssA[half][row] (each lane owns one entry: no atomics). The read is
+  // issued before the chunk's wait, which completes it, and the write follows the wait: nothing
+  // is carried in registers across chunks. The epilogue adds the two halves and clears them.
+  float tA = 0.f, tB = 0.f;
+  auto ss_slot = [&]() {
+    int o = (lane >> 5) * T + (lane & 31);
+    asm volatile("" : "+v"(o));
+    return o;
+  };
+  if (kRow) {
+    const int o = ss_slot();
+    s_ssA[o + wm * 128 + wn * 32] = 0.f;
+    s_ssB[o + wn * 64 + wm * 32] = 0.f;
+  }
   // One chunk from stage st whose k-step-0 fragments are already in ra0 / rb0; the 4 copies of
   // chunk kc into dst go between the MFMA groups. With next != nullptr the next chunk's wait
   // and barrier come before the last MFMA group, and its k-step-0 fragments are read under it.
@@ -195,25 +290,32 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   // inline constant) instead of reading them, so that nothing has to clear them.
   const f32x16 zero16 = {};
   auto compute_pipe = [&](auto FIRST, const uint8_t* st, int kc, uint8_t* dst, bool valid, const uint8_t* next) {
-    int sub = lane >> 2;
-    asm volatile("" : "+v"(sub));
-    const uint32_t kb = (uint32_t)kc * (uint32_t)a.S * RB;
-    const uint32_t c = (uint32_t)sub * RB + 16u * (uint32_t)((lane & 3) ^ ((sub >> 2) & 3));
-    const uint32_t laneA = pbA + c, laneB = pbB + c;
+    int sub, pc;
+    lane_terms(sub, pc);
+    const bool ok = live(kc, pc, valid);
+    const uint32_t kb = (uint32_t)kc * chunkB;
     auto copy = [&](int ks, int h) {
       const int r0 = wave * 32 + ks * 16;
       // the descriptor is rebuilt from the first lane at each copy: carried across the loop it
       // is taken as per-lane, and every copy through it became a loop over distinct values
       const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
-      if (h == 0) dma16(xr, dst + r0 * RB, valid ? laneA + (uint32_t)r0 * RB : OOB, kb);
-      else dma16(xr, dst + T * RB + r0 * RB, valid ? laneB + (uint32_t)r0 * RB : OOB, kb);
+      if (h == 0) dma16(xr, dst + r0 * RB, ok ? src_off(pbA, limA, r0, sub, pc) : OOB, kb);
+      else dma16(xr, dst + T * RB + r0 * RB, ok ? src_off(pbB, limB, r0, sub, pc) : OOB, kb);
     };
+    if (kRow) {   // before the MFMAs, which stay the fragments' last readers
+      tA = sumsq8(ra0[0], 0.f);
+      tB = sumsq8(rb0[0], 0.f);
+    }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
-    fetch1(st);
+    if (kRow) {
+      fetch_lo(ra1, rb1, 1, st);
+    } else {
+      fetch1(st);
+    }
     copy(0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -221,8 +323,13 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         acc[mb][nb] = mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
+    if (kRow) fetch_hi(ra1, 1, st);
     copy(0, 1);
     __builtin_amdgcn_sched_barrier(0);
+    if (kRow) {
+      tA = sumsq8(ra1[0], tA);
+      tB = sumsq8(rb1[0], tB);
+    }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -230,14 +337,32 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     copy(1, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (next) {
+      float oA = 0.f, oB = 0.f;
+      int so = 0;
+      if (kRow) {
+        so = ss_slot();
+        oA = s_ssA[so + wm * 128 + wn * 32];
+        oB = s_ssB[so + wn * 64 + wm * 32];
+      }
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
       WAIT_KEEP(7);
-      fetch0(next);
+      if (kRow) {
+        s_ssA[so + wm * 128 + wn * 32] = oA + tA;
+        s_ssB[so + wn * 64 + wm * 32] = oB + tB;
+        fetch_lo(ra0, rb0, 0, next);
+      } else {
+        fetch0(next);
+      }
+    } else if (kRow) {
+      const int so = ss_slot();
+      s_ssA[so + wm * 128 + wn * 32] += tA;
+      s_ssB[so + wn * 64 + wm * 32] += tB;
     }
 #pragma unroll
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
+    if (kRow && next) fetch_hi(ra0, 0, next);
     copy(1, 1);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -318,8 +443,24 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     const bool full = cLimA == T && cLimB == T;   // no padding token in this unit
     // (two stores to named arrays: a store through a selected pointer would make the compiler
     // wait for the copies in flight)
-    if (is_row) s_biA[own] = valid ? 0.f : -INFINITY;
-    else s_biB[own] = valid ? 0.f : -INFINITY;
+    if (!kRow) {
+      if (is_row) s_biA[own] = valid ? 0.f : -INFINITY;
+      else s_biB[own] = valid ? 0.f : -INFINITY;
+    }
+    if (kRow) {
+      // the token norms of this wave's rows from its own LDS sums (the two k-halves); the sums
+      // restart at zero for the next unit
+      if (lane < 32) {
+        const int ia = wm * 128 + wn * 32 + lane, ib = wn * 64 + wm * 32 + lane;
+        const float sa = s_ssA[ia] + s_ssA[T + ia], sb = s_ssB[ib] + s_ssB[T + ib];
+        s_ssA[ia] = 0.f;
+        s_ssA[T + ia] = 0.f;
+        s_ssB[ib] = 0.f;
+        s_ssB[T + ib] = 0.f;
+        s_rnA[ia] = sa > 0.f ? 1.0f / sqrtf(sa) : 0.f;
+        s_rnB[ib] = sb > 0.f ? 1.0f / sqrtf(sb) : 0.f;
+      }
+    }
     lds_sync();   // also: every wave is done reading stage 3
 
     // One pass over the accumulators, both directions:
@@ -328,9 +469,15 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     // A two-step transposing max across the 4 lanes of a quad leaves lane q with row e = q of
     // each group of 4 rows, so each lane stores one value per group.
     const int q = lane & 3, par = lane & 1, hi2 = (lane >> 1) & 1;
-    float* const wscr = reinterpret_cast<float*>(st3) + wave * (128 * 8) + ((lane & 31) >> 2);
+    // per-lane scratch slot; kRow rebuilds it at each store (rotated block offsets, held for
+    // every slot, would be long-lived registers)
+    auto wscr_at = [&](int idx) {
+      int o = wave * (128 * 8) + ((lane & 31) >> 2);
+      if (kRow) asm volatile("" : "+v"(o));
+      return reinterpret_cast<float*>(st3) + o + idx;
+    };
     float cm[2] = {-INFINITY, -INFINITY};
-    auto reduce_store = [&](int mb, int g, const float (&m)[4]) {
+    auto reduce_store = [&](int ba, int g, const float (&m)[4]) {
       // step 1, lanes l and l ^ 1: the even lane keeps rows e = 0, 2, the odd lane e = 1, 3
       const float s0 = par ? m[0] : m[1], k0 = par ? m[1] : m[0];
       const float s1 = par ? m[2] : m[3], k1 = par ? m[3] : m[2];
@@ -339,11 +486,51 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       // step 2, lanes l and l ^ 2: keep row e = par (hi2 == 0) or e = par + 2 (hi2 == 1)
       const float s2 = hi2 ? t0 : t1, k2 = hi2 ? t1 : t0;
       const float f = fmaxf(k2, __builtin_amdgcn_update_dpp(0.f, s2, 0x4E, 0xF, 0xF, false));
-      wscr[(mb * 32 + g * 8 + (lane >> 5) * 4 + q) * 8] = f;
+      *wscr_at((ba * 32 + g * 8 + (lane >> 5) * 4 + q) * 8) = f;
     };
-    // Accumulator element v of block (mb, nb) in lane l: row mb*32 + 8(v >> 2) + 4(l >> 5) + (v & 3)
-    // of the wave's rows, column nb*32 + (l & 31) of its columns.
-    if (full) {
+    // Accumulator element v of slot (s, u) in lane l: row blkA(s)*32 + 8(v >> 2) + 4(l >> 5) + (v & 3)
+    // of the wave's rows, column blkB(u)*32 + (l & 31) of its columns.
+    if (kRow) {
+      // Padding rows and columns repeat a valid token, so no mask is needed. Column direction:
+      // the accumulators are scaled in place by rn_t, C_tu rn_t, and maximised over this wave's
+      // rows; row direction: the scaled values times rn_u are the cosines, maximised over this
+      // wave's columns.
+#pragma unroll
+      for (int s_ = 0; s_ < 4; ++s_) {
+        int lo = (lane >> 5) * 4;
+        asm volatile("" : "+v"(lo));
+        const float* rnA_lane = s_rnA + wm * 128 + blkA(s_) * 32 + lo;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 rs = *reinterpret_cast<const float4*>(rnA_lane + g * 8);
+          const float rs4[4] = {rs.x, rs.y, rs.z, rs.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int u_ = 0; u_ < 2; ++u_) {
+              acc[s_][u_][g * 4 + e] *= rs4[e];
+              cm[u_] = fmaxf(cm[u_], acc[s_][u_][g * 4 + e]);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float csc[2];
+#pragma unroll
+      for (int u_ = 0; u_ < 2; ++u_) csc[u_] = s_rnB[wn * 64 + blkB(u_) * 32 + (lane & 31)];
+#pragma unroll
+      for (int s_ = 0; s_ < 4; ++s_) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float m[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            m[e] = fmaxf(acc[s_][0][g * 4 + e] * csc[0], acc[s_][1][g * 4 + e] * csc[1]);
+          reduce_store(blkA(s_), g, m);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (full) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -386,9 +573,9 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       }
     }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float m = fmaxf(cm[nb], __shfl_xor(cm[nb], 32));
-      if (lane < 32) s_cm[wm][wn * 64 + nb * 32 + lane] = m;
+    for (int u_ = 0; u_ < 2; ++u_) {
+      const float m = fmaxf(cm[u_], __shfl_xor(cm[u_], 32));
+      if (lane < 32) s_cm[wm][wn * 64 + blkB(u_) * 32 + lane] = m;
     }
     lds_sync();
     if (is_row) {
@@ -411,7 +598,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       float cmv = fmaxf(s_cm[0][own], s_cm[1][own]);
       if (!first_ua) cmv = fmaxf(cmv, s_colmax[cur.ub * T + own]);
       if (!last_ua) s_colmax[cur.ub * T + own] = cmv;
-      else if (valid) part += cmv;
+      else if (valid) part += kRow ? cmv * s_rnB[own] : cmv;
     }
 
     if (last_ua && last_ub) {
@@ -443,26 +630,46 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   wait_vmem();    // the zero-filled copies issued past the last unit land before the exit
 }
 
-}  // namespace
-
-hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
-                              hipStream_t stream) {
+MaxsimParams params(const uint16_t* x, int64_t ld, int64_t B, int64_t N, int d, int S, float* scores) {
   MaxsimParams p;
-  p.xp = xp;
+  p.x = x;
+  p.ld = ld;
   p.N = N;
   p.d = d;
   p.S = S;
   p.n_s = (int)((N + S - 1) / S);
+  p.nk = (d + KH - 1) / KH;
   p.q = (S + T - 1) / T;
   p.pairs = (int)((int64_t)p.n_s * (p.n_s - 1) / 2);
   p.tiles = B * (int64_t)p.pairs;
   p.scores = scores;
+  return p;
+}
+
+int64_t grid_for(int64_t tiles) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  const int64_t grid = p.tiles < cus ? p.tiles : cus;
-  hipLaunchKernelGGL(maxsim_bf16_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
+  return tiles < cus ? tiles : cus;
+}
+
+}  // namespace
+
+hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
+                              hipStream_t stream) {
+  const MaxsimParams p = params(xp, 0, B, N, d, S, scores);
+  hipLaunchKernelGGL((maxsim_bf16_kernel<false, false>), dim3((unsigned)grid_for(p.tiles)), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_maxsim_rows_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld, int S, float* scores,
+                                   hipStream_t stream) {
+  const MaxsimParams p = params(x, ld, B, N, d, S, scores);
+  if (d % KH)
+    hipLaunchKernelGGL((maxsim_bf16_kernel<true, true>), dim3((unsigned)grid_for(p.tiles)), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((maxsim_bf16_kernel<true, false>), dim3((unsigned)grid_for(p.tiles)), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

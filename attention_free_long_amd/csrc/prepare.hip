@@ -4,9 +4,10 @@
 // zero-padded). One pass over X; the sum of squares is accumulated in fp32.
 //
 // Output layouts (the ranker's workspace):
-//   bf16: [B][n_s][d / 32][S][32] -- for each split, chunk-planes of 32 features holding S
-//         token rows of 64 bytes, so that a block of consecutive tokens of one chunk is one
-//         contiguous run of memory. Values are N(x) rounded to bf16 (round to nearest even).
+//   bf16: [B][n_s][nk][S][32], nk = ceil(d / 32) -- for each split, chunk-planes of 32
+//         features holding S token rows of 64 bytes, so that a block of consecutive tokens of
+//         one chunk is one contiguous run of memory. Values are N(x) rounded to bf16 (round to
+//         nearest even); the features d .. 32 nk - 1 of the last plane are zero.
 //   fp32: [B][n_s * S][d] row-major, N(x) in fp32.
 #include "avey_common.h"
 #include "launch.h"
@@ -43,7 +44,7 @@ __global__ void __launch_bounds__(256) prepare_bf16_kernel(const uint16_t* __res
   const float rn = s > 0.f ? 1.0f / sqrtf(s) : 0.f;
   if (!live) return;
   const int j = (int)(tp / S), slot = (int)(tp % S);
-  const int nkc = d / 32;
+  const int nkc = (d + 31) / 32, dp = nkc * 32;   // features padded with zeros to whole chunks
   uint16_t* dst = xp + ((b * n_s + j) * (int64_t)nkc * S + slot) * 32;
   auto put = [&](int c, uint4 u) {
     uint4 o;
@@ -57,10 +58,10 @@ __global__ void __launch_bounds__(256) prepare_bf16_kernel(const uint16_t* __res
 #pragma unroll
   for (int p = 0; p < RP; ++p) {
     const int c = lane16 * 8 + p * 128;
-    if (c < d) put(c, v[p]);
+    if (c < dp) put(c, v[p]);   // zero past d
   }
-  for (int c = lane16 * 8 + RP * 128; c < d; c += 128)
-    put(c, valid ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0));
+  for (int c = lane16 * 8 + RP * 128; c < dp; c += 128)
+    put(c, (valid && c < d) ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0));
 }
 
 __global__ void __launch_bounds__(256) prepare_f32_kernel(const float* __restrict__ x, int64_t rows_p, int64_t N,

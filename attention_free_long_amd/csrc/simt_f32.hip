@@ -60,6 +60,48 @@ __global__ void __launch_bounds__(256) maxsim_f32_kernel(const float* __restrict
   if (threadIdx.x == 0) *out = tot;
 }
 
+// One workgroup per ordered pair (b, i, j), straight from X (row stride ld): the inverse norms of
+// the candidate split's valid tokens go to LDS first, then each thread takes target tokens t and
+// sums rn_t max_u (x_t . x_u) rn_u, the largest cosine over the candidate's valid tokens.
+__global__ void __launch_bounds__(256) maxsim_rows_f32_kernel(const float* __restrict__ x, int64_t N, int d,
+                                                               int64_t ld, int S, int n_s,
+                                                               float* __restrict__ scores) {
+  __shared__ float rnj[512];
+  __shared__ float red[4];
+  const int64_t pr = blockIdx.x;
+  const int j = (int)(pr % n_s);
+  const int i = (int)((pr / n_s) % n_s);
+  const int64_t b = pr / ((int64_t)n_s * n_s);
+  float* out = scores + pr;
+  if (i == j) {
+    if (threadIdx.x == 0) *out = -INFINITY;
+    return;
+  }
+  const float* xb = x + b * N * ld;
+  const int64_t ti0 = (int64_t)i * S, tj0 = (int64_t)j * S;
+  const int ni = (int)min((int64_t)S, N - ti0), nj = (int)min((int64_t)S, N - tj0);
+  for (int u = threadIdx.x; u < nj; u += 256) {
+    const float n = norm_f32(xb + (tj0 + u) * ld, d);
+    rnj[u] = n > 0.f ? 1.0f / n : 0.f;
+  }
+  __syncthreads();
+  float part = 0.f;
+  for (int t = threadIdx.x; t < ni; t += 256) {
+    const float* xt = xb + (ti0 + t) * ld;
+    const float nt = norm_f32(xt, d);
+    float best = -INFINITY;
+    for (int u = 0; u < nj; ++u) {
+      const float* xu = xb + (tj0 + u) * ld;
+      float dot = 0.f;
+      for (int c = 0; c < d; ++c) dot = fmaf(xt[c], xu[c], dot);
+      best = fmaxf(best, dot * rnj[u]);
+    }
+    part += best * (nt > 0.f ? 1.0f / nt : 0.f);
+  }
+  const float tot = block_sum(part, red);
+  if (threadIdx.x == 0) *out = tot;
+}
+
 // One thread per output element (b, token, feature).
 __global__ void __launch_bounds__(256) compress_f32_kernel(const float* __restrict__ x, int64_t B, int64_t N, int d,
                                                             int64_t ld_x, int S, int k, int n_s,
@@ -186,6 +228,14 @@ hipError_t launch_maxsim_f32(const float* xn, int64_t B, int64_t N, int d, int S
   const int n_s = (int)((N + S - 1) / S);
   const int64_t grid = B * n_s * n_s;
   hipLaunchKernelGGL(maxsim_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, xn, N, d, S, n_s, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_maxsim_rows_f32(const float* x, int64_t B, int64_t N, int d, int64_t ld, int S, float* scores,
+                                  hipStream_t stream) {
+  const int n_s = (int)((N + S - 1) / S);
+  const int64_t grid = B * n_s * n_s;
+  hipLaunchKernelGGL(maxsim_rows_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, N, d, ld, S, n_s, scores);
   return hipGetLastError();
 }
 

@@ -93,8 +93,8 @@ def pipeline_roofline(cfg, value: float, peak_tflops: float) -> dict:
     compress, dynamic layer; top-k's few KiB are left out): tokens/s the step would reach if every
     kernel ran at its bound, max(FLOP / MFMA peak, bytes / HBM peak) per kernel, and the two
     single-resource figures B N peak / sum(FLOP) and B N BW / sum(bytes). The normalised operand
-    copy of the explicit-workspace ranker is an implementation choice, not work of the method: it
-    is not counted."""
+    copy of the explicit-workspace ranker path is an implementation choice, not work of the method:
+    it is not counted."""
     work = algorithmic(cfg)
     names = ("maxsim", "compress", "dyn")
     flop = sum(work[n]["flop"] for n in names)
@@ -323,9 +323,11 @@ def time_workload(A, cfg, inp, steps: int, warmup: int, peak: float):
     scores = torch.empty((B, n_s, n_s), device="cuda", dtype=torch.float32)
     idx = torch.empty((B, n_s, k), device="cuda", dtype=torch.int32)
     w = torch.empty((B, n_s, k), device="cuda", dtype=torch.float32)
-    ws = A.rank_workspace(x, S)
     xhat = torch.empty((B, N, cfg.d), device="cuda", dtype=dt)
     out = torch.empty((B, N, cfg.m_t), device="cuda", dtype=dt)
+    # The ranker through its explicit-workspace path (the faster of the two; the workspace-free
+    # avey_split_rank is timed beside it), then gather + compress and the dynamic layer
+    ws = A.rank_workspace(x, S)
     names = ("prepare", "maxsim", "topk", "compress", "dyn")
     calls = (
         lambda: A.avey_maxsim_prepare(x, S, ws),
@@ -382,7 +384,32 @@ def time_workload(A, cfg, inp, steps: int, warmup: int, peak: float):
     }
     res["compress_cold"]["mfma_frac"] = round(work["compress"]["flop"] / (res["compress_cold"]["median_us"] * 1e-6)
                                               / 1e12 / peak, 4)
+    res["rank_workspace_free"] = time_workspace_free(A, x, S, k, work, steps, peak)
     return res, (x, z_tail, work)
+
+
+def time_workspace_free(A, x, S: int, k: int, work, steps: int, peak: float):
+    """The workspace-free ranker, avey_split_rank (MaxSim straight from x with the token norms on
+    chip, then top-k), beside the step's explicit-workspace one: one HIP-event interval per call
+    on the launch stream."""
+    import numpy as np
+    import torch
+    B, N, _ = x.shape
+    n_s = -(-N // S)
+    scores = torch.empty((B, n_s, n_s), device="cuda", dtype=torch.float32)
+    idx = torch.empty((B, n_s, k), device="cuda", dtype=torch.int32)
+    w = torch.empty((B, n_s, k), device="cuda", dtype=torch.float32)
+    for _ in range(3):
+        A.avey_split_rank(x, S, k, scores, idx, w)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        A.avey_split_rank(x, S, k, scores, idx, w)
+        e[1].record()
+    torch.cuda.synchronize()
+    t = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    return {"split_rank_avg_us": round(t * 1e6, 3),
+            "maxsim_frac_upper_bound": round(work["maxsim"]["flop"] / t / 1e12 / peak, 4), "launches": steps}
 
 
 def workload_name(cfg) -> str:
@@ -464,7 +491,7 @@ def main(argv=None):
         "maxsim_mfma_util_pct": round(100 * achieved / peak, 2),
     }
     for key in ("compress_hbm_frac", "compress_mfma_frac", "dyn_hbm_frac", "dyn_mfma_frac", "kernels",
-                "compress_cold", "gap_histogram"):
+                "compress_cold", "rank_workspace_free", "gap_histogram"):
         result[key] = r[key]
     if cfg.dtype == "bf16":
         mp_ = measured_peaks(A)
@@ -487,6 +514,7 @@ def main(argv=None):
             "maxsim": {"achieved": round(e["maxsim_achieved_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(e["maxsim_achieved_tflops"] / PEAK_BF16_TFLOPS, 4)},
             "compress_cold": e["compress_cold"],
+            "rank_workspace_free": e["rank_workspace_free"],
             "compress_hbm_frac": e["compress_hbm_frac"],
             "dyn_hbm_frac": e["dyn_hbm_frac"], "dyn_mfma_frac": e["dyn_mfma_frac"],
             "pipeline_roofline": e["pipeline_roofline"],

@@ -31,10 +31,11 @@
  *   - Outputs must not overlap inputs.
  *   - Empty work (B == 0 or N == 0) returns AVEY_OK and enqueues nothing; pointers may then
  *     be NULL.
- *   - Shape limits: 1 <= S <= 512. For AVEY_BF16 additionally S % 64 == 0, every feature
- *     width (d, m_t) is a multiple of 64, every ld is a multiple of 8 and every tensor pointer
- *     is 16-byte aligned; for AVEY_F32 every tensor pointer is 4-byte aligned.
- *     Violations return AVEY_ERR_SHAPE, AVEY_ERR_ALIGN or AVEY_ERR_UNSUPPORTED.
+ *   - Shape limits: 1 <= S <= 512. For AVEY_BF16 additionally every ld is a multiple of 8 and
+ *     every tensor pointer is 16-byte aligned; the ranker (avey_split_rank, avey_maxsim and the
+ *     workspace path) takes S % 16 == 0 and d % 8 == 0, the other entry points S % 64 == 0 and
+ *     feature widths (d, m_t, m) that are multiples of 64. For AVEY_F32 every tensor pointer is
+ *     4-byte aligned. Violations return AVEY_ERR_SHAPE, AVEY_ERR_ALIGN or AVEY_ERR_UNSUPPORTED.
  */
 #ifndef AVEY_H
 #define AVEY_H
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define AVEY_ABI_VERSION 1
+#define AVEY_ABI_VERSION 2
 
 typedef enum { AVEY_F32 = 0, AVEY_BF16 = 1 } avey_dtype;
 
@@ -66,15 +67,37 @@ int32_t avey_abi_version(void);
 const char* avey_status_str(int32_t status);
 
 /*
- * Ranker workspace. The ranker first writes a normalised, zero-padded copy of X -- the
- * "L2-normalised tiles" its MaxSim contraction reads -- into caller-provided device memory:
- * n_t = N(x_t) = x_t / |x_t| (sum of squares in fp32; N(0) = 0) for t < N, zero rows for the
- * padding tokens of the last split ([notes] 关键设计 2; 整体框架). Its layout is internal to
- * the library (bf16: split-packed chunk planes of 32 features; fp32: row-major n_s * S rows).
+ * avey_maxsim -- all-pairs split relevance ([summary] section 3: the ranker scores every split
+ * against the target split with MaxSim; [notes] 整体框架), straight from x, with no workspace.
+ *
+ *   scores[b, i, j] = sum over valid tokens t of split i of
+ *                     max over valid tokens u of split j of cos(x_t, x_u),     for i != j
+ *   scores[b, i, i] = -INFINITY
+ * cos(x_t, x_u) = (x_t . x_u) / (|x_t| |x_u|), and 0 when either token is zero ([notes] 关键设计
+ * 2: N(.) divides each token by its L2 norm). Padding tokens take part neither in the sum nor in
+ * the max; rows t >= N of x are never read. For AVEY_BF16 the dot products and squared norms
+ * accumulate in fp32 from the bf16 values; x must be finite: with a NaN or infinite token the
+ * scores are unspecified.
+ *
+ *   x       [B, N, d] row stride ld_x, dtype dt (input)
+ *   scores  [B, n_s, n_s] float32, contiguous (output)
+ * Requires n_s >= 2. For AVEY_BF16, (N + 512) * ld_x < 2^30. MaxSim is not symmetric; both
+ * directions of each split pair come from one pass over the pair.
+ */
+avey_status avey_maxsim(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d, int64_t ld_x,
+                        int32_t S, float* scores, void* stream);
+
+/*
+ * Explicit-workspace scoring: the same scores as avey_maxsim from a normalised, zero-padded copy
+ * of X in caller-provided device memory: n_t = N(x_t) = x_t / |x_t| (sum of squares in fp32;
+ * N(0) = 0) for t < N, zero rows for the padding tokens of the last split ([notes] 关键设计 2;
+ * 整体框架). Its layout is internal to the library (bf16: split-packed chunk planes of 32
+ * features, features padded with zeros to a multiple of 32; fp32: row-major n_s * S rows).
  *
  * avey_rank_workspace_bytes -- size in bytes of that workspace for (dt, B, N, d, S):
- * B * n_s * S * d * (2 for AVEY_BF16, 4 for AVEY_F32), 0 for empty work, or a negative
- * avey_status if the shape is rejected (the same checks as avey_maxsim_prepare).
+ * B * n_s * S * d' * (2 for AVEY_BF16, 4 for AVEY_F32) with d' = d rounded up to a multiple of 32
+ * for AVEY_BF16 (d for AVEY_F32), 0 for empty work, or a negative avey_status if the shape is
+ * rejected (the same checks as avey_maxsim_prepare).
  */
 int64_t avey_rank_workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S);
 
@@ -89,20 +112,13 @@ avey_status avey_maxsim_prepare(const void* x, avey_dtype dt, int64_t B, int64_t
                                 int64_t ld_x, int32_t S, void* workspace, void* stream);
 
 /*
- * avey_maxsim_scores -- all-pairs split relevance ([summary] section 3: the ranker scores
- * every split against the target split with MaxSim; [notes] 整体框架), from a workspace that
- * avey_maxsim_prepare filled (enqueued earlier) for the same (dt, B, N, d, S).
- *
- *   scores[b, i, j] = sum over valid tokens t of split i of
- *                     max over valid tokens u of split j of n_t . n_u,     for i != j
- *   scores[b, i, i] = -INFINITY
- * n_t . n_u is the cosine of x_t and x_u (0 when either is zero). Padding tokens take part
- * neither in the sum nor in the max. Dot products accumulate in fp32. x must be finite: with a
- * NaN or infinite token the scores are unspecified.
+ * avey_maxsim_scores -- the scores of avey_maxsim from a workspace that avey_maxsim_prepare
+ * filled (enqueued earlier) for the same (dt, B, N, d, S). With unit vectors the contraction
+ * holds the cosines themselves: scores[b, i, j] = sum_t max_u n_t . n_u (dot products in fp32 of
+ * the rounded n for AVEY_BF16).
  *
  *   workspace  (input, not modified)
  *   scores     [B, n_s, n_s] float32, contiguous (output)
- * MaxSim is not symmetric; both directions of each split pair come from one pass over the pair.
  */
 avey_status avey_maxsim_scores(const void* workspace, avey_dtype dt, int64_t B, int64_t N,
                                int64_t d, int32_t S, float* scores, void* stream);
@@ -126,14 +142,15 @@ avey_status avey_topk_norm(const float* scores, int64_t B, int64_t n_s, int32_t 
                            int32_t* idx, float* w, void* stream);
 
 /*
- * avey_split_rank -- avey_maxsim_prepare, avey_maxsim_scores and avey_topk_norm on the same
- * stream. Every argument check of the three runs before the first launch.
- *   workspace  avey_rank_workspace_bytes(...) bytes, 16-byte aligned (scratch; overwritten)
- *   outputs scores [B, n_s, n_s], idx [B, n_s, k], w [B, n_s, k] as described above.
+ * avey_split_rank -- the bidirectional ranker: avey_maxsim, then avey_topk_norm, on the same
+ * stream, with no workspace. Every argument check of both runs before the first launch.
+ *   x                [B, N, d] row stride ld_x, dtype dt (input)
+ *   scores, idx, w   [B, n_s, n_s], [B, n_s, k], [B, n_s, k] as described above (outputs)
+ * Requires 1 <= k <= n_s - 1.
  */
 avey_status avey_split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
-                            int64_t ld_x, int32_t S, int32_t k, void* workspace, float* scores,
-                            int32_t* idx, float* w, void* stream);
+                            int64_t ld_x, int32_t S, int32_t k, float* scores, int32_t* idx,
+                            float* w, void* stream);
 
 /*
  * avey_topk_norm_preceding -- the unidirectional ranker's selection ([summary] section 3: the
@@ -148,13 +165,12 @@ avey_status avey_topk_norm_preceding(const float* scores, int64_t B, int64_t n_s
                                      int32_t* idx, float* w, void* stream);
 
 /*
- * avey_split_rank_preceding -- avey_maxsim_prepare, avey_maxsim_scores and
- * avey_topk_norm_preceding on the same stream; arguments as avey_split_rank.
+ * avey_split_rank_preceding -- the unidirectional ranker: avey_maxsim, then
+ * avey_topk_norm_preceding, on the same stream; arguments as avey_split_rank.
  */
 avey_status avey_split_rank_preceding(const void* x, avey_dtype dt, int64_t B, int64_t N,
-                                      int64_t d, int64_t ld_x, int32_t S, int32_t k,
-                                      void* workspace, float* scores, int32_t* idx, float* w,
-                                      void* stream);
+                                      int64_t d, int64_t ld_x, int32_t S, int32_t k, float* scores,
+                                      int32_t* idx, float* w, void* stream);
 
 /*
  * avey_select_compress -- weighted gather and neural compression ([notes] 关键设计 4, eq. 8;

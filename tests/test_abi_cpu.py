@@ -34,7 +34,7 @@ def test_exports_match_header(lib):
     so = ctypes.CDLL(A.LIB_PATH)
     for name in decl:
         assert hasattr(so, name), name
-    assert lib.avey_abi_version() == A.AVEY_ABI_VERSION == 1
+    assert lib.avey_abi_version() == A.AVEY_ABI_VERSION == 2
 
 
 def test_status_strings(lib):
@@ -45,35 +45,53 @@ def test_status_strings(lib):
 
 def test_split_rank_validation(lib):
     f = lib.avey_split_rank
-    # (x, dt, B, N, d, ld, S, k, workspace, scores, idx, w, stream)
-    assert f(P16, 7, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == DTYPE
-    assert f(P16, 1, -1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == SHAPE
-    assert f(P16, 1, 1, 1024, 64, 64, 0, 3, P16, P16, P16, P16, None) == SHAPE
-    assert f(P16, 1, 1, 1024, 64, 64, 1024, 3, P16, P16, P16, P16, None) == SHAPE      # S > 512
-    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None, None) == OK       # B == 0: no work
-    assert f(None, 1, 1, 0, 64, 64, 64, 3, None, None, None, None, None) == OK          # N == 0: no work
-    assert f(None, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == NULL
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, P16, None) == NULL         # no workspace
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, None, P16, P16, None) == NULL
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, P16, None) == SHAPE        # k > n_s - 1
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, P16, None) == SHAPE
-    assert f(P16, 1, 1, 64, 64, 64, 64, 1, P16, P16, P16, P16, None) == SHAPE           # a single split
-    assert f(P16, 1, 1, 1024, 64, 32, 64, 3, P16, P16, P16, P16, None) == SHAPE         # ld < d
-    assert f(P16, 1, 1, 1024, 96, 96, 64, 3, P16, P16, P16, P16, None) == UNSUP         # bf16 d % 64
-    assert f(P16, 1, 1, 1024, 64, 68, 64, 3, P16, P16, P16, P16, None) == ALIGN         # bf16 ld % 8
-    assert f(P4, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, P16, None) == ALIGN          # bf16 x alignment
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P4, P16, P16, P16, None) == ALIGN          # workspace alignment
-    assert f(P16, 1, 1, 1000, 64, 64, 100, 3, P16, P16, P16, P16, None) == UNSUP        # bf16 S % 64
-    assert f(P16, 0, 1, 1000, 64, 64, 64, 3, P16, P16, P16 + 2, P16, None) == ALIGN     # idx alignment
-    assert f(P16, 1, 1, 1 << 25, 64, 64, 256, 3, P16, P16, P16, P16, None) == UNSUP     # > 2^30 elements
+    # (x, dt, B, N, d, ld, S, k, scores, idx, w, stream): no workspace
+    assert f(P16, 7, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == DTYPE
+    assert f(P16, 1, -1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 0, 3, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 64, 64, 1024, 3, P16, P16, P16, None) == SHAPE      # S > 512
+    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None) == OK       # B == 0: no work
+    assert f(None, 1, 1, 0, 64, 64, 64, 3, None, None, None, None) == OK          # N == 0: no work
+    assert f(None, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, None) == NULL        # scores
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, None, P16, None) == NULL        # idx
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, None, None) == NULL        # w
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, None) == SHAPE       # k > n_s - 1
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 64, 64, 64, 64, 1, P16, P16, P16, None) == SHAPE          # a single split
+    assert f(P16, 1, 1, 1024, 64, 32, 64, 3, P16, P16, P16, None) == SHAPE        # ld < d
+    assert f(P16, 1, 1, 1024, 100, 104, 64, 3, P16, P16, P16, None) == UNSUP      # bf16 d % 8
+    assert f(P16, 1, 1, 1000, 64, 64, 100, 3, P16, P16, P16, None) == UNSUP       # bf16 S % 16
+    assert f(P16, 1, 1, 1024, 64, 68, 64, 3, P16, P16, P16, None) == ALIGN        # bf16 ld % 8
+    assert f(P4, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, None) == ALIGN         # bf16 x alignment
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16 + 2, P16, P16, None) == ALIGN    # scores alignment
+    assert f(P16, 0, 1, 1000, 64, 64, 64, 3, P16, P16 + 2, P16, None) == ALIGN    # idx alignment
+    assert f(P16, 1, 1, 1 << 25, 64, 64, 256, 3, P16, P16, P16, None) == UNSUP    # > 2^30 elements
+    assert f(P16, 1, 1, 1024, 64, 1 << 20, 64, 3, P16, P16, P16, None) == UNSUP   # (N + 512) ld >= 2^30
+
+
+def test_maxsim_validation(lib):
+    f = lib.avey_maxsim
+    # (x, dt, B, N, d, ld, S, scores, stream)
+    assert f(None, 1, 0, 1024, 64, 64, 64, None, None) == OK
+    assert f(None, 1, 1, 1024, 64, 64, 64, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, None, None) == NULL
+    assert f(P16, 1, 1, 64, 64, 64, 64, P16, None) == SHAPE                # a single split
+    assert f(P16, 1, 1, 1024, 64, 64, 40, P16, None) == UNSUP              # bf16 S % 16
+    assert f(P16, 1, 1, 1024, 12, 16, 64, P16, None) == UNSUP              # bf16 d % 8
+    assert f(P16, 0, 1, 1024, 12, 12, 40, P16 + 1, None) == ALIGN          # f32: any S, d; scores 4-aligned
+    assert f(P16, 9, 1, 1024, 64, 64, 64, P16, None) == DTYPE
 
 
 def test_workspace_prepare_and_scores_validation(lib):
     n = lib.avey_rank_workspace_bytes
     assert n(1, 2, 32768, 768, 256) == 2 * 128 * 256 * 768 * 2
-    assert n(0, 1, 1000, 64, 64) == 1 * 16 * 64 * 64 * 4                # padded to whole splits
+    assert n(1, 1, 1000, 72, 64) == 1 * 16 * 64 * 96 * 2                # bf16 d padded to 32
+    assert n(0, 1, 1000, 72, 64) == 1 * 16 * 64 * 72 * 4                 # fp32 d as it is
+    assert n(0, 1, 1000, 64, 64) == 1 * 16 * 64 * 64 * 4                 # padded to whole splits
     assert n(1, 0, 1000, 64, 64) == 0
-    assert n(1, 1, 1000, 64, 100) == UNSUP
+    assert n(1, 1, 1000, 64, 100) == UNSUP                               # bf16 S % 16
+    assert n(1, 1, 1000, 60, 64) == UNSUP                                # bf16 d % 8
     assert n(9, 1, 1000, 64, 64) == DTYPE
     assert n(1, 1, 64, 64, 64) == SHAPE                                  # a single split
     p = lib.avey_maxsim_prepare
@@ -83,15 +101,15 @@ def test_workspace_prepare_and_scores_validation(lib):
     assert p(None, 1, 1, 1024, 64, 64, 64, P16, None) == NULL
     assert p(P16, 1, 1, 1024, 64, 32, 64, P16, None) == SHAPE
     assert p(P16, 1, 1, 1024, 64, 64, 64, P4, None) == ALIGN
-    assert p(P16, 1, 1, 1024, 96, 96, 64, P16, None) == UNSUP
+    assert p(P16, 1, 1, 1024, 100, 104, 64, P16, None) == UNSUP
     m = lib.avey_maxsim_scores
     # (workspace, dt, B, N, d, S, scores, stream)
     assert m(None, 1, 1, 0, 64, 64, None, None) == OK
     assert m(None, 1, 1, 1024, 64, 64, P16, None) == NULL
     assert m(P16, 1, 1, 1024, 64, 64, None, None) == NULL
     assert m(P16, 1, 1, 64, 64, 64, P16, None) == SHAPE                  # a single split
-    assert m(P16, 1, 1, 1024, 64, 96, P16, None) == UNSUP                # bf16 S % 64
-    assert m(P16, 1, 1, 1024, 96, 64, P16, None) == UNSUP                # bf16 d % 64
+    assert m(P16, 1, 1, 1024, 64, 72, P16, None) == UNSUP                # bf16 S % 16
+    assert m(P16, 1, 1, 1024, 100, 64, P16, None) == UNSUP               # bf16 d % 8
     assert m(P16, 0, 1, 1024, 64, 64, P16 + 1, None) == ALIGN
 
 
@@ -108,10 +126,10 @@ def test_topk_validation(lib, fn):
 def test_split_rank_preceding_validation(lib):
     f = lib.avey_split_rank_preceding
     # same argument list and checks as avey_split_rank
-    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None, None) == OK
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, P16, None) == NULL
-    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, P16, None) == SHAPE
-    assert f(P16, 1, 1, 1024, 96, 96, 64, 3, P16, P16, P16, P16, None) == UNSUP
+    assert f(None, 1, 0, 1024, 64, 64, 64, 3, None, None, None, None) == OK
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 3, None, P16, P16, None) == NULL
+    assert f(P16, 1, 1, 1024, 64, 64, 64, 16, P16, P16, P16, None) == SHAPE
+    assert f(P16, 1, 1, 1024, 100, 104, 64, 3, P16, P16, P16, None) == UNSUP
 
 
 def test_select_compress_validation(lib):

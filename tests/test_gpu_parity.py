@@ -305,12 +305,14 @@ def test_preceding_ranker_parity(gpu_ok, name):
 
 def test_side_stream_and_workspace_reuse(gpu_ok):
     """Work is enqueued on the caller's current stream, and one workspace serves calls of
-    different sizes in a row: results equal the default-stream ones bitwise."""
+    different sizes in a row: results equal the default-stream ones bitwise, on both ranker
+    paths."""
     cfg = SMALL["small_bf16"]
     inp = make_inputs(cfg)
     say("side stream, workspace reuse")
     x, P, z, z_tail = upload(inp)
     ref = [t.clone() for t in A.avey_split_rank(x, cfg.S, cfg.k)]
+    ref_ws = [t.clone() for t in A.avey_split_rank_ws(x, cfg.S, cfg.k)]
     ref_x = A.avey_select_compress(x, ref[1], ref[2], P, cfg.S)
     ref_o = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
     torch.cuda.synchronize()
@@ -318,19 +320,92 @@ def test_side_stream_and_workspace_reuse(gpu_ok):
     small = x[:1, :1100]
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
-        s1 = A.avey_split_rank(small, cfg.S, cfg.k, workspace=ws)   # smaller problem first
-        s2 = A.avey_split_rank(x, cfg.S, cfg.k, workspace=ws)
-        xh = A.avey_select_compress(x, s2[1], s2[2], P, cfg.S)
+        s1 = A.avey_split_rank_ws(small, cfg.S, cfg.k, workspace=ws)   # smaller problem first
+        s2 = A.avey_split_rank_ws(x, cfg.S, cfg.k, workspace=ws)
+        s3 = A.avey_split_rank(x, cfg.S, cfg.k)
+        xh = A.avey_select_compress(x, s3[1], s3[2], P, cfg.S)
         o = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
     side.synchronize()
-    for a_, b_ in zip(ref, s2):
+    for a_, b_ in zip(ref_ws, s2):
+        assert torch.equal(a_, b_)
+    for a_, b_ in zip(ref, s3):
         assert torch.equal(a_, b_)
     assert torch.equal(ref_x.view(torch.int16), xh.view(torch.int16))
     assert torch.equal(ref_o.view(torch.int16), o.view(torch.int16))
-    s1_ref = A.avey_split_rank(small, cfg.S, cfg.k)
+    s1_ref = A.avey_split_rank_ws(small, cfg.S, cfg.k)
     torch.cuda.synchronize()
     for a_, b_ in zip(s1_ref, s1):
         assert torch.equal(a_, b_)
+
+
+# The ranker's shape range (S a multiple of 16 up to 512, d a multiple of 8), both paths. The
+# d % 32 != 0 cases end every row on a partial 32-feature chunk; S not a multiple of 256 leaves
+# rows of every unit past the split; N not a multiple of S leaves a ragged last split.
+RANK_SHAPES = {
+    "S208_d200": Config("r208", B=2, N=2000, d=200, S=208, k=3, m_t=64, m=64, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+    "S48_d72": Config("r48", B=1, N=1000, d=72, S=48, k=4, m_t=64, m=64, dtype="bf16",
+                      x_dist="mixture", n_centroids=16),
+    "S16_d8": Config("r16", B=2, N=300, d=8, S=16, k=2, m_t=64, m=64, dtype="bf16",
+                     x_dist="mixture", n_centroids=8),
+    "S400_d776": Config("r400", B=1, N=3000, d=776, S=400, k=2, m_t=64, m=64, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+    "S512_d40": Config("r512", B=2, N=2100, d=40, S=512, k=3, m_t=64, m=64, dtype="bf16",
+                       x_dist="mixture", n_centroids=16),
+}
+
+
+@pytest.mark.parametrize("path", ["rows", "workspace"])
+@pytest.mark.parametrize("name", list(RANK_SHAPES))
+def test_rank_shape_range(gpu_ok, name, path):
+    """Every score, top-k set and weight against the oracle over the ranker's shape range, on the
+    workspace-free path (avey_split_rank) and the explicit-workspace path. One token is zero
+    (its cosine with everything is 0) and x has a row stride larger than d."""
+    cfg = RANK_SHAPES[name]
+    tol = TOL[cfg.dtype]
+    inp = make_inputs(cfg)
+    say(f"rank {path} {name}: B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S} k={cfg.k}")
+    xd = dev_tensor(inp.x, cfg.dtype)
+    wide = torch.full((cfg.B, cfg.N, cfg.d + 24), float("nan"), device="cuda", dtype=xd.dtype)
+    wide[..., : cfg.d] = xd
+    x = wide[..., : cfg.d]                          # row stride d + 24, NaN beyond d
+    x[cfg.B - 1, 5].zero_()
+    x64 = inp.x_f64().copy()
+    x64[cfg.B - 1, 5] = 0.0
+    if path == "rows":
+        scores, idx, w = A.avey_split_rank(x, cfg.S, cfg.k)
+    else:
+        scores, idx, w = A.avey_split_rank_ws(x, cfg.S, cfg.k)
+    torch.cuda.synchronize()
+    g_s = scores.cpu().numpy().astype(np.float64)
+    g_i, g_w = idx.cpu().numpy(), w.cpu().numpy()
+    worst = 0.0
+    for (b, i), (o_row, o_idx, o_w, gap) in O.split_rank(x64, cfg.S, cfg.k).items():
+        worst = max(worst, check_score_row(g_s[b, i], o_row, i, tol["scores"]))
+        check_topk_row(g_i[b, i], g_w[b, i], o_row, o_idx, gap, i, cfg.k, tol["w"])
+    say(f"rank {path} {name}: worst score relative error {worst:.2e}")
+
+
+def test_rank_paths_agree_at_full_size(gpu_ok):
+    """The two ranker paths on the 32K-token workload: scores within the score tolerance of each
+    other everywhere, the same top-k sets wherever the gap between the k-th and (k+1)-th score
+    exceeds twice that tolerance."""
+    cfg = CONFIGS["long"]
+    inp = make_inputs(cfg)
+    say("rank paths at B=2 N=32768 d=768 S=256 k=3")
+    x = dev_tensor(inp.x, cfg.dtype)
+    s_r, i_r, w_r = [t.cpu().numpy() for t in A.avey_split_rank(x, cfg.S, cfg.k)]
+    s_w, i_w, w_w = [t.cpu().numpy() for t in A.avey_split_rank_ws(x, cfg.S, cfg.k)]
+    off = ~np.eye(cfg.n_s, dtype=bool)[None].repeat(cfg.B, 0)
+    rel = np.abs(s_r[off].astype(np.float64) - s_w[off]) / np.abs(s_w[off])
+    assert rel.max() <= 2 * TOL["bf16"]["scores"]
+    srt = -np.sort(-np.where(off, s_w, -np.inf), axis=-1)
+    gap = (srt[..., cfg.k - 1] - srt[..., cfg.k]) / np.abs(srt[..., cfg.k - 1])
+    clear = gap > 4 * TOL["bf16"]["scores"]
+    same = np.array([[set(i_r[b, i]) == set(i_w[b, i]) for i in range(cfg.n_s)] for b in range(cfg.B)])
+    assert same[clear].all()
+    assert (w_r[..., 0] == 1.0).all() and (w_w[..., 0] == 1.0).all()
+    say(f"rank paths: max relative score difference {rel.max():.2e}, {int(clear.sum())} clear rows")
 
 
 # Shapes with at least one 256-feature x 256-token unit per CU (256 CUs), so that compression
