@@ -42,8 +42,9 @@ avey_status check_tensor(const void* p, avey_dtype dt, int64_t N, int64_t width,
   return AVEY_OK;
 }
 
+// bf16 split lengths: multiples of 16 (the MFMA operand tiles are padded with zero rows).
 avey_status check_split_bf16(avey_dtype dt, int32_t S) {
-  return (dt == AVEY_BF16 && S % 64) ? AVEY_ERR_UNSUPPORTED : AVEY_OK;
+  return (dt == AVEY_BF16 && S % 16) ? AVEY_ERR_UNSUPPORTED : AVEY_OK;
 }
 
 #define AVEY_TRY(expr)                      \
@@ -236,8 +237,8 @@ avey_status dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, i
   bool empty = false;
   AVEY_TRY(check_common(dt, B, N, S, &empty));
   if (empty) return AVEY_OK;
-  AVEY_TRY(check_tensor(z_tail, dt, N, m_t, ld_z));
-  AVEY_TRY(check_tensor(out, dt, N, m_t, ld_out));
+  AVEY_TRY(check_tensor(z_tail, dt, N, m_t, ld_z, 8));
+  AVEY_TRY(check_tensor(out, dt, N, m_t, ld_out, 8));
   AVEY_TRY(check_split_bf16(dt, S));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dt == AVEY_BF16) {
@@ -280,8 +281,8 @@ avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_
   AVEY_TRY(check_common(dt, B, N, S, &empty));
   if (empty) return AVEY_OK;
   if (!idx || !w || !P) return AVEY_ERR_NULL;
-  AVEY_TRY(check_tensor(x, dt, N, d, ld_x));
-  AVEY_TRY(check_tensor(xhat, dt, N, d, ld_out));
+  AVEY_TRY(check_tensor(x, dt, N, d, ld_x, 8));
+  AVEY_TRY(check_tensor(xhat, dt, N, d, ld_out, 8));
   if (k < 1 || (residual != 0 && residual != 1)) return AVEY_ERR_SHAPE;
   if (!aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
   if ((int64_t)S * (k + 1) * S >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // P byte offsets < 2^31
@@ -327,8 +328,8 @@ avey_status avey_static_layer(const void* z_tail, avey_dtype dt, int64_t B, int6
   LayerEpi epi;
   AVEY_TRY(check_epi(bias, act, &epi));
   if (!V) return AVEY_ERR_NULL;
-  AVEY_TRY(check_tensor(z_tail, dt, N, m_t, ld_z));
-  AVEY_TRY(check_tensor(out, dt, N, m_t, ld_out));
+  AVEY_TRY(check_tensor(z_tail, dt, N, m_t, ld_z, 8));
+  AVEY_TRY(check_tensor(out, dt, N, m_t, ld_out, 8));
   AVEY_TRY(check_split_bf16(dt, S));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // V Z_i is the gather + compress product with no retrieved block (k = 0: X_cat = Z_i, P = V)

@@ -117,7 +117,10 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((int64_t)a.S * KP * 2));
   const int32_t* idx_i = a.idx + split * a.k;
   const float* w_i = a.w + split * a.k;
-  const int nk = KP / KH;
+  // chunks per block: the last one of a block is partial when S % 32 != 0 (its rows past S load
+  // zeros, so the columns of P they meet, the next block's, add nothing)
+  const int cpb = (a.S + KH - 1) / KH;
+  const int nk = (a.k + 1) * cpb;
   const int nk3 = (nk + 2) / 3 * 3;
   const int f_base = ft * TF;
 
@@ -151,7 +154,6 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   __syncthreads();
   // Chunk c of the K loop covers slot (c / cpb + 1) mod (k + 1): slots 1..k, then slot 0; j is
   // its offset within the block.
-  const int cpb = a.S / KH;
   auto chunk_block = [&](int c, int& r, int& j) {
     const int q = c / cpb;
     r = q < a.k ? q + 1 : 0;
@@ -161,7 +163,7 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
   // Chunk kc into stage st, 6 copies per wave: X tokens 8w .. 8w + 7 (n = 0..3, 2 tokens per
   // copy, 1 KiB) and P rows 32w .. 32w + 31 (n = 4, 5, 16 rows per copy). Lane terms are
   // recomputed per chunk (laundered so they are not hoisted into long-lived registers). Tokens
-  // past N, features past d and rows past S load zeros.
+  // past N or past their block's S tokens, features past d and rows past S load zeros.
   auto copy_chunk = [&](int kc, uint8_t* st, bool valid, int n) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -174,7 +176,7 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
       const int c = (p >> 1) ^ (2 * (t & 3));                      // logical 32-byte piece
       const int f = f_base + c * 16 + (p & 1) * 8;
       const int64_t tok = (int64_t)tok0 + t;
-      const bool ok = valid && tok >= 0 && tok < a.N && f < a.d;
+      const bool ok = valid && tok >= 0 && tok < a.N && j + t < a.S && f < a.d;
       dma16(xr, st + (wave * 8 + n * 2) * XB, ok ? (uint32_t)((tok * a.ld_x + f) * 2) : OOB, 0);
     } else {
       const int r0 = wave * 32 + (n - 4) * 16;
@@ -380,8 +382,10 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   if (t >= cnt) return;
 
   const int KP = (a.k + 1) * a.S;
-  const int cpb = CPB ? CPB : a.S / KH;   // chunks per block
-  const int nk = KP / KH;
+  // chunks per block, even (the residual's pipeline parity below relies on it): when S is not a
+  // multiple of 64 the last chunks of a block are partial or empty, their rows past S zeros
+  const int cpb = CPB ? CPB : (a.S + 2 * KH - 1) / (2 * KH) * 2;
+  const int nk = (a.k + 1) * cpb;
   const int nk4 = (nk + 3) / 4 * 4;       // padded with zero chunks: every unit starts on stage 0
   // floor(c / cpb) as (c * cpb_magic) >> 20: exact while c * (cpb_magic * cpb - 2^20) < 2^20,
   // i.e. for c < 2^16 with cpb <= 16, far above any chunk index here
@@ -447,18 +451,20 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     r = q < a.k ? q + 1 : 0;
     j = c - q * cpb;
   };
-  // First token (x) and first column of P (y) of chunk kc: lane reads instead of LDS loads, whose
-  // wait would also drain the fragment reads.
+  // First token (x), first column of P (y) and the block's rows left from the chunk's first (z)
+  // of chunk kc: lane reads instead of LDS loads, whose wait would also drain the fragment reads.
   auto chunk_src = [&](int kc) {
     int r, j;
     chunk_block(kc, r, j);
-    return make_int2(__builtin_amdgcn_readlane(vtok, r) + j * KH, __builtin_amdgcn_readlane(vcol, r) + j * KH);
+    return make_int3(__builtin_amdgcn_readlane(vtok, r) + j * KH, __builtin_amdgcn_readlane(vcol, r) + j * KH,
+                     a.S - j * KH);
   };
   // Copy n of chunk kc into stage st: n = 0, 1 are X rows 4 w + 2 n, + 1 (1 KiB), n = 2, 3 are
-  // P rows 32 w + 16 (n - 2) .. + 15. Tokens past N, features past d and rows past S load zeros:
+  // P rows 32 w + 16 (n - 2) .. + 15. Tokens past N or past their block's S tokens, features past
+  // d and rows past S load zeros:
   // their offset gets the high bit, past the descriptor's range (a sequence and P are < 2^31
   // bytes), so that the offsets are plain 32-bit arithmetic without a branch.
-  auto copy = [&](uint8_t* st, bool valid, int n, int2 src) {
+  auto copy = [&](uint8_t* st, bool valid, int n, int3 src) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     if (n < 2) {
@@ -467,7 +473,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       const int c = (p >> 1) ^ (2 * (tr & 3));
       const int fl = c * 16 + (p & 1) * 8;                 // feature within the tile
       const uint32_t tok = (uint32_t)(src.x + tr);         // an empty block's tokens wrap above N
-      const bool ok = valid & (tok < (uint32_t)a.N) & (fl < a.d - c_fb);
+      const bool ok = valid & (tok < (uint32_t)a.N) & (tr < src.z) & (fl < a.d - c_fb);
       const uint32_t off = (tok * (uint32_t)a.ld_x + (uint32_t)(c_fb + fl)) * 2u;
       dma16(xr, st + (wave * 4 + n * 2) * XB, off | ((uint32_t)!ok << 31), 0);
     } else {
@@ -481,7 +487,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     }
   };
   auto dma = [&](int kc, uint8_t* st, bool valid) {
-    const int2 src = chunk_src(kc);
+    const int3 src = chunk_src(kc);
 #pragma unroll
     for (int n = 0; n < 4; ++n) copy(st, valid, n, src);
   };
@@ -567,7 +573,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   // inline constant) instead of reading them, so that nothing has to clear them.
   auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
                           const uint8_t* next) {
-    const int2 src = chunk_src(kc);
+    const int3 src = chunk_src(kc);
     const bool ron = (c == rc0) | (c == rc1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)

@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   const bool p_ok = p < valid_rows;
   const bool relu = a.epi.act != 0;
   const float bv = layer_bias(a.epi, p, p_ok);
-  const int nk1 = a.m_t / KC;                     // phase-1 chunks of 64 features
+  const int nk1 = (a.m_t + KC - 1) / KC;          // phase-1 chunks of 64 features (last partial)
   const int nk1p = (nk1 + 3) / 4 * 4;             // padded with zero chunks to a multiple of 4
   const int nft = (a.m_t + FT - 1) / FT;
 
@@ -126,12 +126,13 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   // between them would join control flow around the copies, after which the compiler drains
   // all copies before the next LDS read.
   auto copy1 = [&](int c, uint8_t* st, bool valid, int n) {
-    // rows 32 w + 8 n .. + 7 of chunk c, 128 bytes each; lane -> row (ln >> 3), position (ln & 7)
+    // rows 32 w + 8 n .. + 7 of chunk c, 128 bytes each; lane -> row (ln >> 3), position (ln & 7);
+    // 16-byte pieces past m_t (the last chunk when m_t % 64 != 0) load zeros
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int row = wave * 32 + n * 8 + (ln >> 3);
     const uint32_t pc = (uint32_t)((ln & 7) ^ (int)swz<SWZ_ROW>(row));
-    const bool ok = valid && c < nk1 && row < valid_rows;
+    const bool ok = valid && c < nk1 && row < valid_rows && 8 * (int)pc < a.m_t - c * KC;
     dma16(zr, st + (wave * 32 + n * 8) * ROWB, ok ? (uint32_t)((base + row) * a.ld_z * 2) + 16u * pc : OOB,
           (uint32_t)c * KC * 2u);
   };
@@ -354,7 +355,7 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
   const int64_t base = (int64_t)i * a.S;
   const int nvalid = (int)min((int64_t)a.S, a.N - base);   // valid tokens of the split
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
-  const int nk = a.m_t / KC;
+  const int nk = (a.m_t + KC - 1) / KC;           // phase-1 chunks (the last one partial)
 
   // ---- phase 1: C1[q][p] for all 512 q and this wave's 32 p. Wave w copies rows 64 w .. +63 of
   // each half of a chunk (8 copies of 8 rows per half), so that every copy has a fixed LDS
@@ -386,11 +387,18 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
   // squared norms (k-halves) of rows 256 (j >> 1) + 64 w + 32 (j & 1) + (l & 31)
   float sq[4] = {0.f, 0.f, 0.f, 0.f};
 
+  // Chunk kc; the 16-byte pieces past m_t (the last chunk when m_t % 64 != 0) load zeros: the
+  // piece of copy n is (l & 7) ^ ((4 (n & 1) + (l >> 4)) & 7), the swizzle of its row.
   auto dma1 = [&](int kc, uint8_t* lo, uint8_t* hi) {
+    const int lim = a.m_t - kc * KC;
+    auto off = [&](int n) {
+      const int c = (lane & 7) ^ ((4 * (n & 1) + (lane >> 4)) & 7);
+      return offZ[n] | ((uint32_t)(8 * c >= lim) << 31);
+    };
 #pragma unroll
-    for (int n = 0; n < 8; ++n) dma16(zr, lo + (wave * 64 + n * 8) * ROWB, offZ[n], (uint32_t)kc * KC * 2);
+    for (int n = 0; n < 8; ++n) dma16(zr, lo + (wave * 64 + n * 8) * ROWB, off(n), (uint32_t)kc * KC * 2);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) dma16(zr, hi + (wave * 64 + n * 8) * ROWB, offZ[8 + n], (uint32_t)kc * KC * 2);
+    for (int n = 0; n < 8; ++n) dma16(zr, hi + (wave * 64 + n * 8) * ROWB, off(8 + n), (uint32_t)kc * KC * 2);
   };
   // Every LDS read names its object (a read through a selected pointer would also wait for
   // the copies in flight): the p fragment is read from both halves and selected. The next

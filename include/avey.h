@@ -31,11 +31,11 @@
  *   - Outputs must not overlap inputs.
  *   - Empty work (B == 0 or N == 0) returns AVEY_OK and enqueues nothing; pointers may then
  *     be NULL.
- *   - Shape limits: 1 <= S <= 512. For AVEY_BF16 additionally every ld is a multiple of 8 and
- *     every tensor pointer is 16-byte aligned; the ranker (avey_split_rank, avey_maxsim and the
- *     workspace path) takes S % 16 == 0 and d % 8 == 0, the other entry points S % 64 == 0 and
- *     feature widths (d, m_t, m) that are multiples of 64. For AVEY_F32 every tensor pointer is
- *     4-byte aligned. Violations return AVEY_ERR_SHAPE, AVEY_ERR_ALIGN or AVEY_ERR_UNSUPPORTED.
+ *   - Shape limits: 1 <= S <= 512. For AVEY_BF16 additionally S % 16 == 0, every ld is a
+ *     multiple of 8, every tensor pointer is 16-byte aligned, the feature widths d and m_t are
+ *     multiples of 8, and the enricher / fuser widths (d, m, m_h, m_t there) multiples of 64.
+ *     For AVEY_F32 every tensor pointer is 4-byte aligned. Violations return AVEY_ERR_SHAPE,
+ *     AVEY_ERR_ALIGN or AVEY_ERR_UNSUPPORTED.
  */
 #ifndef AVEY_H
 #define AVEY_H

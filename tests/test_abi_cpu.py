@@ -142,7 +142,8 @@ def test_select_compress_validation(lib):
     assert f(P16, 1, 1, 1024, 64, 64, 64, 0, P16, P16, P16, 1, P16, 64, None) == SHAPE
     assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P16, 1, P16, 60, None) == SHAPE   # ld_out < d
     assert f(P16, 1, 1, 1024, 64, 64, 64, 3, P16, P16, P4, 1, P16, 64, None) == ALIGN    # P alignment
-    assert f(P16, 1, 1, 1024, 64, 64, 32, 3, P16, P16, P16, 1, P16, 64, None) == UNSUP   # bf16 S % 64
+    assert f(P16, 1, 1, 1024, 64, 64, 40, 3, P16, P16, P16, 1, P16, 64, None) == UNSUP   # bf16 S % 16
+    assert f(P16, 1, 1, 1024, 60, 64, 64, 3, P16, P16, P16, 1, P16, 64, None) == UNSUP   # bf16 d % 8
     assert f(P16, 1, 1, 1 << 20, 64, 64, 64, 600, P16, P16, P16, 1, P16, 64, None) == UNSUP   # bf16 k + 1 > 512
 
 
@@ -152,7 +153,8 @@ def test_dyn_context_validation(lib):
     assert f(None, 1, 0, 1024, 64, 64, 64, 1e-8, None, 64, None) == OK
     assert f(None, 1, 1, 1024, 64, 64, 64, 1e-8, P16, 64, None) == NULL
     assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, None, 64, None) == NULL
-    assert f(P16, 1, 1, 1024, 100, 104, 64, 1e-8, P16, 104, None) == UNSUP    # bf16 m_t % 64
+    assert f(P16, 1, 1, 1024, 100, 104, 64, 1e-8, P16, 104, None) == UNSUP    # bf16 m_t % 8
+    assert f(P16, 1, 1, 1024, 64, 64, 72, 1e-8, P16, 64, None) == UNSUP       # bf16 S % 16
     assert f(P16, 1, 1, 1024, 64, 64, 600, 1e-8, P16, 64, None) == SHAPE      # S > 512
     assert f(P16 + 8, 1, 1, 1024, 64, 64, 64, 1e-8, P16, 64, None) == ALIGN
     assert f(P16, 9, 1, 1024, 64, 64, 64, 1e-8, P16, 64, None) == DTYPE
@@ -174,7 +176,7 @@ def test_dyn_layer_validation(lib):
     assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, 4, None, 0, P16, 64, None) == SHAPE     # unknown norm
     assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, -1, None, 0, P16, 64, None) == SHAPE
     assert f(P16, 1, 1, 1024, 64, 64, 64, 1e-8, 1, P16 + 2, 1, P16, 64, None) == ALIGN  # bias not 4-aligned
-    assert f(P16, 1, 1, 1024, 64, 64, 96, 1e-8, 2, None, 1, P16, 64, None) == UNSUP    # bf16 S % 64
+    assert f(P16, 1, 1, 1024, 64, 64, 88, 1e-8, 2, None, 1, P16, 64, None) == UNSUP    # bf16 S % 16
     assert f(P16, 9, 1, 1024, 64, 64, 64, 1e-8, 3, None, 0, P16, 64, None) == DTYPE
 
 
@@ -189,7 +191,8 @@ def test_static_layer_validation(lib):
     assert f(P16, 1, 1, 1024, 64, 64, 64, P16 + 8, None, 0, P16, 64, None) == ALIGN  # bf16 V 16-aligned
     assert f(P16, 0, 1, 1024, 64, 64, 64, P16 + 2, None, 0, P16, 64, None) == ALIGN  # f32 V 4-aligned
     assert f(P16, 1, 1, 1024, 64, 64, 64, P16, P16 + 1, 0, P16, 64, None) == ALIGN   # bias
-    assert f(P16, 1, 1, 1024, 64, 64, 32, P16, None, 0, P16, 64, None) == UNSUP     # bf16 S % 64
+    assert f(P16, 1, 1, 1024, 64, 64, 40, P16, None, 0, P16, 64, None) == UNSUP     # bf16 S % 16
+    assert f(P16, 1, 1, 1024, 12, 16, 64, P16, None, 0, P16, 16, None) == UNSUP     # bf16 m_t % 8
     assert f(P16, 1, 1, 1024, 64, 32, 64, P16, None, 0, P16, 64, None) == SHAPE     # ld_z < m_t
     assert f(P16, 1, 1, 1024, 64, 64, 0, P16, None, 0, P16, 64, None) == SHAPE      # S < 1
 

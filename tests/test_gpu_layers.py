@@ -32,6 +32,12 @@ CASES = {
     "s64_bf16": Config("s64_bf16", B=1, N=700, d=64, S=64, k=2, m_t=64, m=128, dtype="bf16",
                        x_dist="mixture", n_centroids=8),
     "tiny": CONFIGS["tiny"],
+    # S = 208 and m_t = 72 (multiples of 16 and 8 only): partial chunks in both layers
+    "s208_bf16": Config("s208_bf16", B=1, N=1500, d=64, S=208, k=2, m_t=72, m=136, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+    # S = 400: the S <= 512 dynamic kernel with a partial group of 128 tokens
+    "s400_bf16": Config("s400_bf16", B=1, N=1300, d=64, S=400, k=2, m_t=200, m=264, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
 }
 
 

@@ -36,6 +36,15 @@ SMALL = {
     "s64_bf16": Config("s64_bf16", B=1, N=700, d=64, S=64, k=2, m_t=64, m=128, dtype="bf16",
                        x_dist="mixture", n_centroids=8),
     "tiny": CONFIGS["tiny"],
+    # S, d and m_t multiples of 16 and 8 only: partial 32-token chunks at the end of every block
+    # of X_cat, a partial 64-feature chunk in the dynamic layer, a ragged last split
+    "s208_d200": Config("s208_d200", B=2, N=2000, d=200, S=208, k=3, m_t=72, m=136, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+    "s48_d72": Config("s48_d72", B=1, N=1000, d=72, S=48, k=4, m_t=40, m=104, dtype="bf16",
+                      x_dist="mixture", n_centroids=16),
+    # 256 < S <= 512 with S % 64 != 0: the S <= 512 dynamic kernel's partial groups of 128 tokens
+    "s400_d136": Config("s400_d136", B=1, N=2100, d=136, S=400, k=2, m_t=200, m=264, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
 }
 
 
@@ -425,6 +434,12 @@ PERSISTENT = {
                          x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
     # 448 units: per XCD one full round and 24 units left over
     "tail24": (Config("ptail24", B=1, N=57294, d=512, S=256, k=3, m_t=512, m=512, dtype="bf16",
+                         x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+    # S = 208 and 400 (cpb rounded up to an even 8 and 14 chunks per block, the last ones
+    # partial or empty), d % 32 != 0: 290 and 300 units
+    "s208_d200": (Config("p208", B=2, N=30000, d=200, S=208, k=3, m_t=200, m=200, dtype="bf16",
+                         x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
+    "s400_d136": (Config("p400", B=1, N=59950, d=136, S=400, k=3, m_t=136, m=136, dtype="bf16",
                          x_dist="mixture", n_centroids=32, z_kind="relu2_x"), True),
     # 320 units but k + 1 = 71 blocks, more than the persistent kernel's table holds: the tiled
     # kernel takes it
