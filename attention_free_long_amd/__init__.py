@@ -37,6 +37,7 @@ EXPORTS = (
     "avey_topk_norm_preceding",
     "avey_split_rank",
     "avey_split_rank_preceding",
+    "avey_split_rank_noalloc",
     "avey_select_compress",
     "avey_dyn_context",
     "avey_dyn_layer",
@@ -85,7 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avey_topk_norm_preceding.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.avey_maxsim.restype = i32
     lib.avey_maxsim.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, vp]
-    for fn in (lib.avey_split_rank, lib.avey_split_rank_preceding):
+    for fn in (lib.avey_split_rank, lib.avey_split_rank_preceding, lib.avey_split_rank_noalloc):
         fn.restype = i32
         fn.argtypes = [vp, i32, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.avey_select_compress.restype = i32
@@ -286,6 +287,21 @@ def avey_split_rank(x, S: int, k: int, scores=None, idx=None, w=None, preceding:
     lib = load_library()
     fn = lib.avey_split_rank_preceding if preceding else lib.avey_split_rank
     _check(fn_name, fn(
+        x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, scores.data_ptr(), idx.data_ptr(), w.data_ptr(),
+        _stream(x)))
+    return scores, idx, w
+
+
+def avey_split_rank_noalloc(x, S: int, k: int, scores=None, idx=None, w=None):
+    """(scores, idx, w) of the bidirectional ranker through the explicit-workspace path with the
+    workspace in the library's own device array (the call allocates no device memory; outputs
+    are allocated here only when not given)."""
+    B, N, d, ld = _rows(x, "x")
+    n_s = n_splits(N, S)
+    fn_name = "avey_split_rank_noalloc"
+    scores = _scores_arg(fn_name, scores, x, B, n_s)
+    idx, w = _topk_args(fn_name, idx, w, x, B, n_s, k)
+    _check(fn_name, load_library().avey_split_rank_noalloc(
         x.data_ptr(), _dtype_code(x), B, N, d, ld, S, k, scores.data_ptr(), idx.data_ptr(), w.data_ptr(),
         _stream(x)))
     return scores, idx, w

@@ -165,6 +165,23 @@ avey_status avey_topk_norm_preceding(const float* scores, int64_t B, int64_t n_s
                                      int32_t* idx, float* w, void* stream);
 
 /*
+ * avey_split_rank_noalloc -- for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that must not call hipMalloc): the results of avey_split_rank,
+ * computed through the explicit-workspace path (avey_maxsim_prepare, avey_maxsim_scores,
+ * avey_topk_norm) with its workspace in a device array of AVEY_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends. Nothing is allocated.
+ *   arguments and outputs as avey_split_rank; runs on the current device
+ * Sequences go through the array in groups of as many as fit; a shape whose single sequence
+ * needs more than AVEY_NOALLOC_SCRATCH_BYTES (avey_rank_workspace_bytes with B = 1) returns
+ * AVEY_ERR_UNSUPPORTED. All calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams or host threads) race and must be ordered by the caller.
+ */
+#define AVEY_NOALLOC_SCRATCH_BYTES (160LL << 20)
+avey_status avey_split_rank_noalloc(const void* x, avey_dtype dt, int64_t B, int64_t N, int64_t d,
+                                    int64_t ld_x, int32_t S, int32_t k, float* scores, int32_t* idx,
+                                    float* w, void* stream);
+
+/*
  * avey_split_rank_preceding -- the unidirectional ranker: avey_maxsim, then
  * avey_topk_norm_preceding, on the same stream; arguments as avey_split_rank.
  */
