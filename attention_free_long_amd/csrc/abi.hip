@@ -105,7 +105,7 @@ avey_status split_rank(const void* x, avey_dtype dt, int64_t B, int64_t N, int64
 // Row-wise (position-wise) entry points: a [M, width] operand set.
 avey_status check_rows(avey_dtype dt, int64_t M, bool* empty) {
   if (dt != AVEY_F32 && dt != AVEY_BF16) return AVEY_ERR_DTYPE;
-  if (M < 0) return AVEY_ERR_SHAPE;
+  if (!size_ok(M)) return AVEY_ERR_SHAPE;
   *empty = M == 0;
   return AVEY_OK;
 }
@@ -129,12 +129,12 @@ avey_status dyn_layer(const void* z_tail, avey_dtype dt, int64_t B, int64_t N, i
   AVEY_TRY(check_split_bf16(dt, S));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dt == AVEY_BF16) {
-    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * (S > 256 ? 2 : 1);
+    const int64_t tiles = prod(B, splits(N, S), (S + 255) / 256, S > 256 ? 2 : 1);
     if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
     return hip_status(launch_dyn_bf16(static_cast<const uint16_t*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
                                       static_cast<uint16_t*>(out), ld_out, st, epi));
   }
-  if (B * N > kI32) return AVEY_ERR_UNSUPPORTED;
+  if (prod(B, N) > kI32) return AVEY_ERR_UNSUPPORTED;
   return hip_status(launch_dyn_f32(static_cast<const float*>(z_tail), B, N, (int)m_t, ld_z, S, eps,
                                    static_cast<float*>(out), ld_out, st, epi));
 }
@@ -178,14 +178,14 @@ avey_status avey_select_compress(const void* x, avey_dtype dt, int64_t B, int64_
   if (dt == AVEY_BF16) {
     if (!aligned(P, 16)) return AVEY_ERR_ALIGN;
     if (k + 1 > kCompressMaxBlocks) return AVEY_ERR_UNSUPPORTED;
-    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * ((d + 255) / 256);
+    const int64_t tiles = prod(B, splits(N, S), (S + 255) / 256, (d + 255) / 256);
     if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
     return hip_status(launch_compress_bf16(static_cast<const uint16_t*>(x), B, N, (int)d, ld_x, S, k, idx, w,
                                            static_cast<const uint16_t*>(P), residual, static_cast<uint16_t*>(xhat),
                                            ld_out, st));
   }
   if (!aligned(P, 4)) return AVEY_ERR_ALIGN;
-  if ((B * N * d + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  if (prod(B, N, d) > 256 * kI32) return AVEY_ERR_UNSUPPORTED;
   return hip_status(launch_compress_f32(static_cast<const float*>(x), B, N, (int)d, ld_x, S, k, idx, w,
                                         static_cast<const float*>(P), residual, static_cast<float*>(xhat), ld_out, st));
 }
@@ -222,14 +222,14 @@ avey_status avey_static_layer(const void* z_tail, avey_dtype dt, int64_t B, int6
   // V Z_i is the gather + compress product with no retrieved block (k = 0: X_cat = Z_i, P = V)
   if (dt == AVEY_BF16) {
     if (!aligned(V, 16)) return AVEY_ERR_ALIGN;
-    const int64_t tiles = B * splits(N, S) * ((S + 255) / 256) * ((m_t + 255) / 256);
+    const int64_t tiles = prod(B, splits(N, S), (S + 255) / 256, (m_t + 255) / 256);
     if (tiles > kI32) return AVEY_ERR_UNSUPPORTED;
     return hip_status(launch_compress_bf16(static_cast<const uint16_t*>(z_tail), B, N, (int)m_t, ld_z, S, 0,
                                            nullptr, nullptr, static_cast<const uint16_t*>(V), 0,
                                            static_cast<uint16_t*>(out), ld_out, st, epi));
   }
   if (!aligned(V, 4)) return AVEY_ERR_ALIGN;
-  if ((B * N * m_t + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  if (prod(B, N, m_t) > 256 * kI32) return AVEY_ERR_UNSUPPORTED;
   return hip_status(launch_compress_f32(static_cast<const float*>(z_tail), B, N, (int)m_t, ld_z, S, 0, nullptr,
                                         nullptr, static_cast<const float*>(V), 0, static_cast<float*>(out), ld_out,
                                         st, epi));
@@ -247,13 +247,13 @@ avey_status avey_enrich(const void* x, avey_dtype dt, int64_t M, int64_t d, int6
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dt == AVEY_BF16) {
     if (!aligned(U, 16)) return AVEY_ERR_ALIGN;
-    if (d * m >= (1LL << 30) || (b && m > kEnrichMaxWidth)) return AVEY_ERR_UNSUPPORTED;
+    if (prod(d, m) >= (1LL << 30) || (b && m > kEnrichMaxWidth)) return AVEY_ERR_UNSUPPORTED;
     return hip_status(launch_enrich_bf16(static_cast<const uint16_t*>(x), M, (int)d, ld_x,
                                          static_cast<const uint16_t*>(U), (int)m, b, static_cast<uint16_t*>(z),
                                          ld_z, st));
   }
   if (!aligned(U, 4)) return AVEY_ERR_ALIGN;
-  if ((M * m + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  if (prod(M, m) > 256 * kI32) return AVEY_ERR_UNSUPPORTED;
   return hip_status(launch_enrich_f32(static_cast<const float*>(x), M, (int)d, ld_x, static_cast<const float*>(U),
                                       (int)m, b, static_cast<float*>(z), ld_z, st));
 }
@@ -265,7 +265,7 @@ avey_status avey_fuse(const void* z, avey_dtype dt, int64_t M, int64_t m_h, int6
   AVEY_TRY(check_rows(dt, M, &empty));
   if (empty) return AVEY_OK;
   if (!O) return AVEY_ERR_NULL;
-  if (m_h < 0) return AVEY_ERR_SHAPE;
+  if (!size_ok(m_h)) return AVEY_ERR_SHAPE;
   if (m_h > 0) AVEY_TRY(check_tensor(z, dt, M, m_h, ld_z));
   AVEY_TRY(check_tensor(c, dt, M, m_t, ld_c));
   AVEY_TRY(check_tensor(x, dt, M, d, ld_x));
@@ -274,21 +274,21 @@ avey_status avey_fuse(const void* z, avey_dtype dt, int64_t M, int64_t m_h, int6
   if (dt == AVEY_BF16) {
     if (m_h % 64) return AVEY_ERR_UNSUPPORTED;
     if (!aligned(O, 16)) return AVEY_ERR_ALIGN;
-    if ((m_h + m_t) * d >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;
+    if (prod(m_h + m_t, d) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;
     return hip_status(launch_fuse_bf16(static_cast<const uint16_t*>(z), M, (int)m_h, ld_z,
                                        static_cast<const uint16_t*>(c), (int)m_t, ld_c,
                                        static_cast<const uint16_t*>(O), (int)d, static_cast<const uint16_t*>(x),
                                        ld_x, static_cast<uint16_t*>(y), ld_y, st));
   }
   if (!aligned(O, 4)) return AVEY_ERR_ALIGN;
-  if ((M * d + 255) / 256 > kI32) return AVEY_ERR_UNSUPPORTED;
+  if (prod(M, d) > 256 * kI32) return AVEY_ERR_UNSUPPORTED;
   return hip_status(launch_fuse_f32(static_cast<const float*>(z), M, (int)m_h, ld_z, static_cast<const float*>(c),
                                     (int)m_t, ld_c, static_cast<const float*>(O), (int)d,
                                     static_cast<const float*>(x), ld_x, static_cast<float*>(y), ld_y, st));
 }
 
 int64_t avey_probe_mfma_flops(int64_t iters) {
-  if (iters < 1) return AVEY_ERR_SHAPE;
+  if (iters < 1 || iters > (1LL << 24)) return AVEY_ERR_SHAPE;
   const int cus = probe_cus();
   if (cus < 0) return AVEY_ERR_HIP;
   // per iteration and wave: 16 MFMAs of 32 x 32 x 16 multiply-adds
@@ -296,7 +296,7 @@ int64_t avey_probe_mfma_flops(int64_t iters) {
 }
 
 avey_status avey_probe_mfma_bf16(int64_t iters, int32_t changing, float* sink, void* stream) {
-  if (iters < 1) return AVEY_ERR_SHAPE;
+  if (iters < 1 || iters > (1LL << 24)) return AVEY_ERR_SHAPE;
   if (!sink) return AVEY_ERR_NULL;
   if (!aligned(sink, 4)) return AVEY_ERR_ALIGN;
   const int cus = probe_cus();

@@ -12,6 +12,19 @@ namespace {
 
 constexpr int64_t kMaxS = 512;
 constexpr int64_t kI32 = 0x7fffffffLL;
+// Every size argument is checked to lie in [0, kMaxDim] before it enters any arithmetic, and
+// products of sizes are formed with prod(), which saturates at INT64_MAX instead of overflowing.
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+
+bool size_ok(int64_t v) { return v >= 0 && v <= kMaxDim; }
+
+int64_t prod(int64_t a) { return a; }
+template <class... R>
+int64_t prod(int64_t a, int64_t b, R... rest) {
+  int64_t p;
+  if (__builtin_mul_overflow(a, b, &p)) p = INT64_MAX;
+  return prod(p, rest...);
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -23,7 +36,7 @@ avey_status hip_status(hipError_t e) { return e == hipSuccess ? AVEY_OK : AVEY_E
 // nothing to do.
 avey_status check_common(avey_dtype dt, int64_t B, int64_t N, int32_t S, bool* empty) {
   if (dt != AVEY_F32 && dt != AVEY_BF16) return AVEY_ERR_DTYPE;
-  if (B < 0 || N < 0 || S < 1 || S > kMaxS) return AVEY_ERR_SHAPE;
+  if (!size_ok(B) || !size_ok(N) || S < 1 || S > kMaxS) return AVEY_ERR_SHAPE;
   *empty = (B == 0 || N == 0);
   return AVEY_OK;
 }
@@ -31,11 +44,11 @@ avey_status check_common(avey_dtype dt, int64_t B, int64_t N, int32_t S, bool* e
 // A [B, N, width] operand with row stride ld; bf16 widths must be multiples of `mult`.
 avey_status check_tensor(const void* p, avey_dtype dt, int64_t N, int64_t width, int64_t ld, int64_t mult = 64) {
   if (!p) return AVEY_ERR_NULL;
-  if (width < 1 || ld < width) return AVEY_ERR_SHAPE;
+  if (width < 1 || ld < width || ld > kMaxDim) return AVEY_ERR_SHAPE;
   if (dt == AVEY_BF16) {
     if (width % mult) return AVEY_ERR_UNSUPPORTED;
     if (ld % 8 || !aligned(p, 16)) return AVEY_ERR_ALIGN;
-    if (N * ld >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // byte offsets within a sequence stay < 2^31
+    if (prod(N, ld) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // byte offsets within a sequence stay < 2^31
   } else {
     if (!aligned(p, 4)) return AVEY_ERR_ALIGN;
   }
@@ -59,7 +72,7 @@ int64_t padded_d(avey_dtype dt, int64_t d) { return dt == AVEY_BF16 ? (d + 31) /
 // Bytes of the ranker workspace (normalised, padded copy of X), or a negative status.
 int64_t workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S) {
   const int64_t eb = dt == AVEY_BF16 ? 2 : 4;
-  return B * splits(N, S) * S * padded_d(dt, d) * eb;
+  return prod(B, splits(N, S), S, padded_d(dt, d), eb);
 }
 
 // Checks of the ranker (scoring, and the workspace path's preparation) on the shape alone. bf16
@@ -67,17 +80,18 @@ int64_t workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t 
 avey_status check_rank_shape(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S, bool* empty) {
   AVEY_TRY(check_common(dt, B, N, S, empty));
   if (*empty) return AVEY_OK;
-  if (d < 1) return AVEY_ERR_SHAPE;
+  if (d < 1 || d > kMaxDim) return AVEY_ERR_SHAPE;
   const int64_t n_s = splits(N, S);
   if (n_s < 2) return AVEY_ERR_SHAPE;
   if (dt == AVEY_BF16) {
     if (S % 16 || d % 8) return AVEY_ERR_UNSUPPORTED;
-    if (n_s * S * padded_d(dt, d) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // workspace offsets < 2^31
-    if (n_s * (n_s - 1) / 2 > kI32) return AVEY_ERR_UNSUPPORTED;
+    if (prod(n_s, S, padded_d(dt, d)) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // workspace offsets < 2^31
+    if (prod(n_s, n_s - 1) / 2 > kI32) return AVEY_ERR_UNSUPPORTED;
   } else {
-    if (B * n_s * n_s > kI32) return AVEY_ERR_UNSUPPORTED;
+    if (prod(B, n_s, n_s) > kI32) return AVEY_ERR_UNSUPPORTED;
   }
-  if ((B * n_s * S + 15) / 16 > kI32) return AVEY_ERR_UNSUPPORTED;
+  if (prod(B, n_s, S) > 16 * kI32) return AVEY_ERR_UNSUPPORTED;            // prepare's grid
+  if (prod(B, n_s, S, padded_d(dt, d)) > (1LL << 45)) return AVEY_ERR_UNSUPPORTED;   // workspace elements
   return AVEY_OK;
 }
 
@@ -85,7 +99,7 @@ avey_status check_rank_shape(avey_dtype dt, int64_t B, int64_t N, int64_t d, int
 // of a whole last unit past N (which it reads as zeros), stay below 2^31.
 avey_status check_rank_rows(const void* x, avey_dtype dt, int64_t N, int64_t d, int64_t ld_x) {
   AVEY_TRY(check_tensor(x, dt, N, d, ld_x, 8));
-  if (dt == AVEY_BF16 && (N + 512) * ld_x >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;
+  if (dt == AVEY_BF16 && prod(N + 512, ld_x) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;
   return AVEY_OK;
 }
 
@@ -110,13 +124,13 @@ avey_status check_scores(const void* ws, avey_dtype dt, int64_t B, int64_t N, in
 
 avey_status check_topk(const float* scores, int64_t B, int64_t n_s, int32_t k, const int32_t* idx, const float* w,
                        bool* empty) {
-  if (B < 0 || n_s < 0) return AVEY_ERR_SHAPE;
+  if (!size_ok(B) || !size_ok(n_s)) return AVEY_ERR_SHAPE;
   *empty = (B == 0 || n_s == 0);
   if (*empty) return AVEY_OK;
   if (!scores || !idx || !w) return AVEY_ERR_NULL;
   if (n_s < 2 || k < 1 || k > n_s - 1 || n_s > kI32) return AVEY_ERR_SHAPE;
   if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(w, 4)) return AVEY_ERR_ALIGN;
-  if ((B * n_s + 3) / 4 > kI32) return AVEY_ERR_UNSUPPORTED;
+  if (prod(B, n_s) > 4 * kI32) return AVEY_ERR_UNSUPPORTED;                 // top-k grid
   return AVEY_OK;
 }
 

@@ -52,6 +52,7 @@ extern "C" avey_status avey_split_rank_noalloc(const void* x, avey_dtype dt, int
   if (!scores) return AVEY_ERR_NULL;
   AVEY_TRY(check_tensor(x, dt, N, d, ld_x, 8));
   if (!aligned(scores, 4)) return AVEY_ERR_ALIGN;
+  if (prod(B, N, ld_x) > (1LL << 50)) return AVEY_ERR_UNSUPPORTED;   // x's offsets stay far from overflow
   const int64_t n_s = splits(N, S);
   AVEY_TRY(check_topk(scores, B, n_s, k, idx, w, &empty));
   // one sequence's copy must fit; as many whole sequences as fit go through each pass

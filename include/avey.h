@@ -48,7 +48,9 @@ extern "C" {
 
 #define AVEY_ABI_VERSION 2
 
-typedef enum { AVEY_F32 = 0, AVEY_BF16 = 1 } avey_dtype;
+/* The last enumerator widens the type's range to every int32 value, so that an unknown value a
+ * caller passes is a valid avey_dtype the checks can reject (AVEY_ERR_DTYPE). */
+typedef enum { AVEY_F32 = 0, AVEY_BF16 = 1, AVEY_DTYPE_RANGE_ = 0x7fffffff } avey_dtype;
 
 typedef enum {
   AVEY_OK = 0,
