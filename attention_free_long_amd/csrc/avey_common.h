@@ -129,6 +129,17 @@ __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
+// 16-byte store through a buffer descriptor. A lane whose offset is out of range (OOB) writes
+// nothing, so a wave can issue the same number of stores whatever its lanes' validity: on this
+// GPU the vector-memory counter counts stores with the loads, and the pipelined kernels account
+// for every store they issue when they wait for their copies. kPolicy is the cache-policy operand
+// (2 sets the non-temporal bit).
+template <int kPolicy = 0>
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, kPolicy);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l writes lds_base + 16 * l, where
 // lds_base must be the same for the whole wave.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_base, uint32_t voff, uint32_t soff) {

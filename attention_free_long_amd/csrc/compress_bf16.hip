@@ -571,8 +571,10 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   const f32x16 zero16 = {};
   // FIRST: the unit's first chunk, whose k-step-0 MFMAs start the accumulators from zero (an
   // inline constant) instead of reading them, so that nothing has to clear them.
+  // late: the previous unit's 16 epilogue stores were issued after the copies of the chunk that
+  // `next` waits for, and may stay in flight as well.
   auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
-                          const uint8_t* next) {
+                          const uint8_t* next, bool late) {
     const int3 src = chunk_src(kc);
     const bool ron = (c == rc0) | (c == rc1);
 #pragma unroll
@@ -600,7 +602,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     __builtin_amdgcn_sched_barrier(0);
     if (next) {
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
-      WAIT_KEEP(7);
+      if (late) WAIT_KEEP(23); else WAIT_KEEP(7);
       fetchA(next, 0, ra0);
       fetchB(next, 0, rb0);
     }
@@ -623,6 +625,7 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   dma(2, st2, 2 < nk);
 
   const bool relu = a.epi.act != 0;
+  bool first_unit = true;
   const std::integral_constant<bool, true> kFirst;
   const std::integral_constant<bool, false> kNext;
   for (;;) {
@@ -641,37 +644,42 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
     }
 
-    // Every chunk is exactly 4 copies per wave and every copy is issued unconditionally, so
-    // WAIT_KEEP(8) at a chunk boundary leaves exactly the two newer chunks in flight (any
-    // epilogue stores of the previous unit are older and only make the wait stricter).
-    WAIT_KEEP(8);
+    // Every chunk is exactly 4 copies per wave, every copy is issued unconditionally and every
+    // epilogue issues exactly 16 stores per wave, so the waits below are exact: at a chunk
+    // boundary the two newer chunks stay in flight, and after the first unit the previous
+    // epilogue's stores too, until chunk 3 (issued after them) is awaited. The branches on
+    // `late` are uniform.
+    const bool late = !first_unit;
+    if (late) WAIT_KEEP(24); else WAIT_KEEP(8);
+    first_unit = false;
     if (has_next) fill_table(nx, bf ^ 1);   // its readers come after later barriers
     fetchA(st0, 0, ra0);
     fetchB(st0, 0, rb0);
     if (nk4 > 4) {
-      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1);
-      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2);
-      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3);
-      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0);
+      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1, late);
+      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2, late);
+      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3, false);
+      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0, false);
       for (int kc = 4; kc + 4 < nk4; kc += 4) {
-        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
-        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
-        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
-        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, false);
+        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2, false);
+        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3, false);
+        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0, false);
       }
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
-      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      const bool late4 = late && nk4 == 4;
+      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, late4);
       if (has_next) set_copy_unit(nx, bf ^ 1);
-      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
-      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
-      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
+      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2, late4);
+      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3, false);
+      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr, false);
     }
 
     // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)
-    uint16_t* ob = a.xhat + cur.b * a.N * a.ld_out;
+    const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.xhat + cur.b * a.N * a.ld_out, (uint32_t)(a.N * a.ld_out * 2));
     lds_sync();   // every wave is done reading stage 3
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -701,7 +709,8 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
         const int s = cur.su * TU + sl;
         const int64_t tok = (int64_t)cur.i * a.S + s;
         const int f = cur.f_base + mb * 64 + p * 8;
-        if (s < a.S && tok < a.N && f < a.d) store16_nt(ob + tok * a.ld_out + f, v);
+        const bool ok = s < a.S && tok < a.N && f < a.d;
+        buf_store16<2>(outr, ok ? (uint32_t)((tok * a.ld_out + f) * 2) : OOB, 0, v);   // non-temporal
       }
       if (mb < 3) lds_sync();
     }

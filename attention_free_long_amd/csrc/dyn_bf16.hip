@@ -280,8 +280,10 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   // Epilogue of feature tile ft, through stage 3 in four rounds of 64 features: each lane writes
   // its 4-feature groups into a [256 tokens][64 features] bf16 tile (16-byte piece c of row t at
   // c ^ ((t >> 1) & 7)), then 8 lanes per token store whole 128-byte row pieces (scattered
-  // 8-byte stores would cost a write request per lane).
-  uint16_t* ob = a.out + b * a.N * a.ld_out;
+  // 8-byte stores would cost a write request per lane). Every wave issues exactly 16 stores per
+  // tile (lanes past the split or past m_t store out of range), which the next tile's first three
+  // copy waits allow for: the stores drain under the MFMAs instead of holding up the next tile.
+  const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.out + b * a.N * a.ld_out, (uint32_t)(a.N * a.ld_out * 2));
   auto epilogue = [&](int ft) {
     lds_sync();   // every wave is done reading stage 3
     const uint32_t rowo = (uint32_t)p * 128u + 8u * (uint32_t)(lane >> 5);
@@ -307,24 +309,28 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
         const int pp = lane & 7;
         const uint4 v = lds_read16(st3, (uint32_t)t * 128u + ((uint32_t)(pp ^ ((t >> 1) & 7)) << 4));
         const int f = ft * FT + rr * 64 + pp * 8;
-        if (t < valid_rows && f < a.m_t) *reinterpret_cast<uint4*>(ob + (base + t) * a.ld_out + f) = v;
+        const bool ok = t < valid_rows && f < a.m_t;
+        buf_store16(outr, ok ? (uint32_t)(((base + t) * a.ld_out + f) * 2) : OOB, 0, v);
       }
       if (rr < 3) lds_sync();
     }
   };
+  // A tile's chunk c0 + q is complete once at most 8 newer copies are outstanding; after an
+  // epilogue its 16 stores are newer than chunks c0 .. c0 + 2 as well (24; the branch on ft is
+  // uniform).
   for (int ft = 0; ft < nft; ++ft) {
     const int c0 = 4 * ft;
-    DYN_WAIT_KEEP(8);
+    if (ft) DYN_WAIT_KEEP(24); else DYN_WAIT_KEEP(8);
     compute2(st0, std::integral_constant<int, 0>{}, c0 + 3, st3);
-    DYN_WAIT_KEEP(8);
+    if (ft) DYN_WAIT_KEEP(24); else DYN_WAIT_KEEP(8);
     compute2(st1, std::integral_constant<int, 1>{}, c0 + 4, st0);
-    DYN_WAIT_KEEP(8);
+    if (ft) DYN_WAIT_KEEP(24); else DYN_WAIT_KEEP(8);
     compute2(st2, std::integral_constant<int, 2>{}, c0 + 5, st1);
     DYN_WAIT_KEEP(8);
     compute2(st3, std::integral_constant<int, 3>{}, c0 + 6, st2);
     epilogue(ft);
   }
-  wait_vmem();   // the zero-filled copies issued past the last chunk land before the exit
+  wait_vmem();   // the copies issued past the last chunk and the last stores complete before the exit
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -544,8 +550,9 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
   };
   // Epilogue of feature tile ft through stage 3 in four rounds of 64 features ([128 tokens][64
   // features] bf16, 16-byte piece c of row t at c ^ ((t >> 1) & 7)), stored as whole 128-byte
-  // row pieces by 8 lanes per token.
-  uint16_t* ob = a.out + b * a.N * a.ld_out;
+  // row pieces by 8 lanes per token. Every wave issues exactly 16 stores per tile (lanes past the
+  // split or past m_t store out of range), which the next tile's first three copy waits allow for.
+  const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.out + b * a.N * a.ld_out, (uint32_t)(a.N * a.ld_out * 2));
   const int pl = wave * 32 + (lane & 31);          // this lane's token within the workgroup
   auto epilogue = [&](int ft) {
     lds_sync();   // every wave is done reading stage 3
@@ -573,23 +580,25 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
         const uint4 v = lds_read16(st3, (uint32_t)t * 128u + ((uint32_t)(pp ^ ((t >> 1) & 7)) << 4));
         const int f = ft * FT + rr * 64 + pp * 8;
         const int tp = pg * 128 + t;
-        if (tp < nvalid && f < a.m_t) *reinterpret_cast<uint4*>(ob + (base + tp) * a.ld_out + f) = v;
+        const bool ok = tp < nvalid && f < a.m_t;
+        buf_store16(outr, ok ? (uint32_t)(((base + tp) * a.ld_out + f) * 2) : OOB, 0, v);
       }
       if (rr < 3) lds_sync();
     }
   };
   // The phase-1 stages are free (the barriers above); chunks 0..2 go into stages 0..2. Before
-  // chunk c: its 8 copies are complete in every wave (the 16 newer ones may stay in flight).
+  // chunk c: its 8 copies are complete in every wave (the 16 newer ones may stay in flight, and
+  // after an epilogue for chunks c0 .. c0 + 2 its 16 stores as well; the branch on ft is uniform).
   for (int n = 0; n < 8; ++n) copy2(0, st0, n);
   for (int n = 0; n < 8; ++n) copy2(1, st1, n);
   for (int n = 0; n < 8; ++n) copy2(2, st2, n);
   for (int ft = 0; ft < nft; ++ft) {
     const int c0 = 8 * ft;
-    DYN_WAIT_KEEP(16);
+    if (ft) DYN_WAIT_KEEP(32); else DYN_WAIT_KEEP(16);
     compute2(st0, std::integral_constant<int, 0>{}, c0 + 3, st3);
-    DYN_WAIT_KEEP(16);
+    if (ft) DYN_WAIT_KEEP(32); else DYN_WAIT_KEEP(16);
     compute2(st1, std::integral_constant<int, 1>{}, c0 + 4, st0);
-    DYN_WAIT_KEEP(16);
+    if (ft) DYN_WAIT_KEEP(32); else DYN_WAIT_KEEP(16);
     compute2(st2, std::integral_constant<int, 2>{}, c0 + 5, st1);
     DYN_WAIT_KEEP(16);
     compute2(st3, std::integral_constant<int, 3>{}, c0 + 6, st2);
@@ -603,7 +612,7 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
     compute2(st3, std::integral_constant<int, 7>{}, c0 + 10, st2);
     epilogue(ft);
   }
-  wait_vmem();   // the zero-filled copies issued past the last chunk land before the exit
+  wait_vmem();   // the copies issued past the last chunk and the last stores complete before the exit
 }
 
 }  // namespace ring
