@@ -8,8 +8,9 @@ and the dynamic layer's row-normalised cosine mixing. The default workload is th
 one (batch 2, N = 32768, d = 768, S = 256, k = 3, tail width 1536).
 
 Prints one JSON line: tokens/s over the timed steps, per-kernel times from HIP events on the
-launch stream, the MaxSim kernel against the bf16 MFMA roofline, and the CPU oracle timed on a
-bounded sample of the same workload.
+launch stream, the MaxSim kernel against the bf16 MFMA roofline, the ceilings measured on the
+device (matrix-core and copy probes, the vendor GEMM on the same contraction shapes), and the
+CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,8 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("baf884bcbc72d556", "long"): {"fetch_kib": 1216465.3, "fetch_scale": 1.99995,
-                                           "write_kib": 252.6, "write_scale": 1.0},
+            ("a4c8a43485b7b117", "long"): {"fetch_kib": 1213562.2, "fetch_scale": 1.99992,
+                                           "write_kib": 252.8, "write_scale": 1.0},
+            ("a4c8a43485b7b117", "extreme"): {"fetch_kib": 5080300.3, "fetch_scale": 1.99992,
+                                              "write_kib": 1181.2, "write_scale": 1.0},
         },
     },
 }
@@ -297,6 +300,42 @@ def measured_peaks(A, reps: int = 10):
                       f"avey_probe_copy (1 GiB, read + written), median of {reps} launches"}
 
 
+def library_gemm_rates(cfg, reps: int = 10):
+    """The vendor GEMM (hipBLASLt through torch.matmul, bf16 in and out, fp32 accumulation) on the
+    contractions of this workload, as a calibration of what the matrix cores sustain here on plain
+    GEMMs of the same shapes: MaxSim's all-pairs token product of one sequence ([N, d] x [d, N],
+    every ordered pair, no max epilogue), the enricher ([B N, d] x [d, m]) and the fuser
+    ([B N, m] x [m, d]). Medians of `reps` launches timed with HIP events; operands are contiguous
+    N(0, 1) bf16."""
+    import numpy as np
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    shapes = {"maxsim_all_pairs": (cfg.N, cfg.d, cfg.N), "enrich": (cfg.B * cfg.N, cfg.d, cfg.m),
+              "fuse": (cfg.B * cfg.N, cfg.m, cfg.d)}
+    out = {}
+    for name, (M, K, N) in shapes.items():
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16, generator=g)
+        c = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, b, out=c)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(ts))
+        tf = 2.0 * M * K * N / t / 1e12
+        out[name] = {"shape_mkn": [M, K, N], "median_us": round(t * 1e6, 1), "tflops": round(tf, 1),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del a, b, c
+    out["method"] = f"torch.matmul (hipBLASLt) bf16, median of {reps} launches"
+    return out
+
+
 def upload(cfg, inp):
     import numpy as np
     import torch
@@ -500,6 +539,7 @@ def main(argv=None):
         roofline["frac_measured"] = round(achieved / mp_["mfma_bf16_tflops_changing_operands"], 4)
         comp_t = r["kernels"]["compress"]["avg_us"] * 1e-6
         result["compress_hbm_frac_measured"] = round(work["compress"]["bytes"] / comp_t / 1e9 / mp_["copy_gbs"], 4)
+        result["library_gemm"] = library_gemm_rates(cfg)
     if not args.no_layers:
         result["layers"] = time_layers(A, cfg, inp, z_tail, work, max(10, args.steps // 2), peak)
     del x, z_tail
@@ -512,7 +552,8 @@ def main(argv=None):
             "value": round(e["value"], 1), "unit": "tokens/s", "ms_per_step": round(e["ms_per_step"], 4),
             "steps": max(5, args.steps // 5),
             "maxsim": {"achieved": round(e["maxsim_achieved_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(e["maxsim_achieved_tflops"] / PEAK_BF16_TFLOPS, 4)},
+                       "unit": "TFLOP/s", "frac": round(e["maxsim_achieved_tflops"] / PEAK_BF16_TFLOPS, 4),
+                       "traffic": traffic_bytes("maxsim", ecfg.name), "traffic_unit": "bytes per launch"},
             "compress_cold": e["compress_cold"],
             "rank_workspace_free": e["rank_workspace_free"],
             "compress_hbm_frac": e["compress_hbm_frac"],
