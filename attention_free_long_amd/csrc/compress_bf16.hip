@@ -59,13 +59,6 @@ __device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* base, uint32_t off)
   return __builtin_bit_cast(uint2, v);
 }
 
-// 16-byte global store with the non-temporal hint: the output stream then takes less of the
-// caches' room from the gathered X rows still to be read (1-4 % faster at 32K-96K tokens).
-__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
-}
-
 // Order of a retrieved block (index src, weight w) in the K loop: ascending |w| (the bits of a
 // finite |w| order as the values do), then the blocks that contribute nothing (an empty block,
 // negative index; a zero weight), then those with a non-finite weight.

@@ -60,13 +60,6 @@ struct GemmParams {
 template <int P>
 using Pos = std::integral_constant<int, P>;
 
-// 16-byte global store with the non-temporal hint (the output stream then takes less of the
-// caches' room from the operands still to be read)
-__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
-}
-
 __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   __shared__ __align__(16) float s_bias[kMaxF];
@@ -93,6 +86,8 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   const __amdgpu_buffer_rsrc_t a1r = make_rsrc(a.A1, (uint32_t)(a.M * a.lda1 * 2));
   const __amdgpu_buffer_rsrc_t a2r = make_rsrc(a.A2, a.A2 ? (uint32_t)(a.M * a.lda2 * 2) : 0u);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R, a.R ? (uint32_t)(a.M * a.ldr * 2) : 0u);
+  // the output; each wave's epilogue stores go through it, lanes out of range at OOB
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.C, (uint32_t)(a.M * a.ldc * 2));
 
   // ---- copy side: the unit whose chunks are being copied
   int64_t c_t0 = 0;
@@ -197,8 +192,10 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   const f32x16 zero16 = {};
   // FIRST: the unit's first chunk, whose k-step-0 MFMAs start the accumulators from zero (an
   // inline constant) instead of reading them, so that nothing has to clear them.
+  // late: the previous unit's 16 epilogue stores were issued after the copies of the chunk that
+  // `next` waits for, and may stay in flight as well.
   auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
-                          const uint8_t* next) {
+                          const uint8_t* next, bool late) {
     const bool ron = has_res && (c == nreg + 2 * wn || c == nreg + 2 * wn + 1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -224,7 +221,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
     __builtin_amdgcn_sched_barrier(0);
     if (next) {
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
-      WAIT_KEEP(7);
+      if (late) WAIT_KEEP(23); else WAIT_KEEP(7);
       fetch(next, 0, ra0, rb0);
     }
 #pragma unroll
@@ -242,6 +239,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   dma(2, st2, 2 < nk);
 
   const bool relu2 = a.relu2 != 0;
+  bool first_unit = true;
   const std::integral_constant<bool, true> kFirst;
   const std::integral_constant<bool, false> kNext;
   for (;;) {
@@ -258,31 +256,36 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
     }
 
-    // Every chunk is exactly 4 copies per wave, issued unconditionally, so WAIT_KEEP(8) at a
-    // chunk boundary leaves exactly the two newer chunks in flight (older epilogue stores only
-    // make the wait stricter).
-    WAIT_KEEP(8);
+    // Every chunk is exactly 4 copies per wave, every copy is issued unconditionally and every
+    // epilogue issues exactly 16 stores per wave, so the waits are exact: at a chunk boundary
+    // the two newer chunks stay in flight, and after the first unit the previous epilogue's
+    // stores too, until chunk 3 (issued after them) is awaited. The branches on `late` are
+    // uniform.
+    const bool late = !first_unit;
+    if (late) WAIT_KEEP(24); else WAIT_KEEP(8);
+    first_unit = false;
     fetch(st0, 0, ra0, rb0);
     if (nk4 > 4) {
-      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1);
-      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2);
-      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3);
-      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0);
+      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1, late);
+      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2, late);
+      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3, false);
+      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0, false);
       for (int kc = 4; kc + 4 < nk4; kc += 4) {
-        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
-        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2);
-        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3);
-        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0);
+        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, false);
+        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2, false);
+        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3, false);
+        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0, false);
       }
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
-      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1);
+      const bool late4 = late && nk4 == 4;
+      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, late4);
       if (has_next) set_copy_unit(t + Gx);
-      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2);
-      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3);
-      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr);
+      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2, late4);
+      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3, false);
+      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr, false);
     }
 
     // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)
@@ -317,7 +320,8 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
         const uint4 v = lds_read16(st3, (uint32_t)sl * 128u + ((uint32_t)(p ^ ((sl >> 1) & 7)) << 4));
         const int64_t tok = t0 + sl;
         const int f = f0 + mb * 64 + p * 8;
-        if (tok < a.M && f < a.F) store16_nt(a.C + tok * a.ldc + f, v);
+        const bool ok = tok < a.M && f < a.F;
+        buf_store16<2>(cr, ok ? (uint32_t)((tok * a.ldc + f) * 2) : OOB, 0, v);   // non-temporal
       }
       if (mb < 3) lds_sync();
     }
