@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   __shared__ __align__(16) float s_rnA[T];   // kRow: per target row 1 / |x_t| (0 for a zero token)
   __shared__ __align__(16) float s_rnB[T];   // kRow: per candidate row
   __shared__ float s_ssA[2 * T], s_ssB[2 * T];   // kRow: running sums of squares, [k-half][row]
-  __shared__ float s_cm[2][T];               // column maxima of the two row halves
+  __shared__ float s_cm[2][2][T];            // column maxima of the two row halves x two lane halves
   __shared__ float s_colmax[2 * T];          // running column maxima over target blocks (S = 512)
   __shared__ float s_red[8];
 
@@ -572,11 +572,10 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // both lane halves store their column maxima (the owner of the column takes the max of the
+    // four), so no cross-lane exchange is needed here
 #pragma unroll
-    for (int u_ = 0; u_ < 2; ++u_) {
-      const float m = fmaxf(cm[u_], __shfl_xor(cm[u_], 32));
-      if (lane < 32) s_cm[wm][wn * 64 + blkB(u_) * 32 + lane] = m;
-    }
+    for (int u_ = 0; u_ < 2; ++u_) s_cm[wm][lane >> 5][wn * 64 + blkB(u_) * 32 + (lane & 31)] = cm[u_];
     lds_sync();
     if (is_row) {
       // target row own: 8 quad maxima from each of the 4 waves that hold its columns
@@ -595,7 +594,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       rmax = first_ub ? m : fmaxf(rmax, m);
       if (last_ub && valid) part += rmax;
     } else {
-      float cmv = fmaxf(s_cm[0][own], s_cm[1][own]);
+      float cmv = fmaxf(fmaxf(s_cm[0][0][own], s_cm[0][1][own]), fmaxf(s_cm[1][0][own], s_cm[1][1][own]));
       if (!first_ua) cmv = fmaxf(cmv, s_colmax[cur.ub * T + own]);
       if (!last_ua) s_colmax[cur.ub * T + own] = cmv;
       else if (valid) part += kRow ? cmv * s_rnB[own] : cmv;
@@ -603,10 +602,19 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 
     if (last_ua && last_ub) {
       // ---- scores of the pair; fixed reduction order (bitwise reproducible)
+      // within each 16-lane row by DPP (lane ^ 1, lane ^ 2, then the mirrors l <-> 7 - l within
+      // 8 lanes and l <-> 15 - l within 16), then the four row sums read from lanes 0, 16, 32 and
+      // 48: no LDS round trip on this dependency chain
       float r = part;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) r += __shfl_xor(r, o);
-      if (lane == 0) s_red[wave] = r;
+      r += __builtin_amdgcn_update_dpp(0.f, r, 0xB1, 0xF, 0xF, false);
+      r += __builtin_amdgcn_update_dpp(0.f, r, 0x4E, 0xF, 0xF, false);
+      r += __builtin_amdgcn_update_dpp(0.f, r, 0x141, 0xF, 0xF, false);
+      r += __builtin_amdgcn_update_dpp(0.f, r, 0x140, 0xF, 0xF, false);
+      auto lane_f = [&](int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), l));
+      };
+      const float rs = ((lane_f(0) + lane_f(16)) + lane_f(32)) + lane_f(48);
+      if (lane == 0) s_red[wave] = rs;
       lds_sync();
       if (tid == 0) {
         const float tr = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
