@@ -36,10 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("a4c8a43485b7b117", "long"): {"fetch_kib": 1213562.2, "fetch_scale": 1.99992,
+            ("325a791a28e101e9", "long"): {"fetch_kib": 1206284.3, "fetch_scale": 1.99992,
                                            "write_kib": 252.8, "write_scale": 1.0},
-            ("a4c8a43485b7b117", "extreme"): {"fetch_kib": 5080300.3, "fetch_scale": 1.99992,
-                                              "write_kib": 1181.2, "write_scale": 1.0},
+            ("325a791a28e101e9", "extreme"): {"fetch_kib": 5325169.7, "fetch_scale": 1.99992,
+                                              "write_kib": 1532.8, "write_scale": 1.0},
         },
     },
 }
