@@ -18,7 +18,8 @@ from make_oracle_scores import x_digest  # noqa: E402
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-@pytest.mark.parametrize("name,rows", [("long", [(0, 0), (1, 64), (1, 127)]), ("extreme", [(0, 5), (0, 383)])])
+@pytest.mark.parametrize("name,rows", [("base", [(0, 0), (7, 31)]), ("long", [(0, 0), (1, 64), (1, 127)]),
+                                       ("extreme", [(0, 5), (0, 383)]), ("wide", [(0, 3), (3, 31)])])
 def test_stored_scores_are_the_oracles(name, rows):
     cfg = CONFIGS[name]
     gold = np.load(os.path.join(GOLDEN, f"oracle_scores_{name}.npz"))

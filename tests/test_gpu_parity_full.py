@@ -1,5 +1,5 @@
-"""GPU parity on every output of the full-size 32K-token and 96K-token workloads, in the launch
-configuration bench.py times.
+"""GPU parity on every output of the full-size bf16 workloads (base 8 x 8192 tokens, 32K and 96K
+tokens, wide 4 x 16384 tokens with S = 512 and k = 7), in the launch configuration bench.py times.
 
 MaxSim relevance of every split to every target split, the top-k of each row and its
 divide-by-max weights (paperlayer.ai "Avey-B" summary, section 3; papernotes.org Avey-B note,
@@ -38,7 +38,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("name", ["long", "extreme"])
+@pytest.mark.parametrize("name", ["base", "long", "extreme", "wide"])
 def test_every_output_at_full_size(gpu_ok, name):
     cfg = CONFIGS[name]
     tol = TOL[cfg.dtype]
