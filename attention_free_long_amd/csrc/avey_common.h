@@ -130,10 +130,13 @@ __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 }
 
 // 16-byte store through a buffer descriptor. A lane whose offset is out of range (OOB) writes
-// nothing, so a wave can issue the same number of stores whatever its lanes' validity: on this
-// GPU the vector-memory counter counts stores with the loads, and the pipelined kernels account
-// for every store they issue when they wait for their copies. kPolicy is the cache-policy operand
-// (2 sets the non-temporal bit).
+// nothing, so a wave can issue the same number of stores whatever its lanes' validity. On this
+// GPU one vector-memory counter (vmcnt) counts buffer loads, direct-to-LDS copies and buffer
+// stores together, and a wave's vector-memory operations report completion in the order they
+// were issued. A wait for "at most n outstanding" therefore completes exactly the operations
+// issued before the last n, and the pipelined kernels add the stores they issued after a chunk's
+// copies to n when they wait for that chunk. kPolicy is the cache-policy operand (2 sets the
+// non-temporal bit).
 template <int kPolicy = 0>
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint4 v) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -194,8 +194,9 @@ def cpu_baseline(inp, budget_s: float = 12.0):
 def time_layers(A, cfg, inp, z_tail, work, steps: int, peak: float):
     """The rest of a neural-processor layer on the same workload, timed apart from the step with
     HIP events on the launch stream (not part of the step's throughput): the static and dynamic
-    contextualizer layers (bias and ReLU) on the tail, the enricher X -> Z (d -> m) and the
-    fuser [Z_h || c] -> Y (m -> d, with the residual)."""
+    contextualizer layers (bias and ReLU) on the tail, the dynamic layer with each of the other
+    row normalisations, the enricher X -> Z (d -> m) and the fuser [Z_h || c] -> Y (m -> d, with
+    the residual)."""
     import numpy as np
     import torch
     from synth import layer_params
@@ -218,11 +219,16 @@ def time_layers(A, cfg, inp, z_tail, work, steps: int, peak: float):
     calls = {
         "static_layer": lambda: A.avey_static_layer(z_tail, Vd, cfg.S, bd, "relu", out=out),
         "dyn_layer": lambda: A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu", out=out),
+        # the row normalisations compared beside eq. 6: softmax, RMS, none
+        "dyn_layer_softmax": lambda: A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu", out=out, norm="softmax"),
+        "dyn_layer_rms": lambda: A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu", out=out, norm="rms"),
+        "dyn_layer_none": lambda: A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu", out=out, norm="none"),
         "enrich": lambda: A.avey_enrich(x, Ud, bUd, out=zf),
         "fuse": lambda: A.avey_fuse(zf, m_h, out, Od, x, out=y),
     }
     res = {}
     for name, call in calls.items():
+        wk = work[name.split("_softmax")[0].split("_rms")[0].split("_none")[0]]
         for _ in range(5):
             call()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -233,8 +239,8 @@ def time_layers(A, cfg, inp, z_tail, work, steps: int, peak: float):
         torch.cuda.synchronize()
         t = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for j in range(steps)])) * 1e-3
         res[name] = {"avg_us": round(t * 1e6, 3),
-                     "hbm_frac": round(work[name]["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4),
-                     "mfma_frac": round(work[name]["flop"] / t / 1e12 / peak, 4),
+                     "hbm_frac": round(wk["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4),
+                     "mfma_frac": round(wk["flop"] / t / 1e12 / peak, 4),
                      "launches": steps}
     return res
 
