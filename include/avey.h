@@ -10,9 +10,11 @@
  *
  * General conventions (all entry points)
  *   - Every pointer argument except the status string is DEVICE memory owned by the caller.
- *     The library allocates nothing, keeps no state between calls, never synchronises and is
- *     safe to call from several host threads at once (calls that share a workspace or an
- *     output buffer must be ordered by the caller, e.g. by using one stream).
+ *     The library allocates nothing, never synchronises, and no result depends on an earlier
+ *     call. The one piece of state it holds is the fixed device array of
+ *     avey_split_rank_noalloc (below). Calls are safe from several host threads at once; calls
+ *     that share a workspace, an output buffer or that array must be ordered by the caller,
+ *     e.g. by using one stream.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream). The call
  *     returns once the kernels are enqueued.
  *   - Return value: AVEY_OK, or an AVEY_ERR_* code. Argument checks run on the host before
