@@ -36,10 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("325a791a28e101e9", "long"): {"fetch_kib": 1206284.3, "fetch_scale": 1.99992,
-                                           "write_kib": 252.8, "write_scale": 1.0},
-            ("325a791a28e101e9", "extreme"): {"fetch_kib": 5325169.7, "fetch_scale": 1.99992,
-                                              "write_kib": 1532.8, "write_scale": 1.0},
+            ("e6aba5177f49f27a", "long"): {"fetch_kib": 1207862.7, "fetch_scale": 1.99992,
+                                           "write_kib": 253.0, "write_scale": 1.0},
+            ("e6aba5177f49f27a", "extreme"): {"fetch_kib": 5339630.3, "fetch_scale": 1.99992,
+                                              "write_kib": 1563.3, "write_scale": 1.0},
         },
     },
 }
