@@ -96,3 +96,61 @@ def test_every_output_at_full_size(gpu_ok, name):
             assert err <= tol["out"], f"dyn {(b, i)}: {err:.3e}"
             worst_o = max(worst_o, err)
     say(f"{name}: worst row relative error, xhat {worst_x:.2e}, dynamic core {worst_o:.2e}")
+
+
+@pytest.mark.parametrize("name", ["long", "extreme"])
+def test_preceding_ranker_every_row_at_full_size(gpu_ok, name):
+    """The unidirectional ranker (candidates precede the target; paperlayer.ai "Avey-B" summary,
+    section 3) on every row of the full-size workload against the stored oracle scores: rows with
+    fewer than k preceding splits end with (-1, 0), the real entries follow the tie rule, and every
+    split of the compression, empty blocks included, matches the oracle."""
+    cfg = CONFIGS[name]
+    tol = TOL[cfg.dtype]
+    gold = np.load(os.path.join(GOLDEN, f"oracle_scores_{name}.npz"))
+    inp = make_inputs(cfg)
+    assert str(gold["x_sha256"]) == x_digest(inp.x)
+    o_scores = gold["scores"]
+    n_s, k = cfg.n_s, cfg.k
+    say(f"{name}: preceding ranker, every row, and the compression of every split")
+    x, P, _, _ = upload(inp)
+    scores, idx, w = A.avey_split_rank(x, cfg.S, k, preceding=True)
+    xhat = A.avey_select_compress(x, idx, w, P, cfg.S, residual=True)
+    torch.cuda.synchronize()
+    g_i, g_w = idx.cpu().numpy(), w.cpu().numpy()
+    how = Counter()
+    for b in range(cfg.B):
+        for i in range(n_s):
+            o_row = o_scores[b, i]
+            o_idx, _, _, gap = O.top_k(o_row, i, k, preceding=True)
+            n_real = min(k, i)
+            gi = [int(v) for v in g_i[b, i]]
+            assert gi[n_real:] == [-1] * (k - n_real) and np.all(g_w[b, i, n_real:] == 0.0)
+            real = gi[:n_real]
+            assert all(0 <= j < i for j in real) and len(set(real)) == n_real
+            if n_real == 0:
+                how["empty"] += 1
+                continue
+            assert g_w[b, i, 0] == 1.0
+            o_real = [int(v) for v in o_idx[:n_real]]
+            if gap >= 1e-3:
+                assert set(real) == set(o_real), f"row {(b, i)}: {real} vs {o_real}"
+                how["exact"] += 1
+            else:
+                kth = o_row[o_real[-1]]
+                for j in set(real) ^ set(o_real):
+                    assert abs(o_row[j] - kth) <= 1e-3 * abs(kth), f"row {(b, i)}: index {j} outside the band"
+                how["band_same" if set(real) == set(o_real) else "band_differs"] += 1
+            ow = np.array([o_row[j] for j in real]) / o_row[real[0]]
+            assert np.max(np.abs(g_w[b, i, :n_real] - ow) / np.abs(ow)) <= tol["w"]
+    say(f"{name}: preceding top-k rows {dict(how)}")
+    P64 = inp.P_f64()
+    worst = 0.0
+    for b in range(cfg.B):
+        xb = inp.x_f64(b)
+        g_x = host_f64(xhat[b])
+        for i in range(n_s):
+            ref = O.compress_split(xb, cfg.S, g_i[b, i], g_w[b, i].astype(np.float64), P64, i)
+            err = row_rel_err(g_x[split_rows_of(cfg.N, cfg.S, i)], ref)
+            assert err <= tol["out"], f"xhat {(b, i)}: {err:.3e}"
+            worst = max(worst, err)
+    say(f"{name}: worst xhat row relative error {worst:.2e}")
