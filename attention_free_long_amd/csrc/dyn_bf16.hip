@@ -310,7 +310,7 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
         const uint4 v = lds_read16(st3, (uint32_t)t * 128u + ((uint32_t)(pp ^ ((t >> 1) & 7)) << 4));
         const int f = ft * FT + rr * 64 + pp * 8;
         const bool ok = t < valid_rows && f < a.m_t;
-        buf_store16(outr, ok ? (uint32_t)(((base + t) * a.ld_out + f) * 2) : OOB, 0, v);
+        buf_store16<2>(outr, ok ? (uint32_t)(((base + t) * a.ld_out + f) * 2) : OOB, 0, v);   // non-temporal
       }
       if (rr < 3) lds_sync();
     }
@@ -581,7 +581,7 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
         const int f = ft * FT + rr * 64 + pp * 8;
         const int tp = pg * 128 + t;
         const bool ok = tp < nvalid && f < a.m_t;
-        buf_store16(outr, ok ? (uint32_t)(((base + tp) * a.ld_out + f) * 2) : OOB, 0, v);
+        buf_store16<2>(outr, ok ? (uint32_t)(((base + tp) * a.ld_out + f) * 2) : OOB, 0, v);   // non-temporal
       }
       if (rr < 3) lds_sync();
     }
