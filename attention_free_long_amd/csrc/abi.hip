@@ -38,7 +38,7 @@ avey_status avey_maxsim_prepare(const void* x, avey_dtype dt, int64_t B, int64_t
   bool empty = false;
   AVEY_TRY(check_prepare(x, dt, B, N, d, ld_x, S, workspace, &empty));
   if (empty) return AVEY_OK;
-  return hip_status(launch_prepare(x, dt == AVEY_BF16, B, N, (int)d, ld_x, S, workspace,
+  return hip_status(launch_prepare(x, dt == AVEY_BF16, B, N, (int)d, ld_x, pack_rows(dt, S), workspace,
                                    reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -70,9 +70,14 @@ avey_status check_split_bf16(avey_dtype dt, int32_t S) {
 int64_t padded_d(avey_dtype dt, int64_t d) { return dt == AVEY_BF16 ? (d + 31) / 32 * 32 : d; }
 
 // Bytes of the ranker workspace (normalised, padded copy of X), or a negative status.
+// Rows per packed block of the bf16 workspace: S, or 256 at S = 64 and 128, where the MaxSim
+// kernel takes 256 / S consecutive splits (256 consecutive tokens) as one side of a unit.
+int32_t pack_rows(avey_dtype dt, int32_t S) { return (dt == AVEY_BF16 && (S == 64 || S == 128)) ? 256 : S; }
+
 int64_t workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S) {
   const int64_t eb = dt == AVEY_BF16 ? 2 : 4;
-  return prod(B, splits(N, S), S, padded_d(dt, d), eb);
+  const int32_t P = pack_rows(dt, S);
+  return prod(B, splits(N, P), P, padded_d(dt, d), eb);
 }
 
 // Checks of the ranker (scoring, and the workspace path's preparation) on the shape alone. bf16
@@ -83,15 +88,17 @@ avey_status check_rank_shape(avey_dtype dt, int64_t B, int64_t N, int64_t d, int
   if (d < 1 || d > kMaxDim) return AVEY_ERR_SHAPE;
   const int64_t n_s = splits(N, S);
   if (n_s < 2) return AVEY_ERR_SHAPE;
+  const int32_t P = pack_rows(dt, S);
+  const int64_t n_p = splits(N, P);                                          // packed blocks
   if (dt == AVEY_BF16) {
     if (S % 16 || d % 8) return AVEY_ERR_UNSUPPORTED;
-    if (prod(n_s, S, padded_d(dt, d)) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // workspace offsets < 2^31
+    if (prod(n_p, P, padded_d(dt, d)) >= (1LL << 30)) return AVEY_ERR_UNSUPPORTED;   // workspace offsets < 2^31
     if (prod(n_s, n_s - 1) / 2 > kI32) return AVEY_ERR_UNSUPPORTED;
   } else {
     if (prod(B, n_s, n_s) > kI32) return AVEY_ERR_UNSUPPORTED;
   }
-  if (prod(B, n_s, S) > 16 * kI32) return AVEY_ERR_UNSUPPORTED;            // prepare's grid
-  if (prod(B, n_s, S, padded_d(dt, d)) > (1LL << 45)) return AVEY_ERR_UNSUPPORTED;   // workspace elements
+  if (prod(B, n_p, P) > 16 * kI32) return AVEY_ERR_UNSUPPORTED;            // prepare's grid
+  if (prod(B, n_p, P, padded_d(dt, d)) > (1LL << 45)) return AVEY_ERR_UNSUPPORTED;   // workspace elements
   return AVEY_OK;
 }
 

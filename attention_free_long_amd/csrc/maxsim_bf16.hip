@@ -21,6 +21,12 @@
 //     instruction reads 1 KiB of contiguous memory.
 //
 // Units are 256 target rows x 256 candidate rows (one per pair at S <= 256, four at S <= 512).
+// At S = 64 and 128 a unit side is instead a group of 256 / S consecutive splits (kG of them):
+// 256 consecutive tokens, which is how the row-major X and the workspace (packed in blocks of
+// 256 rows at these S) already lie, so the K loop and the copies are the same. Each unit then
+// serves every pair between its two groups (including the pairs inside one group, on the
+// diagonal units), and the epilogue keeps one maximum per split: columns of one split are whole
+// waves (64 or 128 columns), rows of one split whole 32-row blocks.
 // One workgroup of 8 waves per CU (2 per SIMD), in a 2 x 4 grid: each wave owns 128 x 64 of the
 // fp32 accumulator (8 MFMA 32x32x16 blocks). Features stream through a 4-stage LDS ring in
 // chunks of 32 by direct global -> LDS copies, three chunks in flight while one is multiplied
@@ -58,6 +64,7 @@ struct MaxsimParams {
   int pairs;            // unordered pairs per sequence
   int64_t tiles;        // B * pairs
   float* scores;
+  int n_out;            // splits per sequence in the score matrix (n_s, or the real count when grouped)
 };
 
 // Unordered pair p of one sequence -> (i, j), i < j. Pairs come in bands of 4 target splits:
@@ -108,8 +115,11 @@ struct Unit {
 // every wave's older copies have landed in LDS and every wave is done with the previous stage.
 #define WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-template <bool kRow, bool kTail>
+// kG: splits per unit side (1, or 256 / S at S = 64 and 128, where a.S is 256 and a.n_s counts
+// the groups).
+template <bool kRow, bool kTail, int kG>
 __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
+  static_assert(kG == 1 || kG == 2 || kG == 4, "splits per unit side");
   // One LDS object per stage (target block, then candidate block): the compiler tracks copies
   // per object, so reads of one stage do not wait for copies into another. Stage 3 doubles as
   // the epilogue's row-max scratch.
@@ -119,9 +129,11 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   __shared__ __align__(16) float s_rnA[T];   // kRow: per target row 1 / |x_t| (0 for a zero token)
   __shared__ __align__(16) float s_rnB[T];   // kRow: per candidate row
   __shared__ float s_ssA[2 * T], s_ssB[2 * T];   // kRow: running sums of squares, [k-half][row]
-  __shared__ float s_cm[2][2][T];            // column maxima of the two row halves x two lane halves
+  // column maxima per row segment (the two row halves; at kG = 4 the four 64-row splits) x lane half
+  __shared__ float s_cm[kG == 4 ? 4 : 2][2][T];
   __shared__ float s_colmax[2 * T];          // running column maxima over target blocks (S = 512)
   __shared__ float s_red[8];
+  __shared__ float s_redg[8][kG];            // grouped units: per wave, one sum per split of the other side
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6), wm = wave >> 2, wn = wave & 3;
@@ -171,7 +183,13 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     const int64_t L = xs + tl;
     u.b = L / a.pairs;
     int i, j;
-    decode_pair((int)(L % a.pairs), a.n_s, i, j);
+    if (kG == 1) {
+      decode_pair((int)(L % a.pairs), a.n_s, i, j);
+    } else {
+      // pairs of groups I <= J: the unordered pairs I < J' of n_s + 1 with J = J' - 1
+      decode_pair((int)(L % a.pairs), a.n_s + 1, i, j);
+      j -= 1;
+    }
     u.i = uniform(i);
     u.j = uniform(j);
     u.ua = 0;
@@ -476,7 +494,12 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       if (kRow) asm volatile("" : "+v"(o));
       return reinterpret_cast<float*>(st3) + o + idx;
     };
-    float cm[2] = {-INFINITY, -INFINITY};
+    // column maxima over this wave's rows, per row segment: one (its 128 rows) unless kG = 4,
+    // where its two 64-row halves are different splits
+    constexpr int NH = kG == 4 ? 2 : 1;
+    float cm[NH][2];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) cm[h][0] = cm[h][1] = -INFINITY;
     auto reduce_store = [&](int ba, int g, const float (&m)[4]) {
       // step 1, lanes l and l ^ 1: the even lane keeps rows e = 0, 2, the odd lane e = 1, 3
       const float s0 = par ? m[0] : m[1], k0 = par ? m[1] : m[0];
@@ -494,7 +517,11 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       // Padding rows and columns repeat a valid token, so no mask is needed. Column direction:
       // the accumulators are scaled in place by rn_t, C_tu rn_t, and maximised over this wave's
       // rows; row direction: the scaled values times rn_u are the cosines, maximised over this
-      // wave's columns.
+      // wave's columns. At kG = 4 the column maxima are kept per slot and sorted into the two
+      // row halves afterwards (the slots are rotated by wn).
+      float cmS[kG == 4 ? 4 : 1][2];
+#pragma unroll
+      for (int s_ = 0; s_ < (kG == 4 ? 4 : 1); ++s_) cmS[s_][0] = cmS[s_][1] = -INFINITY;
 #pragma unroll
       for (int s_ = 0; s_ < 4; ++s_) {
         int lo = (lane >> 5) * 4;
@@ -509,11 +536,25 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 #pragma unroll
             for (int u_ = 0; u_ < 2; ++u_) {
               acc[s_][u_][g * 4 + e] *= rs4[e];
-              cm[u_] = fmaxf(cm[u_], acc[s_][u_][g * 4 + e]);
+              float& c = cmS[kG == 4 ? s_ : 0][u_];
+              c = fmaxf(c, acc[s_][u_][g * 4 + e]);
             }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u_ = 0; u_ < 2; ++u_) {
+        if (kG == 4) {
+#pragma unroll
+          for (int s_ = 0; s_ < 4; ++s_) {
+            const bool upper = ((s_ + rotA) & 2) != 0;   // block blkA(s_) lies in rows 64 .. 127
+            cm[NH - 1][u_] = upper ? fmaxf(cm[NH - 1][u_], cmS[kG == 4 ? s_ : 0][u_]) : cm[NH - 1][u_];
+            cm[0][u_] = upper ? cm[0][u_] : fmaxf(cm[0][u_], cmS[kG == 4 ? s_ : 0][u_]);
+          }
+        } else {
+          cm[0][u_] = cmS[0][u_];
+        }
       }
       float csc[2];
 #pragma unroll
@@ -540,8 +581,8 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
           for (int e = 0; e < 4; ++e) {
             const float c0 = acc[mb][0][g * 4 + e], c1 = acc[mb][1][g * 4 + e];
             m[e] = fmaxf(c0, c1);
-            cm[0] = fmaxf(cm[0], c0);
-            cm[1] = fmaxf(cm[1], c1);
+            cm[(mb >> 1) & (NH - 1)][0] = fmaxf(cm[(mb >> 1) & (NH - 1)][0], c0);
+            cm[(mb >> 1) & (NH - 1)][1] = fmaxf(cm[(mb >> 1) & (NH - 1)][1], c1);
           }
           reduce_store(mb, g, m);
         }
@@ -564,8 +605,8 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
           for (int e = 0; e < 4; ++e) {
             const float c0 = acc[mb][0][g * 4 + e], c1 = acc[mb][1][g * 4 + e];
             m[e] = fmaxf(c0 + cbi[0], c1 + cbi[1]);
-            cm[0] = fmaxf(cm[0], c0 + rb4[e]);
-            cm[1] = fmaxf(cm[1], c1 + rb4[e]);
+            cm[(mb >> 1) & (NH - 1)][0] = fmaxf(cm[(mb >> 1) & (NH - 1)][0], c0 + rb4[e]);
+            cm[(mb >> 1) & (NH - 1)][1] = fmaxf(cm[(mb >> 1) & (NH - 1)][1], c1 + rb4[e]);
           }
           reduce_store(mb, g, m);
         }
@@ -575,59 +616,129 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     // both lane halves store their column maxima (the owner of the column takes the max of the
     // four), so no cross-lane exchange is needed here
 #pragma unroll
-    for (int u_ = 0; u_ < 2; ++u_) s_cm[wm][lane >> 5][wn * 64 + blkB(u_) * 32 + (lane & 31)] = cm[u_];
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int u_ = 0; u_ < 2; ++u_) s_cm[wm * NH + h][lane >> 5][wn * 64 + blkB(u_) * 32 + (lane & 31)] = cm[h][u_];
     lds_sync();
-    if (is_row) {
-      // target row own: 8 quad maxima from each of the 4 waves that hold its columns
-      const int wr = own >> 7, rl = own & 127;
-      const float* p = reinterpret_cast<const float*>(st3) + wr * (4 * 128 * 8) + rl * 8;
-      float m = -INFINITY;
+    if constexpr (kG == 1) {
+      if (is_row) {
+        // target row own: 8 quad maxima from each of the 4 waves that hold its columns
+        const int wr = own >> 7, rl = own & 127;
+        const float* p = reinterpret_cast<const float*>(st3) + wr * (4 * 128 * 8) + rl * 8;
+        float m = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < 4; ++w) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int cc = ((c + (rl >> 3)) & 1) * 4;   // rotation: no bank conflicts
-          const float4 u = *reinterpret_cast<const float4*>(p + w * (128 * 8) + cc);
-          m = fmaxf(m, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
+          for (int c = 0; c < 2; ++c) {
+            const int cc = ((c + (rl >> 3)) & 1) * 4;   // rotation: no bank conflicts
+            const float4 u = *reinterpret_cast<const float4*>(p + w * (128 * 8) + cc);
+            m = fmaxf(m, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
+          }
         }
+        rmax = first_ub ? m : fmaxf(rmax, m);
+        if (last_ub && valid) part += rmax;
+      } else {
+        float cmv = fmaxf(fmaxf(s_cm[0][0][own], s_cm[0][1][own]), fmaxf(s_cm[1][0][own], s_cm[1][1][own]));
+        if (!first_ua) cmv = fmaxf(cmv, s_colmax[cur.ub * T + own]);
+        if (!last_ua) s_colmax[cur.ub * T + own] = cmv;
+        else if (valid) part += kRow ? cmv * s_rnB[own] : cmv;
       }
-      rmax = first_ub ? m : fmaxf(rmax, m);
-      if (last_ub && valid) part += rmax;
-    } else {
-      float cmv = fmaxf(fmaxf(s_cm[0][0][own], s_cm[0][1][own]), fmaxf(s_cm[1][0][own], s_cm[1][1][own]));
-      if (!first_ua) cmv = fmaxf(cmv, s_colmax[cur.ub * T + own]);
-      if (!last_ua) s_colmax[cur.ub * T + own] = cmv;
-      else if (valid) part += kRow ? cmv * s_rnB[own] : cmv;
-    }
 
-    if (last_ua && last_ub) {
-      // ---- scores of the pair; fixed reduction order (bitwise reproducible)
-      // within each 16-lane row by DPP (lane ^ 1, lane ^ 2, then the mirrors l <-> 7 - l within
-      // 8 lanes and l <-> 15 - l within 16), then the four row sums read from lanes 0, 16, 32 and
-      // 48: no LDS round trip on this dependency chain
-      float r = part;
-      r += __builtin_amdgcn_update_dpp(0.f, r, 0xB1, 0xF, 0xF, false);
-      r += __builtin_amdgcn_update_dpp(0.f, r, 0x4E, 0xF, 0xF, false);
-      r += __builtin_amdgcn_update_dpp(0.f, r, 0x141, 0xF, 0xF, false);
-      r += __builtin_amdgcn_update_dpp(0.f, r, 0x140, 0xF, 0xF, false);
-      auto lane_f = [&](int l) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), l));
-      };
-      const float rs = ((lane_f(0) + lane_f(16)) + lane_f(32)) + lane_f(48);
-      if (lane == 0) s_red[wave] = rs;
-      lds_sync();
-      if (tid == 0) {
-        const float tr = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
-        const float tc = ((s_red[4] + s_red[5]) + s_red[6]) + s_red[7];
-        float* sb = a.scores + cur.b * (int64_t)a.n_s * a.n_s;
-        sb[(int64_t)cur.i * a.n_s + cur.j] = tr;
-        sb[(int64_t)cur.j * a.n_s + cur.i] = tc;
-        if (cur.j == cur.i + 1) {
-          sb[(int64_t)cur.i * a.n_s + cur.i] = -INFINITY;
-          if (cur.j == a.n_s - 1) sb[(int64_t)cur.j * a.n_s + cur.j] = -INFINITY;
+      if (last_ua && last_ub) {
+        // ---- scores of the pair; fixed reduction order (bitwise reproducible)
+        // within each 16-lane row by DPP (lane ^ 1, lane ^ 2, then the mirrors l <-> 7 - l within
+        // 8 lanes and l <-> 15 - l within 16), then the four row sums read from lanes 0, 16, 32 and
+        // 48: no LDS round trip on this dependency chain
+        float r = part;
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0xB1, 0xF, 0xF, false);
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0x4E, 0xF, 0xF, false);
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0x141, 0xF, 0xF, false);
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0x140, 0xF, 0xF, false);
+        auto lane_f = [&](int l) {
+          return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), l));
+        };
+        const float rs = ((lane_f(0) + lane_f(16)) + lane_f(32)) + lane_f(48);
+        if (lane == 0) s_red[wave] = rs;
+        lds_sync();
+        if (tid == 0) {
+          const float tr = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
+          const float tc = ((s_red[4] + s_red[5]) + s_red[6]) + s_red[7];
+          float* sb = a.scores + cur.b * (int64_t)a.n_s * a.n_s;
+          sb[(int64_t)cur.i * a.n_s + cur.j] = tr;
+          sb[(int64_t)cur.j * a.n_s + cur.i] = tc;
+          if (cur.j == cur.i + 1) {
+            sb[(int64_t)cur.i * a.n_s + cur.i] = -INFINITY;
+            if (cur.j == a.n_s - 1) sb[(int64_t)cur.j * a.n_s + cur.j] = -INFINITY;
+          }
+        }
+        part = 0.f;
+      }
+    } else {
+      // ---- grouped unit: every pair between target split I kG + a and candidate split
+      // J kG + b. Row owner t (target split a = t / S): one maximum per candidate split b, over
+      // the quad maxima of the waves holding b's columns; column owner u (candidate split
+      // b = u / S): one maximum per target split a. Sums over the S rows (columns) of one split
+      // are per-wave DPP sums, then over the waves of the split, in a fixed order.
+      constexpr int WPS = 4 / kG;   // waves (of 64 rows or columns) per split
+      float pg[kG];
+      if (is_row) {
+        const int wr = own >> 7, rl = own & 127;
+        const float* p = reinterpret_cast<const float*>(st3) + wr * (4 * 128 * 8) + rl * 8;
+#pragma unroll
+        for (int b_ = 0; b_ < kG; ++b_) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int w = b_ * WPS; w < (b_ + 1) * WPS; ++w) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const int cc = ((c + (rl >> 3)) & 1) * 4;   // rotation: no bank conflicts
+              const float4 u = *reinterpret_cast<const float4*>(p + w * (128 * 8) + cc);
+              m = fmaxf(m, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
+            }
+          }
+          pg[b_] = valid ? m : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int a_ = 0; a_ < kG; ++a_) {
+          const float cmv = fmaxf(s_cm[a_][0][own], s_cm[a_][1][own]);
+          pg[a_] = valid ? (kRow ? cmv * s_rnB[own] : cmv) : 0.f;
         }
       }
-      part = 0.f;
+#pragma unroll
+      for (int v = 0; v < kG; ++v) {
+        float r = pg[v];
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0xB1, 0xF, 0xF, false);
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0x4E, 0xF, 0xF, false);
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0x141, 0xF, 0xF, false);
+        r += __builtin_amdgcn_update_dpp(0.f, r, 0x140, 0xF, 0xF, false);
+        auto lane_f = [&](int l) {
+          return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), l));
+        };
+        const float rs = ((lane_f(0) + lane_f(16)) + lane_f(32)) + lane_f(48);
+        if (lane == 0) s_redg[wave][v] = rs;
+      }
+      lds_sync();
+      if (tid < kG * kG) {
+        const int a_ = tid / kG, b_ = tid % kG;
+        float tr = 0.f, tc = 0.f;
+#pragma unroll
+        for (int w = 0; w < WPS; ++w) {
+          tr += s_redg[a_ * WPS + w][b_];        // rows of target split a_, maxima over b_
+          tc += s_redg[4 + b_ * WPS + w][a_];    // columns of candidate split b_, maxima over a_
+        }
+        const int si = cur.i * kG + a_, sj = cur.j * kG + b_;
+        if (si < a.n_out && sj < a.n_out) {
+          float* sb = a.scores + cur.b * (int64_t)a.n_out * a.n_out;
+          if (cur.i == cur.j) {
+            // a diagonal unit: the row direction gives every ordered pair inside the group
+            sb[(int64_t)si * a.n_out + sj] = a_ == b_ ? -INFINITY : tr;
+          } else {
+            sb[(int64_t)si * a.n_out + sj] = tr;
+            sb[(int64_t)sj * a.n_out + si] = tc;
+          }
+        }
+      }
     }
 
     if (!has_next) break;
@@ -638,17 +749,23 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   wait_vmem();    // the zero-filled copies issued past the last unit land before the exit
 }
 
+// Splits per unit side: 256 / S at S = 64 and 128, else 1.
+int group_of(int S) { return (S == 64 || S == 128) ? T / S : 1; }
+
 MaxsimParams params(const uint16_t* x, int64_t ld, int64_t B, int64_t N, int d, int S, float* scores) {
+  const int g = group_of(S);
   MaxsimParams p;
   p.x = x;
   p.ld = ld;
   p.N = N;
   p.d = d;
-  p.S = S;
-  p.n_s = (int)((N + S - 1) / S);
+  p.S = S * g;                              // rows of a unit side: a split, or a group of splits
+  p.n_s = (int)((N + p.S - 1) / p.S);
+  p.n_out = (int)((N + S - 1) / S);
   p.nk = (d + KH - 1) / KH;
-  p.q = (S + T - 1) / T;
-  p.pairs = (int)((int64_t)p.n_s * (p.n_s - 1) / 2);
+  p.q = (p.S + T - 1) / T;
+  // unordered pairs of splits, or of groups with the diagonal (a group's own pairs)
+  p.pairs = (int)(g == 1 ? (int64_t)p.n_s * (p.n_s - 1) / 2 : (int64_t)p.n_s * (p.n_s + 1) / 2);
   p.tiles = B * (int64_t)p.pairs;
   p.scores = scores;
   return p;
@@ -667,17 +784,29 @@ int64_t grid_for(int64_t tiles) {
 hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
                               hipStream_t stream) {
   const MaxsimParams p = params(xp, 0, B, N, d, S, scores);
-  hipLaunchKernelGGL((maxsim_bf16_kernel<false, false>), dim3((unsigned)grid_for(p.tiles)), dim3(512), 0, stream, p);
+  const dim3 grid((unsigned)grid_for(p.tiles));
+  switch (group_of(S)) {
+    case 4: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 4>), grid, dim3(512), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 2>), grid, dim3(512), 0, stream, p); break;
+    default: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 1>), grid, dim3(512), 0, stream, p); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_maxsim_rows_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld, int S, float* scores,
                                    hipStream_t stream) {
   const MaxsimParams p = params(x, ld, B, N, d, S, scores);
-  if (d % KH)
-    hipLaunchKernelGGL((maxsim_bf16_kernel<true, true>), dim3((unsigned)grid_for(p.tiles)), dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((maxsim_bf16_kernel<true, false>), dim3((unsigned)grid_for(p.tiles)), dim3(512), 0, stream, p);
+  const dim3 grid((unsigned)grid_for(p.tiles));
+  const int g = group_of(S);
+  if (d % KH) {
+    if (g == 4) hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 4>), grid, dim3(512), 0, stream, p);
+    else if (g == 2) hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 2>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 1>), grid, dim3(512), 0, stream, p);
+  } else {
+    if (g == 4) hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 4>), grid, dim3(512), 0, stream, p);
+    else if (g == 2) hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 2>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 1>), grid, dim3(512), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ extern "C" avey_status avey_split_rank_noalloc(const void* x, avey_dtype dt, int
     const int64_t nb = B - b0 < per_pass ? B - b0 : per_pass;
     const void* xb = static_cast<const uint8_t*>(x) + b0 * N * ld_x * eb;
     float* sb = scores + b0 * n_s * n_s;
-    AVEY_TRY(hip_status(launch_prepare(xb, dt == AVEY_BF16, nb, N, (int)d, ld_x, S, ws, st)));
+    AVEY_TRY(hip_status(launch_prepare(xb, dt == AVEY_BF16, nb, N, (int)d, ld_x, pack_rows(dt, S), ws, st)));
     if (dt == AVEY_BF16)
       AVEY_TRY(hip_status(launch_maxsim_bf16(static_cast<const uint16_t*>(ws), nb, N, (int)d, S, sb, st)));
     else

@@ -95,13 +95,15 @@ avey_status avey_maxsim(const void* x, avey_dtype dt, int64_t B, int64_t N, int6
  * Explicit-workspace scoring: the same scores as avey_maxsim from a normalised, zero-padded copy
  * of X in caller-provided device memory: n_t = N(x_t) = x_t / |x_t| (sum of squares in fp32;
  * N(0) = 0) for t < N, zero rows for the padding tokens of the last split ([notes] 关键设计 2;
- * 整体框架). Its layout is internal to the library (bf16: split-packed chunk planes of 32
- * features, features padded with zeros to a multiple of 32; fp32: row-major n_s * S rows).
+ * 整体框架). Its layout is internal to the library (bf16: packed block by block in chunk planes
+ * of 32 features, features padded with zeros to a multiple of 32, a block being one split, or
+ * 256 consecutive tokens at S = 64 and 128; fp32: row-major n_s * S rows).
  *
  * avey_rank_workspace_bytes -- size in bytes of that workspace for (dt, B, N, d, S):
- * B * n_s * S * d' * (2 for AVEY_BF16, 4 for AVEY_F32) with d' = d rounded up to a multiple of 32
- * for AVEY_BF16 (d for AVEY_F32), 0 for empty work, or a negative avey_status if the shape is
- * rejected (the same checks as avey_maxsim_prepare).
+ * B * ceil(N / P) * P * d' * (2 for AVEY_BF16, 4 for AVEY_F32) with P = S (P = 256 for AVEY_BF16
+ * at S = 64 and 128) and d' = d rounded up to a multiple of 32 for AVEY_BF16 (d for AVEY_F32),
+ * 0 for empty work, or a negative avey_status if the shape is rejected (the same checks as
+ * avey_maxsim_prepare).
  */
 int64_t avey_rank_workspace_bytes(avey_dtype dt, int64_t B, int64_t N, int64_t d, int32_t S);
 

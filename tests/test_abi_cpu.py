@@ -87,6 +87,10 @@ def test_workspace_prepare_and_scores_validation(lib):
     n = lib.avey_rank_workspace_bytes
     assert n(1, 2, 32768, 768, 256) == 2 * 128 * 256 * 768 * 2
     assert n(1, 1, 1000, 72, 64) == 1 * 16 * 64 * 96 * 2                # bf16 d padded to 32
+    assert n(1, 1, 1100, 64, 64) == 1 * 5 * 256 * 64 * 2                 # bf16 S = 64: blocks of 256 tokens
+    assert n(1, 1, 1100, 64, 128) == 1 * 5 * 256 * 64 * 2                # bf16 S = 128 likewise
+    assert n(1, 1, 1100, 64, 48) == 1 * 23 * 48 * 64 * 2                 # other S: blocks of one split
+    assert n(0, 1, 1100, 64, 64) == 1 * 18 * 64 * 64 * 4                 # fp32: splits
     assert n(0, 1, 1000, 72, 64) == 1 * 16 * 64 * 72 * 4                 # fp32 d as it is
     assert n(0, 1, 1000, 64, 64) == 1 * 16 * 64 * 64 * 4                 # padded to whole splits
     assert n(1, 0, 1000, 64, 64) == 0

@@ -190,11 +190,12 @@ def test_full_size_sampled(gpu_ok, name):
     assert np.isfinite(g["xhat"]).all() and np.isfinite(g["out"]).all()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prepare_normalises_and_pads(gpu_ok, dtype):
-    """The ranker workspace holds the oracle's N(x) (bf16: rounded, in split-packed chunk
-    planes; fp32: row-major) and zero rows for the padding tokens of the last split."""
-    cfg = Config("prep_" + dtype, B=2, N=1000, d=128, S=64, k=2, m_t=64, m=128, dtype=dtype,
+@pytest.mark.parametrize("dtype,S", [("bf16", 64), ("bf16", 48), ("f32", 64)])
+def test_prepare_normalises_and_pads(gpu_ok, dtype, S):
+    """The ranker workspace holds the oracle's N(x) (bf16: rounded, packed block by block in
+    chunk planes, a block being a split or, at S = 64 and 128, 256 consecutive tokens; fp32:
+    row-major) and zero rows for the padding tokens after N."""
+    cfg = Config("prep_" + dtype, B=2, N=1000, d=128, S=S, k=2, m_t=64, m=128, dtype=dtype,
                  x_dist="mixture", n_centroids=8)
     inp = make_inputs(cfg)
     say(f"maxsim_prepare {dtype} B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S}")
@@ -202,12 +203,15 @@ def test_prepare_normalises_and_pads(gpu_ok, dtype):
     x[1, 17].zero_()
     ws = A.avey_maxsim_prepare(x, cfg.S)
     torch.cuda.synchronize()
-    n_s, S, d = cfg.n_s, cfg.S, cfg.d
+    d = cfg.d
+    P = 256 if dtype == "bf16" and S in (64, 128) else S      # rows per packed block
+    n_p = -(-cfg.N // P)
+    assert ws.numel() == cfg.B * n_p * P * d * (2 if dtype == "bf16" else 4)
     if dtype == "bf16":
-        got = ws[: cfg.B * n_s * S * d * 2].view(torch.bfloat16).float()
-        got = got.reshape(cfg.B, n_s, d // 32, S, 32).permute(0, 1, 3, 2, 4).reshape(cfg.B, n_s * S, d)
+        got = ws[: cfg.B * n_p * P * d * 2].view(torch.bfloat16).float()
+        got = got.reshape(cfg.B, n_p, d // 32, P, 32).permute(0, 1, 3, 2, 4).reshape(cfg.B, n_p * P, d)
     else:
-        got = ws[: cfg.B * n_s * S * d * 4].view(torch.float32).reshape(cfg.B, n_s * S, d)
+        got = ws[: cfg.B * n_p * P * d * 4].view(torch.float32).reshape(cfg.B, n_p * P, d)
     got = got.cpu().numpy().astype(np.float64)
     xs = host_f64(x)
     assert np.all(got[:, cfg.N:] == 0.0)
@@ -361,6 +365,14 @@ RANK_SHAPES = {
                         x_dist="mixture", n_centroids=16),
     "S512_d40": Config("r512", B=2, N=2100, d=40, S=512, k=3, m_t=64, m=64, dtype="bf16",
                        x_dist="mixture", n_centroids=16),
+    # S = 64 and 128: units of 256 / S splits per side; ragged last split and last group
+    "S64_d136": Config("r64", B=2, N=1500, d=136, S=64, k=3, m_t=64, m=64, dtype="bf16",
+                       x_dist="mixture", n_centroids=16),
+    "S128_d64": Config("r128", B=2, N=1000, d=64, S=128, k=2, m_t=64, m=64, dtype="bf16",
+                       x_dist="mixture", n_centroids=16),
+    # one group only: every pair inside a single diagonal unit
+    "S64_one_group": Config("r64g", B=1, N=200, d=64, S=64, k=2, m_t=64, m=64, dtype="bf16",
+                            x_dist="mixture", n_centroids=8),
 }
 
 

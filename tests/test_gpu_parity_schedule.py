@@ -39,6 +39,10 @@ CASES = {
     # 79 splits per sequence, the last one 32 tokens: 9243 tiles over 3 sequences
     "ragged_many": Config("ragged_many", B=3, N=20000, d=128, S=256, k=3, m_t=128, m=256, dtype="bf16",
                           x_dist="mixture", n_centroids=64),
+    # S = 64: 4 splits per unit side, 256 splits per sequence (the last one 16 tokens), 64 groups:
+    # 4160 units over 2 sequences, 64 of them diagonal
+    "s64_many": Config("s64_many", B=2, N=16336, d=128, S=64, k=3, m_t=128, m=256, dtype="bf16",
+                       x_dist="mixture", n_centroids=64),
 }
 
 
@@ -52,7 +56,11 @@ def test_all_outputs_many_tiles(gpu_ok, name):
     cfg = CASES[name]
     tol = TOL[cfg.dtype]
     pairs = cfg.B * cfg.n_s * (cfg.n_s - 1) // 2
-    units = pairs * (-(-cfg.S // 256)) ** 2
+    if cfg.S in (64, 128):                       # units of 256 / S splits per side, diagonal included
+        groups = -(-cfg.N // 256)
+        units = cfg.B * groups * (groups + 1) // 2
+    else:
+        units = pairs * (-(-cfg.S // 256)) ** 2
     say(f"{name}: B={cfg.B} N={cfg.N} d={cfg.d} S={cfg.S} k={cfg.k}: {pairs} pairs, {units} MaxSim units")
     inp = make_inputs(cfg)
     x, P, z, z_tail = upload(inp)
