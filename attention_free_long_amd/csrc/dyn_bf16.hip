@@ -28,6 +28,10 @@ struct DynParams {
   uint16_t* out;
   int64_t N, ld_z, ld_out, tiles;
   int m_t, S, n_s, pgroups;
+  // S = 64 and 128 (ring kernel): a workgroup takes 256 / S consecutive splits (S above is then
+  // 256 and n_s counts the groups) and mixes tokens p, q only when p >> gshift == q >> gshift;
+  // otherwise gshift is 8 and seg == S.
+  int seg, gshift;
   float eps;
   LayerEpi epi;
 };
@@ -46,12 +50,13 @@ __device__ __forceinline__ float layer_bias(const LayerEpi& e, int p, bool p_ok)
 // row's scale is computed from, over the rounded weights: their sum (sum, softmax) or the sum
 // of their squares (rms). Softmax weights are exp(G_pq) for valid q and 0 for padding q.
 __device__ __forceinline__ void g_weights(float g0, float g1, float g2, float g3, int q0, int nvalid, int norm,
-                                          uint32_t& lo, uint32_t& hi, float& stat) {
+                                          uint32_t& lo, uint32_t& hi, float& stat, bool keep = true) {
+  if (!keep) g0 = g1 = g2 = g3 = 0.f;   // q0 .. q0 + 3 belong to another split than p
   if (norm == kNormSoftmax) {
-    g0 = q0 + 0 < nvalid ? __expf(g0) : 0.f;
-    g1 = q0 + 1 < nvalid ? __expf(g1) : 0.f;
-    g2 = q0 + 2 < nvalid ? __expf(g2) : 0.f;
-    g3 = q0 + 3 < nvalid ? __expf(g3) : 0.f;
+    g0 = keep && q0 + 0 < nvalid ? __expf(g0) : 0.f;
+    g1 = keep && q0 + 1 < nvalid ? __expf(g1) : 0.f;
+    g2 = keep && q0 + 2 < nvalid ? __expf(g2) : 0.f;
+    g3 = keep && q0 + 3 < nvalid ? __expf(g3) : 0.f;
   }
   lo = pack_bf16(g0, g1);
   hi = pack_bf16(g2, g3);
@@ -113,10 +118,11 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   const int64_t base = (int64_t)i * a.S;
   const int valid_rows = (int)min((int64_t)a.S, a.N - base);
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
-  const int p = wave * 32 + (lane & 31);          // this lane's output token (split-local)
+  const int p = wave * 32 + (lane & 31);          // this lane's output token (in the workgroup's rows)
   const bool p_ok = p < valid_rows;
   const bool relu = a.epi.act != 0;
-  const float bv = layer_bias(a.epi, p, p_ok);
+  const int pseg = p >> a.gshift;                 // p's split among the workgroup's (0 unless grouped)
+  const float bv = layer_bias(a.epi, p - (pseg << a.gshift), p_ok);   // bias of p's position in its split
   const int nk1 = (a.m_t + KC - 1) / KC;          // phase-1 chunks of 64 features (last partial)
   const int nk1p = (nk1 + 3) / 4 * 4;             // padded with zero chunks to a multiple of 4
   const int nft = (a.m_t + FT - 1) / FT;
@@ -232,13 +238,15 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
           const float4 rq = *reinterpret_cast<const float4*>(&s_rn[q0]);
           const int v0 = s2 * 8 + h * 4;
           g_weights(acc1[qb][v0 + 0] * rq.x * rnp, acc1[qb][v0 + 1] * rq.y * rnp, acc1[qb][v0 + 2] * rq.z * rnp,
-                    acc1[qb][v0 + 3] * rq.w * rnp, q0, valid_rows, a.epi.norm, pk[2 * h + 0], pk[2 * h + 1], r);
+                    acc1[qb][v0 + 3] * rq.w * rnp, q0, valid_rows, a.epi.norm, pk[2 * h + 0], pk[2 * h + 1], r,
+                    (q0 >> a.gshift) == pseg);
         }
         gfrag[qb][s2] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     }
     r += __shfl_xor(r, 32);
-    inv = row_scale(a.epi.norm, r, a.eps, valid_rows);
+    // valid tokens of p's split (the RMS mean runs over them)
+    inv = row_scale(a.epi.norm, r, a.eps, min(a.seg, valid_rows - (pseg << a.gshift)));
   }
 
   // ---- phase 2. G fragment (qb, s2) of lane half h holds q = 32 qb + 16 s2 + {4h .. 4h+3,
@@ -626,10 +634,16 @@ hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int
   p.N = N; p.ld_z = ld_z; p.ld_out = ld_out;
   p.m_t = m_t; p.S = S; p.eps = eps;
   p.epi = epi;
-  p.n_s = (int)((N + S - 1) / S);
+  p.seg = S;
+  p.gshift = 8;
+  if (S == 64 || S == 128) {   // 256 / S splits per workgroup
+    p.S = 256;
+    p.gshift = S == 64 ? 6 : 7;
+  }
+  p.n_s = (int)((N + p.S - 1) / p.S);
   p.tiles = B * p.n_s;
   p.pgroups = 1;
-  if (S <= 256) {
+  if (p.S <= 256) {
     hipLaunchKernelGGL(ring::dyn_ring_kernel, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
     return hipGetLastError();
   }

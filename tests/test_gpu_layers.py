@@ -28,9 +28,12 @@ CASES = {
     # S = 512 (two 256-token halves per split), last split 40 tokens
     "s512_bf16": Config("s512_bf16", B=1, N=1576, d=128, S=512, k=2, m_t=192, m=256, dtype="bf16",
                         x_dist="mixture", n_centroids=16),
-    # S = 64: a quarter of an output tile per split
+    # S = 64: four splits per workgroup of the dynamic layer, the last group partial
     "s64_bf16": Config("s64_bf16", B=1, N=700, d=64, S=64, k=2, m_t=64, m=128, dtype="bf16",
                        x_dist="mixture", n_centroids=8),
+    # S = 128: two splits per workgroup; the last split 4 tokens, alone in a partial group
+    "s128_bf16": Config("s128_bf16", B=2, N=900, d=64, S=128, k=2, m_t=136, m=200, dtype="bf16",
+                        x_dist="mixture", n_centroids=8),
     "tiny": CONFIGS["tiny"],
     # S = 208 and m_t = 72 (multiples of 16 and 8 only): partial chunks in both layers
     "s208_bf16": Config("s208_bf16", B=1, N=1500, d=64, S=208, k=2, m_t=72, m=136, dtype="bf16",
