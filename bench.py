@@ -36,10 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("e6aba5177f49f27a", "long"): {"fetch_kib": 1207862.7, "fetch_scale": 1.99992,
-                                           "write_kib": 253.0, "write_scale": 1.0},
-            ("e6aba5177f49f27a", "extreme"): {"fetch_kib": 5339630.3, "fetch_scale": 1.99992,
-                                              "write_kib": 1563.3, "write_scale": 1.0},
+            ("2396f7bd914b1be6", "long"): {"fetch_kib": 1177182.3, "fetch_scale": 1.99992,
+                                           "write_kib": 272.4, "write_scale": 1.0},
+            ("2396f7bd914b1be6", "extreme"): {"fetch_kib": 6684500.6, "fetch_scale": 1.99992,
+                                              "write_kib": 2134.0, "write_scale": 1.0},
         },
     },
 }
