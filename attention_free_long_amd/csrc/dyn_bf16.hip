@@ -77,6 +77,11 @@ __device__ __forceinline__ float layer_out(float v, float scale, float bv, bool 
   const float y = fmaf(v, scale, bv);
   return relu ? fmaxf(y, 0.f) : y;
 }
+template <bool kRelu>
+__device__ __forceinline__ float layer_out(float v, float scale, float bv) {
+  const float y = fmaf(v, scale, bv);
+  return kRelu ? fmaxf(y, 0.f) : y;
+}
 
 // ---------------------------------------------------------------------------------------------
 // S <= 256: one 8-wave workgroup per split, both GEMMs fed by one 4-stage ring of 32 KiB
@@ -84,16 +89,20 @@ __device__ __forceinline__ float layer_out(float v, float scale, float bv, bool 
 //   Phase 1, chunk kc: Z rows q = 0..255 x features 64 kc .. +63 (128-byte LDS rows). Wave w
 //   owns p = 32 w .. 32 w + 31: C1[q][p] over all 256 q (8 MFMA blocks); the squared norms of
 //   its p rows come from the B fragments it reads anyway.
-//   Phase 2, chunk (ft, qc): Z rows q = 64 qc .. +63 x features 256 ft .. +255 (512-byte LDS
+//   Phase 2, chunk (ft, qh): Z rows q = 128 qh .. +127 x features 128 ft .. +127 (256-byte LDS
 //   rows), read as Z^T fragments by the LDS transpose read, times the G fragments the wave
-//   holds in registers: O^T[f][p] for 256 features x its 32 p.
+//   holds in registers: O^T[f][p] for 128 features x its 32 p, two chunks per feature tile.
 // The phase-2 chunks stream without waiting for phase 1's result: only their products do.
+// In both phases a wave reads the next k-step's fragments while the current one's MFMAs run,
+// which the 128-feature tiles leave registers for (G alone takes 64 per lane).
 namespace ring {
 
 constexpr int QR = 256;                 // q rows per split (padded)
 constexpr int STAGE = QR * ROWB;        // 32 KiB: phase 1 chunk (256 x 64 features)
-constexpr int ZB = 512;                 // phase 2 LDS row: 256 features
-constexpr int FT = 256;                 // phase 2 features per tile
+constexpr int ZB = 512;                 // S <= 512 kernel, phase 2 LDS row: 256 features
+constexpr int FT = 256;                 // S <= 512 kernel, phase 2 features per tile
+constexpr int ZR = 256;                 // S <= 256 kernel, phase 2 LDS row: 128 features
+constexpr int FR = 128;                 // S <= 256 kernel, phase 2 features per tile
 
 __device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* base, uint32_t off) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -104,6 +113,7 @@ __device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* base, uint32_t off)
 
 #define DYN_WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+template <bool kRelu>
 __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   __shared__ float s_sq[QR];
@@ -120,18 +130,17 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
   const int p = wave * 32 + (lane & 31);          // this lane's output token (in the workgroup's rows)
   const bool p_ok = p < valid_rows;
-  const bool relu = a.epi.act != 0;
   const int pseg = p >> a.gshift;                 // p's split among the workgroup's (0 unless grouped)
   const float bv = layer_bias(a.epi, p - (pseg << a.gshift), p_ok);   // bias of p's position in its split
   const int nk1 = (a.m_t + KC - 1) / KC;          // phase-1 chunks of 64 features (last partial)
   const int nk1p = (nk1 + 3) / 4 * 4;             // padded with zero chunks to a multiple of 4
-  const int nft = (a.m_t + FT - 1) / FT;
+  const int nft = (a.m_t + FR - 1) / FR;          // phase-2 feature tiles (two chunks each)
 
   // ---- copies: 4 per wave per chunk, zeros when !valid or out of range. The two phases have
   // separate copy routines, chosen at compile time at every call site: a run-time branch
   // between them would join control flow around the copies, after which the compiler drains
   // all copies before the next LDS read.
-  auto copy1 = [&](int c, uint8_t* st, bool valid, int n) {
+  auto copy1 = [&](int c, uint8_t* st, bool valid, int n) __attribute__((always_inline)) {
     // rows 32 w + 8 n .. + 7 of chunk c, 128 bytes each; lane -> row (ln >> 3), position (ln & 7);
     // 16-byte pieces past m_t (the last chunk when m_t % 64 != 0) load zeros
     int ln = lane;
@@ -142,19 +151,19 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     dma16(zr, st + (wave * 32 + n * 8) * ROWB, ok ? (uint32_t)((base + row) * a.ld_z * 2) + 16u * pc : OOB,
           (uint32_t)c * KC * 2u);
   };
-  auto copy2 = [&](int c2, uint8_t* st, bool valid, int n) {
-    // rows 8 w + 2 n, + 1 (512 bytes each) of q chunk qc, f tile ft; 32-byte piece
-    // (p >> 1) ^ 2 (t & 3) of row t
+  auto copy2 = [&](int c2, uint8_t* st, bool valid, int n) __attribute__((always_inline)) {
+    // rows 16 w + 4 n .. + 3 (256 bytes each) of q half qh, f tile ft; LDS 32-byte slot s of row
+    // t holds the row's 32-byte piece s ^ 2 (t & 3)
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int ft = c2 >> 2, qc = c2 & 3;
-    const int t = wave * 8 + n * 2 + (ln >> 5);
-    const int q = qc * 64 + t;
-    const int pp = ln & 31;
+    const int ft = c2 >> 1, qh = c2 & 1;
+    const int t = wave * 16 + n * 4 + (ln >> 4);
+    const int q = qh * 128 + t;
+    const int pp = ln & 15;
     const int pc = (pp >> 1) ^ (2 * (t & 3));
-    const int f = ft * FT + pc * 16 + (pp & 1) * 8;
-    const bool ok = valid && c2 < 4 * nft && q < valid_rows && f < a.m_t;
-    dma16(zr, st + (wave * 8 + n * 2) * ZB, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
+    const int f = ft * FR + pc * 16 + (pp & 1) * 8;
+    const bool ok = valid && c2 < 2 * nft && q < valid_rows && f < a.m_t;
+    dma16(zr, st + (wave * 16 + n * 4) * ZR, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
   };
 
   // ---- phase 1
@@ -167,17 +176,45 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc1[qb][v] = 0.f;
   float sq = 0.f;
-  // one chunk of MFMAs from stage st; issue(ks) issues the ks-th copy of a later chunk
-  auto compute1 = [&](const uint8_t* st, auto&& issue) {
+  // Fragments of the k-step being multiplied: ra for the 8 q blocks, rb for this wave's p block.
+  // The next k-step's are read in two halves, each right after the MFMAs that last read those
+  // registers are issued, so that the reads run under the other half's MFMAs. A chunk's last
+  // k-step reads the next chunk's first one the same way, after the wait and barrier for that
+  // chunk, which therefore sit between the two MFMA halves.
+  // The fragment offsets are laundered through an empty asm at each read, so that the stage
+  // base is added there: hoisted, the sums for every stage would be long-lived registers.
+  uint4 ra[8], rb, rbn;
+  auto read1 = [&](const uint8_t* st, int ks, int h) __attribute__((always_inline)) {
+    if (h == 0) {
+      uint32_t o = fp[ks];
+      asm volatile("" : "+v"(o));
+      rbn = lds_read16(st, o);
+    }
+    uint32_t o = fq[ks];
+    asm volatile("" : "+v"(o));
+#pragma unroll
+    for (int qb = 4 * h; qb < 4 * h + 4; ++qb) ra[qb] = lds_read16(st, o + qb * 32 * ROWB);
+  };
+  // One chunk of MFMAs from stage st, whose first k-step is in ra / rb; issue(ks) issues the
+  // ks-th copy of a later chunk; next is the following chunk's stage (nullptr: none).
+  auto compute1 = [&](const uint8_t* st, auto&& issue, const uint8_t* next) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint4 rb = lds_read16(st, fp[ks]);
-      uint4 ra[8];
-#pragma unroll
-      for (int qb = 0; qb < 8; ++qb) ra[qb] = lds_read16(st, fq[ks] + qb * 32 * ROWB);
       sq = sumsq8(rb, sq);
 #pragma unroll
-      for (int qb = 0; qb < 8; ++qb) acc1[qb] = mfma32(as_bf16x8(ra[qb]), as_bf16x8(rb), acc1[qb]);
+      for (int qb = 0; qb < 4; ++qb) acc1[qb] = mfma32(as_bf16x8(ra[qb]), as_bf16x8(rb), acc1[qb]);
+      if (ks < 3) {
+        read1(st, ks + 1, 0);
+      } else if (next) {
+        DYN_WAIT_KEEP(7);   // 3 of this chunk's copies and the 4 of the previous one may stay in flight
+        read1(next, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qb = 4; qb < 8; ++qb) acc1[qb] = mfma32(as_bf16x8(ra[qb]), as_bf16x8(rb), acc1[qb]);
+      if (ks < 3) read1(st, ks + 1, 1);
+      else if (next) read1(next, 0, 1);
+      rb = rbn;
       issue(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -188,27 +225,23 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   for (int n = 0; n < 4; ++n) copy1(0, st0, true, n);
   for (int n = 0; n < 4; ++n) copy1(1, st1, true, n);
   for (int n = 0; n < 4; ++n) copy1(2, st2, true, n);
+  DYN_WAIT_KEEP(8);
+  read1(st0, 0, 0);
+  read1(st0, 0, 1);
+  rb = rbn;
   for (int kc = 0; kc + 4 < nk1p; kc += 4) {
-    DYN_WAIT_KEEP(8);
-    compute1(st0, c1(kc + 3, st3));
-    DYN_WAIT_KEEP(8);
-    compute1(st1, c1(kc + 4, st0));
-    DYN_WAIT_KEEP(8);
-    compute1(st2, c1(kc + 5, st1));
-    DYN_WAIT_KEEP(8);
-    compute1(st3, c1(kc + 6, st2));
+    compute1(st0, c1(kc + 3, st3), st1);
+    compute1(st1, c1(kc + 4, st0), st2);
+    compute1(st2, c1(kc + 5, st1), st3);
+    compute1(st3, c1(kc + 6, st2), st0);
   }
   {
     // last four phase-1 chunks; the first three phase-2 chunks are copied meanwhile
     const int kc = nk1p - 4;
-    DYN_WAIT_KEEP(8);
-    compute1(st0, c1(kc + 3, st3));
-    DYN_WAIT_KEEP(8);
-    compute1(st1, c2(0, st0));
-    DYN_WAIT_KEEP(8);
-    compute1(st2, c2(1, st1));
-    DYN_WAIT_KEEP(8);
-    compute1(st3, c2(2, st2));
+    compute1(st0, c1(kc + 3, st3), st1);
+    compute1(st1, c2(0, st0), st2);
+    compute1(st2, c2(1, st1), st3);
+    compute1(st3, c2(2, st2), nullptr);
   }
 
   // ---- norms, G (bf16) as phase-2 B fragments, r_p from the rounded values
@@ -251,93 +284,126 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
 
   // ---- phase 2. G fragment (qb, s2) of lane half h holds q = 32 qb + 16 s2 + {4h .. 4h+3,
   // 8+4h .. 8+4h+3}; the Z^T fragments are read with the same q order (two transpose reads:
-  // tokens +4h and +8+4h), features 32 fb + (l & 31).
-  uint32_t offZ[8];
+  // tokens +4h and +8+4h), features 32 fb + (l & 31). The offset of block fb in a chunk row is
+  // ((2 fb + g1) ^ 2 s2x) * 32 + 8 (l & 3), so the fragment offset is offZ0 ^ (fb << 6) (the
+  // row, lane and g1 terms fill other bits): one register for all four blocks.
+  uint32_t offZ0;
   {
     const int s2x = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
-    const uint32_t row = (uint32_t)(4 * (lane >> 5) + ((lane & 15) >> 2)) * ZB;
-#pragma unroll
-    for (int fb = 0; fb < 8; ++fb)
-      offZ[fb] = row + (uint32_t)(((2 * fb + g1) ^ (2 * s2x)) << 5) + 8u * (lane & 3);
+    const uint32_t row = (uint32_t)(4 * (lane >> 5) + ((lane & 15) >> 2)) * ZR;
+    offZ0 = row + (uint32_t)((g1 << 5) | (s2x << 6)) + 8u * (lane & 3);
   }
-  f32x16 acc2[8];
+  f32x16 acc2[4];
   const f32x16 zero16 = {};
-  auto compute2 = [&](const uint8_t* st, auto qc_tag, int cnext, uint8_t* dst) {
-    // cnext: phase-2 chunk index of the copies issued meanwhile
-    constexpr int qc = decltype(qc_tag)::value;
+  uint4 rz[4], rzn[4];   // Z^T fragments of the k-step being multiplied and of the next one
+  auto read2 = [&](const uint8_t* st, int ks) __attribute__((always_inline)) {   // token rows 16 ks .. +15
+    uint32_t o0 = offZ0;
+    asm volatile("" : "+v"(o0));
+    const uint32_t tok = (uint32_t)(16 * ks) * ZR;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {                 // (qb_local, s2) = (ks >> 1, ks & 1)
-      const int qbl = ks >> 1, s2 = ks & 1;
-      const uint32_t tok = (uint32_t)(32 * qbl + 16 * s2) * ZB;
-      uint4 ra[8];
+    for (int fb = 0; fb < 4; ++fb) {
+      const uint32_t o = o0 ^ ((uint32_t)fb << 6);
+      const uint2 lo = lds_read_tr8(st, o + tok);
+      const uint2 hi = lds_read_tr8(st, o + tok + 8 * ZR);
+      rzn[fb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
+  // One chunk (q half qh of a feature tile) from stage st, whose first k-step is in rzn; the
+  // copies of phase-2 chunk cnext into dst go out at k-steps 0, 2, 4 and 6. With next, the
+  // following chunk's wait and barrier sit between the two MFMA halves of the last k-step, and
+  // its first k-step is read there: 4 copies of the chunk after it and the 4 of this chunk may
+  // stay in flight, and (after_epi) the 8 stores of the epilogue before this chunk.
+  auto compute2 = [&](const uint8_t* st, auto qh_tag, int cnext, uint8_t* dst, const uint8_t* next,
+                      auto after_epi) __attribute__((always_inline)) {
+    constexpr int qh = decltype(qh_tag)::value;
 #pragma unroll
-      for (int fb = 0; fb < 8; ++fb) {
-        const uint2 lo = lds_read_tr8(st, offZ[fb] + tok);
-        const uint2 hi = lds_read_tr8(st, offZ[fb] + tok + 8 * ZB);
-        ra[fb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-      const uint4 gb = gfrag[2 * qc + qbl][s2];
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) rz[fb] = rzn[fb];
+      const uint4 gb = gfrag[4 * qh + (ks >> 1)][ks & 1];
       // the tile's first k-step starts the accumulators from an inline zero
-      const bool first = qc == 0 && ks == 0;
+      const bool first = qh == 0 && ks == 0;
+      if (ks < 7) read2(st, ks + 1);
 #pragma unroll
-      for (int fb = 0; fb < 8; ++fb) acc2[fb] = mfma32(as_bf16x8(ra[fb]), as_bf16x8(gb), first ? zero16 : acc2[fb]);
-      copy2(cnext, dst, true, ks);
+      for (int fb = 0; fb < 2; ++fb) acc2[fb] = mfma32(as_bf16x8(rz[fb]), as_bf16x8(gb), first ? zero16 : acc2[fb]);
+      if (ks == 7 && next) {
+        if constexpr (decltype(after_epi)::value) DYN_WAIT_KEEP(16); else DYN_WAIT_KEEP(8);
+        read2(next, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fb = 2; fb < 4; ++fb) acc2[fb] = mfma32(as_bf16x8(rz[fb]), as_bf16x8(gb), first ? zero16 : acc2[fb]);
+      if ((ks & 1) == 0) copy2(cnext, dst, true, ks >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Epilogue of feature tile ft, through stage 3 in four rounds of 64 features: each lane writes
-  // its 4-feature groups into a [256 tokens][64 features] bf16 tile (16-byte piece c of row t at
-  // c ^ ((t >> 1) & 7)), then 8 lanes per token store whole 128-byte row pieces (scattered
-  // 8-byte stores would cost a write request per lane). Every wave issues exactly 16 stores per
-  // tile (lanes past the split or past m_t store out of range), which the next tile's first three
-  // copy waits allow for: the stores drain under the MFMAs instead of holding up the next tile.
+  // Epilogue of feature tile ft, staged through stage sst (the tile's second chunk, done) in two
+  // rounds of 64 features: each lane writes its 4-feature groups into a [256 tokens][64 features]
+  // bf16 tile (16-byte piece c of row t at c ^ ((t >> 1) & 7)), then 8 lanes per token store
+  // whole 128-byte row pieces (scattered 8-byte stores would cost a write request per lane, and
+  // 64-byte pieces measured slower). A wave writes and reads only its own 32 rows, so after the
+  // first barrier (every wave is done reading the stage) it needs none. Every wave issues exactly
+  // 8 stores per tile (lanes past the split or past m_t store out of range), which the next
+  // tile's waits allow for: the stores drain under the MFMAs instead of holding up the next tile.
   const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.out + b * a.N * a.ld_out, (uint32_t)(a.N * a.ld_out * 2));
-  auto epilogue = [&](int ft) {
-    lds_sync();   // every wave is done reading stage 3
-    const uint32_t rowo = (uint32_t)p * 128u + 8u * (uint32_t)(lane >> 5);
+  // write: row p, piece c at wofs ^ (c << 4); read: row 32 w + 8 it + (lane >> 3), piece lane & 7,
+  // at rofs ^ ((it & 1) << 6) + 1024 it (the row's swizzle is 4 (it & 1) + (lane >> 4))
+  const uint32_t wofs = ((uint32_t)p * 128u + 8u * (uint32_t)(lane >> 5)) | ((uint32_t)((p >> 1) & 7) << 4);
+  const uint32_t rofs = (uint32_t)(wave * 32 + (lane >> 3)) * 128u + ((uint32_t)((lane & 7) ^ (lane >> 4)) << 4);
+  uint32_t srow[4];   // byte offset of each read row's token in the output, OOB past the split
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+  for (int it = 0; it < 4; ++it) {
+    const int t = wave * 32 + it * 8 + (lane >> 3);
+    srow[it] = t < valid_rows ? (uint32_t)((base + t) * a.ld_out * 2) : OOB;
+  }
+  auto epilogue = [&](int ft, uint8_t* sst) __attribute__((always_inline)) {
+    lds_sync();   // every wave is done reading the stage
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
 #pragma unroll
       for (int fh = 0; fh < 2; ++fh) {
         const int fb = 2 * rr + fh;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint32_t lo = pack_bf16(layer_out(acc2[fb][g * 4 + 0], inv, bv, relu),
-                                        layer_out(acc2[fb][g * 4 + 1], inv, bv, relu));
-          const uint32_t hi = pack_bf16(layer_out(acc2[fb][g * 4 + 2], inv, bv, relu),
-                                        layer_out(acc2[fb][g * 4 + 3], inv, bv, relu));
-          const uint32_t pc = (uint32_t)(4 * fh + g) ^ (uint32_t)((p >> 1) & 7);
-          *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(lo, hi);
+          const uint32_t lo = pack_bf16(layer_out<kRelu>(acc2[fb][g * 4 + 0], inv, bv),
+                                        layer_out<kRelu>(acc2[fb][g * 4 + 1], inv, bv));
+          const uint32_t hi = pack_bf16(layer_out<kRelu>(acc2[fb][g * 4 + 2], inv, bv),
+                                        layer_out<kRelu>(acc2[fb][g * 4 + 3], inv, bv));
+          *reinterpret_cast<uint2*>(sst + (wofs ^ ((uint32_t)(4 * fh + g) << 4))) = make_uint2(lo, hi);
         }
       }
-      lds_sync();
+      const int f = ft * FR + rr * 64 + (lane & 7) * 8;
+      const bool fok = f < a.m_t;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int t = wave * 32 + it * 8 + (lane >> 3);
-        const int pp = lane & 7;
-        const uint4 v = lds_read16(st3, (uint32_t)t * 128u + ((uint32_t)(pp ^ ((t >> 1) & 7)) << 4));
-        const int f = ft * FT + rr * 64 + pp * 8;
-        const bool ok = t < valid_rows && f < a.m_t;
-        buf_store16<2>(outr, ok ? (uint32_t)(((base + t) * a.ld_out + f) * 2) : OOB, 0, v);   // non-temporal
+        const uint4 v = lds_read16(sst, (rofs ^ ((uint32_t)(it & 1) << 6)) + (uint32_t)it * 1024u);
+        buf_store16<2>(outr, fok ? srow[it] + (uint32_t)f * 2u : OOB, 0, v);   // non-temporal
       }
-      if (rr < 3) lds_sync();
     }
   };
-  // A tile's chunk c0 + q is complete once at most 8 newer copies are outstanding; after an
-  // epilogue its 16 stores are newer than chunks c0 .. c0 + 2 as well (24; the branch on ft is
-  // uniform).
-  for (int ft = 0; ft < nft; ++ft) {
-    const int c0 = 4 * ft;
-    if (ft) DYN_WAIT_KEEP(24); else DYN_WAIT_KEEP(8);
-    compute2(st0, std::integral_constant<int, 0>{}, c0 + 3, st3);
-    if (ft) DYN_WAIT_KEEP(24); else DYN_WAIT_KEEP(8);
-    compute2(st1, std::integral_constant<int, 1>{}, c0 + 4, st0);
-    if (ft) DYN_WAIT_KEEP(24); else DYN_WAIT_KEEP(8);
-    compute2(st2, std::integral_constant<int, 2>{}, c0 + 5, st1);
-    DYN_WAIT_KEEP(8);
-    compute2(st3, std::integral_constant<int, 3>{}, c0 + 6, st2);
-    epilogue(ft);
+  // Feature tile ft: chunks 2 ft (stage sa) and 2 ft + 1 (stage sb); the copies issued meanwhile
+  // are those of chunks 2 ft + 3 (into sd) and 2 ft + 4 (into sa). Its first chunk is complete
+  // once at most 8 newer copies are outstanding, and after an epilogue its 8 stores as well
+  // (16). The epilogue comes between two tiles, so a tile's first k-step is read after that
+  // wait, not ahead.
+  auto tile = [&](int ft, uint8_t* sa, uint8_t* sb, uint8_t* sd, auto after_epi) __attribute__((always_inline)) {
+    const std::integral_constant<int, 0> kQ0;
+    const std::integral_constant<int, 1> kQ1;
+    const std::integral_constant<bool, false> kNoStores;
+    if constexpr (decltype(after_epi)::value) DYN_WAIT_KEEP(16); else DYN_WAIT_KEEP(8);
+    read2(sa, 0);
+    compute2(sa, kQ0, 2 * ft + 3, sd, sb, after_epi);
+    compute2(sb, kQ1, 2 * ft + 4, sa, nullptr, kNoStores);
+    epilogue(ft, sb);
+  };
+  const std::integral_constant<bool, true> kAfterEpi;
+  tile(0, st0, st1, st3, std::integral_constant<bool, false>{});
+  int ft = 1;
+  for (; ft + 1 < nft; ft += 2) {
+    tile(ft, st2, st3, st1, kAfterEpi);
+    tile(ft + 1, st0, st1, st3, kAfterEpi);
   }
+  if (ft < nft) tile(ft, st2, st3, st1, kAfterEpi);
   wait_vmem();   // the copies issued past the last chunk and the last stores complete before the exit
 }
 
@@ -644,7 +710,8 @@ hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int
   p.tiles = B * p.n_s;
   p.pgroups = 1;
   if (p.S <= 256) {
-    hipLaunchKernelGGL(ring::dyn_ring_kernel, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
+    if (epi.act != 0) hipLaunchKernelGGL(ring::dyn_ring_kernel<true>, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL(ring::dyn_ring_kernel<false>, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
   p.pgroups = (S + 127) / 128;   // workgroups of 128 tokens p per split

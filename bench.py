@@ -29,7 +29,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attention_free_
 # HBM traffic of one launch of the dominant kernel, from two rocprofv3 --pmc passes (FETCH_SIZE,
 # then WRITE_SIZE, KiB per dispatch, averaged over the dispatches of the run) over this bench on
 # the named workload, each scaled by what the same counter reads for a plain 1 GiB device copy
-# (FETCH_SIZE read 524300 KiB for 1048576 KiB moved: x2.0; WRITE_SIZE read 1048576 KiB: x1.0).
+# (FETCH_SIZE read 524308 KiB for 1048576 KiB moved: x1.99992; WRITE_SIZE read 1048576 KiB: x1.0).
 # Keyed by the digest of the kernel's sources: once they change the figures no longer apply and
 # traffic is reported as null until the counters are taken again.
 TRAFFIC = {
