@@ -22,7 +22,7 @@ from helpers import TOL, dev_tensor, host_f64, split_rows_of, upload
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # 8 splits of 256 (last one 208 tokens), 2 sequences, m_t = 320 (a 256-feature tile and a 64-feature one)
+    # 8 splits of 256 (last one 208 tokens), 2 sequences, m_t = 320 (two 128-feature tiles and a 64-feature one)
     "small_bf16": Config("small_bf16", B=2, N=2000, d=256, S=256, k=3, m_t=320, m=384, dtype="bf16",
                          x_dist="mixture", n_centroids=16),
     # S = 512 (two 256-token halves per split), last split 40 tokens
