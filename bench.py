@@ -36,10 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("2396f7bd914b1be6", "long"): {"fetch_kib": 1177182.3, "fetch_scale": 1.99992,
-                                           "write_kib": 272.4, "write_scale": 1.0},
-            ("2396f7bd914b1be6", "extreme"): {"fetch_kib": 6684500.6, "fetch_scale": 1.99992,
-                                              "write_kib": 2134.0, "write_scale": 1.0},
+            ("1bf9bd03542cd2fd", "long"): {"fetch_kib": 1198576.8, "fetch_scale": 1.99992,
+                                           "write_kib": 236.8, "write_scale": 1.0},
+            ("1bf9bd03542cd2fd", "extreme"): {"fetch_kib": 5431596.6, "fetch_scale": 1.99992,
+                                              "write_kib": 1131.3, "write_scale": 1.0},
         },
     },
 }
