@@ -321,14 +321,15 @@ __global__ void __launch_bounds__(256, 2) compress_bf16_kernel(CompressParams a)
 // 32 KiB (three chunks in flight) and the next unit's first three chunks copied while the
 // current one finishes. Compared with the tiled kernel, each gathered X row is staged once per
 // feature tile instead of once per 128 output tokens.
-//   * Features of wave (wm, mb): 64 mb + 32 wm + (0..31), so that the four 64-feature slices of
-//     the output tile are whole 128-byte row pieces.
+//   * Features of wave (wm, mb): 128 wm + 32 mb + (0..31), so that each wave holds two whole
+//     64-feature slices (128-byte row pieces) of its 64 tokens.
 //   * Residual: the split's own block comes last; in the chunk of it that holds a wave's token
 //     block nb, 8 more MFMAs of that chunk's X^T fragments with an identity B operand add
 //     X_i[s][f] to C[f][s] exactly.
-//   * Epilogue, through stage 3 in four rounds (one 64-feature slice each): lanes write their
-//     4-feature groups into a [256 tokens][64 features] bf16 tile, then 8 lanes per token store
-//     whole 128-byte rows (scattered 8-byte stores would cost a write request per lane).
+//   * Epilogue, through stage 3, each wave through its own 4 KiB of it (one barrier per unit), in
+//     four rounds of 32 tokens x 64 features: lanes write their 4-feature groups into a bf16
+//     tile, then 8 lanes per token store whole 128-byte row pieces (scattered 8-byte stores
+//     would cost a write request per lane, and 64-byte pieces measured slower).
 //   * Source splits and weights of the next unit are read with scalar loads into a second LDS
 //     table, so that the copies stay the only vector-memory operations of the K loop. When the
 //     copies move on to a unit, its block table is loaded once into one VGPR (lane r: block r's
@@ -354,8 +355,9 @@ typedef const __attribute__((address_space(4))) float* sc_f32;
 template <int P>
 using Pos = std::integral_constant<int, P>;
 
-// CPB: chunks per block (S / 32) as a compile-time constant, or 0 for any S.
-template <int CPB>
+// CPB: chunks per block (S / 32) as a compile-time constant, or 0 for any S; kRelu: the layer
+// epilogue's activation.
+template <int CPB, bool kRelu>
 __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a) {
   __shared__ __align__(16) uint8_t st0[USTAGE], st1[USTAGE], st2[USTAGE], st3[USTAGE];
   __shared__ int s_tok0[2][MAXBLK];   // per unit (two tables): first token of block r's split
@@ -485,14 +487,14 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
     for (int n = 0; n < 4; ++n) copy(st, valid, n, src);
   };
 
-  // ---- fragments (transpose reads of X for A, P rows for B), feature blocks 64 mb + 32 wm
+  // ---- fragments (transpose reads of X for A, P rows for B), feature blocks 128 wm + 32 mb
   uint32_t offA[4];
   {
     const int s2 = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
     const uint32_t row = (uint32_t)(8 * (lane >> 5) + ((lane & 15) >> 2)) * XB;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      offA[mb] = row + (uint32_t)((((4 * mb + 2 * wm) ^ (2 * s2)) + g1) << 5) + 8u * (lane & 3);
+      offA[mb] = row + (uint32_t)((((8 * wm + 2 * mb) ^ (2 * s2)) + g1) << 5) + 8u * (lane & 3);
   }
   uint32_t offB[2];
 #pragma unroll
@@ -617,7 +619,6 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   dma(1, st1, 1 < nk);
   dma(2, st2, 2 < nk);
 
-  const bool relu = a.epi.act != 0;
   bool first_unit = true;
   const std::integral_constant<bool, true> kFirst;
   const std::integral_constant<bool, false> kNext;
@@ -671,41 +672,46 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
       compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr, false);
     }
 
-    // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)
+    // ---- epilogue through stage 3: wave w uses bytes 4096 w .. +4095, a [32 tokens][64
+    // features] bf16 tile whose 16-byte piece c of row r sits at c ^ ((r >> 1) & 7). A wave
+    // writes and reads back only its own tile, so after the first barrier (every wave is done
+    // reading stage 3) it needs none. Round (nb, fh): token block nb, features 128 wm + 64 fh.
     const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.xhat + cur.b * a.N * a.ld_out, (uint32_t)(a.N * a.ld_out * 2));
-    lds_sync();   // every wave is done reading stage 3
+    lds_sync();
+    uint8_t* const stg = st3 + wave * 4096;
+    // write: row lane & 31, half lane >> 5, piece c at wofs ^ (c << 4); read: row 8 it + (lane >> 3),
+    // piece lane & 7, at (rofs ^ ((it & 1) << 6)) + 1024 it (the row's swizzle is 4 (it & 1) + (lane >> 4))
+    const uint32_t wofs = ((uint32_t)(lane & 31) * 128u + 8u * (uint32_t)(lane >> 5)) | ((uint32_t)((lane >> 1) & 7) << 4);
+    const uint32_t rofs = (uint32_t)(lane >> 3) * 128u + ((uint32_t)((lane & 7) ^ (lane >> 4)) << 4);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int nb = 0; nb < 2; ++nb) {
+      const float bv = s_bias[(cur.su * TU + wn * 64 + nb * 32 + (lane & 31)) & 511];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int sl = wn * 64 + nb * 32 + (lane & 31);
-        const float bv = s_bias[(cur.su * TU + sl) & 511];
-        const uint32_t rowo = (uint32_t)sl * 128u + 8u * (uint32_t)(lane >> 5);
+      for (int fh = 0; fh < 2; ++fh) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float y = acc[mb][nb][g * 4 + e] + bv;
-            v[e] = relu ? fmaxf(y, 0.f) : y;
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float y = acc[2 * fh + h][nb][g * 4 + e] + bv;
+              v[e] = kRelu ? fmaxf(y, 0.f) : y;
+            }
+            *reinterpret_cast<uint2*>(stg + (wofs ^ ((uint32_t)(4 * h + g) << 4))) =
+                make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
           }
-          const uint32_t pc = (uint32_t)(4 * wm + g) ^ (uint32_t)((sl >> 1) & 7);
-          *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        }
+        const int f = cur.f_base + wm * 128 + fh * 64 + (lane & 7) * 8;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const uint4 v = lds_read16(stg, (rofs ^ ((uint32_t)(it & 1) << 6)) + (uint32_t)it * 1024u);
+          const int s = cur.su * TU + wn * 64 + nb * 32 + it * 8 + (lane >> 3);
+          const int64_t tok = (int64_t)cur.i * a.S + s;
+          const bool ok = s < a.S && tok < a.N && f < a.d;
+          buf_store16<2>(outr, ok ? (uint32_t)((tok * a.ld_out + f) * 2) : OOB, 0, v);   // non-temporal
         }
       }
-      lds_sync();
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int sl = wave * 32 + it * 8 + (lane >> 3);
-        const int p = lane & 7;
-        const uint4 v = lds_read16(st3, (uint32_t)sl * 128u + ((uint32_t)(p ^ ((sl >> 1) & 7)) << 4));
-        const int s = cur.su * TU + sl;
-        const int64_t tok = (int64_t)cur.i * a.S + s;
-        const int f = cur.f_base + mb * 64 + p * 8;
-        const bool ok = s < a.S && tok < a.N && f < a.d;
-        buf_store16<2>(outr, ok ? (uint32_t)((tok * a.ld_out + f) * 2) : OOB, 0, v);   // non-temporal
-      }
-      if (mb < 3) lds_sync();
     }
     if (!has_next) break;
     t += Gx;
@@ -743,12 +749,17 @@ hipError_t launch_compress_bf16(const uint16_t* x, int64_t B, int64_t N, int d, 
     p.s_tiles = (S + unit::TU - 1) / unit::TU;
     p.tiles = units;
     // chunks per block as a constant for the common split lengths
-    if (S == 256)
-      hipLaunchKernelGGL(unit::compress_unit_kernel<8>, dim3((unsigned)cus), dim3(512), 0, stream, p);
-    else if (S == 512)
-      hipLaunchKernelGGL(unit::compress_unit_kernel<16>, dim3((unsigned)cus), dim3(512), 0, stream, p);
-    else
-      hipLaunchKernelGGL(unit::compress_unit_kernel<0>, dim3((unsigned)cus), dim3(512), 0, stream, p);
+    const bool relu = epi.act != 0;
+    if (S == 256) {
+      if (relu) hipLaunchKernelGGL((unit::compress_unit_kernel<8, true>), dim3((unsigned)cus), dim3(512), 0, stream, p);
+      else hipLaunchKernelGGL((unit::compress_unit_kernel<8, false>), dim3((unsigned)cus), dim3(512), 0, stream, p);
+    } else if (S == 512) {
+      if (relu) hipLaunchKernelGGL((unit::compress_unit_kernel<16, true>), dim3((unsigned)cus), dim3(512), 0, stream, p);
+      else hipLaunchKernelGGL((unit::compress_unit_kernel<16, false>), dim3((unsigned)cus), dim3(512), 0, stream, p);
+    } else {
+      if (relu) hipLaunchKernelGGL((unit::compress_unit_kernel<0, true>), dim3((unsigned)cus), dim3(512), 0, stream, p);
+      else hipLaunchKernelGGL((unit::compress_unit_kernel<0, false>), dim3((unsigned)cus), dim3(512), 0, stream, p);
+    }
     return hipGetLastError();
   }
   p.tiles = B * p.n_s * p.s_tiles * p.f_tiles;
