@@ -11,14 +11,16 @@
 // gather and the block weights. A unit is 256 output features x 256 tokens; W streams through
 // LDS as 32-row chunks of 256 features (512-byte rows, read back with the LDS transpose read)
 // and A as 256 token rows x 32 K-values (64 bytes) per chunk, through a 4-stage ring of 32 KiB
-// direct-copy stages, one 8-wave workgroup per CU (2 x 4 waves of 128 features x 64 tokens).
+// direct-copy stages, one 8-wave workgroup per CU (2 x 4 waves of 128 features x 64 tokens;
+// wave (wm, wn) holds features 128 wm .. +127, two whole 64-feature slices of its tokens).
 //   * The fuser's A is two tensors along K: columns [0, m_h) of Z (its head), then C.
 //   * The fuser's residual: 8 more chunks stage the unit's 256 token rows of X (256 features)
 //     in the W part, with zeros in the A part; in the chunk holding a wave's token block, 8
 //     MFMAs of those rows' transposed fragments against an identity operand add X[t][f] to
 //     C^T[f][t] exactly (products with 1.0, fp32 accumulation).
-//   * Epilogue through stage 3 in four 64-feature rounds, stored as whole 128-byte row pieces;
-//     the enricher adds b[f] and squares the ReLU in fp32 before the single rounding to bf16.
+//   * Epilogue through stage 3, each wave through its own 4 KiB of it (one barrier per unit), in
+//     four rounds of 32 tokens x 64 features stored as whole 128-byte row pieces; the enricher
+//     adds b[f] and squares the ReLU in fp32 before the single rounding to bf16.
 #include "avey_common.h"
 #include "launch.h"
 
@@ -60,6 +62,8 @@ struct GemmParams {
 template <int P>
 using Pos = std::integral_constant<int, P>;
 
+// kRelu2: the enricher's epilogue (bias, squared ReLU); otherwise the plain product.
+template <bool kRelu2>
 __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   __shared__ __align__(16) float s_bias[kMaxF];
@@ -137,14 +141,14 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
     for (int n = 0; n < 4; ++n) copy(kc, st, valid, n);
   };
 
-  // ---- fragments: transposed W for the A operand (features 64 mb + 32 wm), A rows for B
+  // ---- fragments: transposed W for the A operand (features 128 wm + 32 mb), A rows for B
   uint32_t offA[4];
   {
     const int s2 = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
     const uint32_t row = (uint32_t)(8 * (lane >> 5) + ((lane & 15) >> 2)) * XB;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      offA[mb] = row + (uint32_t)((((4 * mb + 2 * wm) ^ (2 * s2)) + g1) << 5) + 8u * (lane & 3);
+      offA[mb] = row + (uint32_t)((((8 * wm + 2 * mb) ^ (2 * s2)) + g1) << 5) + 8u * (lane & 3);
   }
   uint32_t offB[2];
 #pragma unroll
@@ -238,7 +242,6 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   dma(1, st1, 1 < nk);
   dma(2, st2, 2 < nk);
 
-  const bool relu2 = a.relu2 != 0;
   bool first_unit = true;
   const std::integral_constant<bool, true> kFirst;
   const std::integral_constant<bool, false> kNext;
@@ -288,42 +291,51 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
       compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr, false);
     }
 
-    // ---- epilogue through stage 3; piece p of tile row s sits at p ^ ((s >> 1) & 7)
-    lds_sync();   // every wave is done reading stage 3
+    // ---- epilogue through stage 3: wave w uses bytes 4096 w .. +4095, a [32 tokens][64
+    // features] bf16 tile whose 16-byte piece c of row r sits at c ^ ((r >> 1) & 7). A wave
+    // writes and reads back only its own tile, so after the first barrier (every wave is done
+    // reading stage 3) it needs none. Round (nb, fh): token block nb, features 128 wm + 64 fh.
+    lds_sync();
+    uint8_t* const stg = st3 + wave * 4096;
+    // write: row lane & 31, half lane >> 5, piece c at wofs ^ (c << 4); read: row 8 it + (lane >> 3),
+    // piece lane & 7, at (rofs ^ ((it & 1) << 6)) + 1024 it (the row's swizzle is 4 (it & 1) + (lane >> 4))
+    const uint32_t wofs = ((uint32_t)(lane & 31) * 128u + 8u * (uint32_t)(lane >> 5)) | ((uint32_t)((lane >> 1) & 7) << 4);
+    const uint32_t rofs = (uint32_t)(lane >> 3) * 128u + ((uint32_t)((lane & 7) ^ (lane >> 4)) << 4);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int sl = wn * 64 + nb * 32 + (lane & 31);
-        const uint32_t rowo = (uint32_t)sl * 128u + 8u * (uint32_t)(lane >> 5);
+      for (int fh = 0; fh < 2; ++fh) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int fl = mb * 64 + wm * 32 + g * 8 + (lane >> 5) * 4;   // feature in the unit
-          const float4 bq = *reinterpret_cast<const float4*>(&s_bias[(f0 + fl) & (kMaxF - 1)]);
-          const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
-          float v[4];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float y = acc[mb][nb][g * 4 + e] + bb[e];
-            const float r = fmaxf(y, 0.f);
-            v[e] = relu2 ? r * r : y;
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+            if constexpr (kRelu2) {
+              const int fl = wm * 128 + (2 * fh + h) * 32 + g * 8 + (lane >> 5) * 4;   // feature in the unit
+              const float4 bq = *reinterpret_cast<const float4*>(&s_bias[(f0 + fl) & (kMaxF - 1)]);
+              const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float r = fmaxf(acc[2 * fh + h][nb][g * 4 + e] + bb[e], 0.f);
+                v[e] = r * r;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[2 * fh + h][nb][g * 4 + e];
+            }
+            *reinterpret_cast<uint2*>(stg + (wofs ^ ((uint32_t)(4 * h + g) << 4))) =
+                make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
           }
-          const uint32_t pc = (uint32_t)(4 * wm + g) ^ (uint32_t)((sl >> 1) & 7);
-          *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        }
+        const int f = f0 + wm * 128 + fh * 64 + (lane & 7) * 8;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const uint4 v = lds_read16(stg, (rofs ^ ((uint32_t)(it & 1) << 6)) + (uint32_t)it * 1024u);
+          const int64_t tok = t0 + wn * 64 + nb * 32 + it * 8 + (lane >> 3);
+          const bool ok = tok < a.M && f < a.F;
+          buf_store16<2>(cr, ok ? (uint32_t)((tok * a.ldc + f) * 2) : OOB, 0, v);   // non-temporal
         }
       }
-      lds_sync();
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int sl = wave * 32 + it * 8 + (lane >> 3);
-        const int p = lane & 7;
-        const uint4 v = lds_read16(st3, (uint32_t)sl * 128u + ((uint32_t)(p ^ ((sl >> 1) & 7)) << 4));
-        const int64_t tok = t0 + sl;
-        const int f = f0 + mb * 64 + p * 8;
-        const bool ok = tok < a.M && f < a.F;
-        buf_store16<2>(cr, ok ? (uint32_t)((tok * a.ldc + f) * 2) : OOB, 0, v);   // non-temporal
-      }
-      if (mb < 3) lds_sync();
     }
     if (!has_next) break;
     t += Gx;
@@ -340,7 +352,8 @@ hipError_t launch_gemm(const GemmParams& p0, hipStream_t stream) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   const int64_t grid = p.units < cus ? p.units : cus;
-  hipLaunchKernelGGL(gemm_unit_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
+  if (p.relu2) hipLaunchKernelGGL(gemm_unit_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL(gemm_unit_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
