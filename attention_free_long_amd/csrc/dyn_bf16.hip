@@ -624,8 +624,10 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
   };
   // Epilogue of feature tile ft through stage 3 in four rounds of 64 features ([128 tokens][64
   // features] bf16, 16-byte piece c of row t at c ^ ((t >> 1) & 7)), stored as whole 128-byte
-  // row pieces by 8 lanes per token. Every wave issues exactly 16 stores per tile (lanes past the
-  // split or past m_t store out of range), which the next tile's first three copy waits allow for.
+  // row pieces by 8 lanes per token. A wave writes and reads back only its own 32 rows, so after
+  // the first barrier (every wave is done reading stage 3) it needs none. Every wave issues
+  // exactly 16 stores per tile (lanes past the split or past m_t store out of range), which the
+  // next tile's first three copy waits allow for.
   const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.out + b * a.N * a.ld_out, (uint32_t)(a.N * a.ld_out * 2));
   const int pl = wave * 32 + (lane & 31);          // this lane's token within the workgroup
   auto epilogue = [&](int ft) {
@@ -646,7 +648,6 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
           *reinterpret_cast<uint2*>(st3 + rowo + (pc << 4)) = make_uint2(lo, hi);
         }
       }
-      lds_sync();
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int t = wave * 32 + it * 8 + (lane >> 3);
@@ -657,7 +658,6 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
         const bool ok = tp < nvalid && f < a.m_t;
         buf_store16<2>(outr, ok ? (uint32_t)(((base + tp) * a.ld_out + f) * 2) : OOB, 0, v);   // non-temporal
       }
-      if (rr < 3) lds_sync();
     }
   };
   // The phase-1 stages are free (the barriers above); chunks 0..2 go into stages 0..2. Before
