@@ -10,8 +10,9 @@
 //     is exactly the B-operand layout the second GEMM needs along its K = q axis (up to a
 //     fixed permutation of q inside each 16-row group, applied identically to both operands).
 //     Token norms come from LDS fragments the waves read anyway where possible.
-//  2. O^T[f][p] = sum_q Z^T[f][q] G[q][p]: Z^T is read from LDS tiles of [64 q][256 f] by the
-//     LDS transpose read, in the same q order; each result lane owns token p and four
+//  2. O^T[f][p] = sum_q Z^T[f][q] G[q][p]: Z^T is read from LDS tiles of [128 q][128 f]
+//     (S <= 256) or [64 q][256 f] (S <= 512) by the LDS transpose read, in the same q order;
+//     each result lane owns token p and four
 //     consecutive features, scaled by 1 / (r_p + eps). G is rounded to bf16 for this product
 //     and r_p is summed from the rounded values, so the applied weights sum to r_p / (r_p + eps).
 // Two kernels below: one 8-wave workgroup per split for S <= 256, four 4-wave workgroups per
