@@ -182,19 +182,22 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     return o + (uint32_t)blkB(u_) * 32 * RB;
   };
 
-  // The pair decode runs on the vector unit (double-precision square root); its results are
-  // wave-uniform and are moved to scalar registers, so that everything derived from them (block
-  // offsets, limits, the descriptor base) stays out of the vector register file.
-  auto tile_unit = [&](int64_t tl) {
+  // Tile t of this workgroup is pair (xs + t) % pairs of sequence (xs + t) / pairs. The
+  // division runs once; each later tile advances the pair index by Gx and carries into the
+  // sequence (scalar work), so that no 64-bit division, whose constants take vector registers,
+  // sits in the unit loop. The pair decode runs on the vector unit (double-precision square
+  // root); its results are wave-uniform and are moved to scalar registers, so that everything
+  // derived from them (block offsets, limits, the descriptor base) stays out of the vector
+  // register file.
+  auto tile_at = [&](int b, int p) {
     Unit u;
-    const int64_t L = xs + tl;
-    u.b = L / a.pairs;
+    u.b = b;
     int i, j;
     if (kG == 1) {
-      decode_pair((int)(L % a.pairs), a.n_s, i, j);
+      decode_pair(p, a.n_s, i, j);
     } else {
       // pairs of groups I <= J: the unordered pairs I < J' of n_s + 1 with J = J' - 1
-      decode_pair((int)(L % a.pairs), a.n_s + 1, i, j);
+      decode_pair(p, a.n_s + 1, i, j);
       j -= 1;
     }
     u.i = uniform(i);
@@ -203,6 +206,8 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     u.ub = 0;
     return u;
   };
+  int tb = (int)((xs + t) / a.pairs);   // sequence and pair index of tile t
+  int tp = (int)((xs + t) % a.pairs);
 
   // Copy addressing: a descriptor over the unit's sequence, the byte offsets of its two blocks'
   // first rows in chunk 0, the bytes from one token row to the next (rowB) and from one chunk to
@@ -292,11 +297,10 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
 #pragma unroll
     for (int s_ = 2; s_ < 4; ++s_) ra[s_] = lds_read16(st, offA(ks, s_));
   };
-  // kRow: sums of squares of this wave's norm rows (slot 0 of each operand). Per chunk each lane
-  // sums the 8 features of its k-half over both k-steps into tA / tB, then adds that to its
-  // running sum in LDS, s_ssA[half][row] (each lane owns one entry: no atomics). The read is
-  // issued before the chunk's wait, which completes it, and the write follows the wait: nothing
-  // is carried in registers across chunks. The epilogue adds the two halves and clears them.
+  // kRow: sums of squares of this wave's norm rows (slot 0 of each operand). Each lane sums the 8
+  // features of its k-half over the unit's chunks into tA / tB and writes the total to its entry
+  // of s_ssA[half][row] at the unit's last chunk (each lane owns one entry: no atomics). The
+  // epilogue adds the two halves and clears them.
   float tA = 0.f, tB = 0.f;
   auto ss_slot = [&]() {
     int o = (lane >> 5) * T + (lane & 31);
@@ -328,8 +332,8 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       else dma16(xr, dst + T * RB + r0 * RB, ok ? src_off(pbB, limB, r0, sub, pc) : OOB, kb);
     };
     if (kRow) {   // before the MFMAs, which stay the fragments' last readers
-      tA = sumsq8(ra0[0], 0.f);
-      tB = sumsq8(rb0[0], 0.f);
+      tA = sumsq8(ra0[0], tA);
+      tB = sumsq8(rb0[0], tB);
     }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -362,18 +366,9 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     copy(1, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (next) {
-      float oA = 0.f, oB = 0.f;
-      int so = 0;
-      if (kRow) {
-        so = ss_slot();
-        oA = s_ssA[so + wm * 128 + wn * 32];
-        oB = s_ssB[so + wn * 64 + wm * 32];
-      }
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
       WAIT_KEEP(7);
       if (kRow) {
-        s_ssA[so + wm * 128 + wn * 32] = oA + tA;
-        s_ssB[so + wn * 64 + wm * 32] = oB + tB;
         fetch_lo(ra0, rb0, 0, next);
       } else {
         fetch0(next);
@@ -398,7 +393,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   const int own = tid & (T - 1);
   float rmax = 0.f, part = 0.f;
 
-  Unit cur = tile_unit(t);
+  Unit cur = tile_at(tb, tp);
   set_unit(cur);
   dma(0, st0, true);
   dma(1, st1, 1 < nk);
@@ -410,15 +405,29 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     // ---- what comes after this unit: candidate blocks inner, target blocks outer, then tiles
     Unit nx = cur;
     bool has_next = true;
+    int np_next = 0;   // pair index of the next tile, when the unit after this is one
     if (cur.ub + 1 < a.q) {
       nx.ub = cur.ub + 1;
     } else if (cur.ua + 1 < a.q) {
       nx.ua = cur.ua + 1;
       nx.ub = 0;
     } else if (t + Gx < cnt) {
-      nx = tile_unit(t + Gx);
+      // tp + Gx, carried into the sequence, without forming a value past pairs
+      int step = Gx, nb = tb;
+      np_next = tp;
+      while (step >= a.pairs - np_next) {
+        step -= a.pairs - np_next;
+        np_next = 0;
+        ++nb;
+      }
+      np_next += step;
+      nx = tile_at(nb, np_next);
     } else {
       has_next = false;
+    }
+    if (kRow) {
+      tA = 0.f;
+      tB = 0.f;
     }
     const int cLimA = limA, cLimB = limB;
     const bool valid = own < (is_row ? cLimA : cLimB);
@@ -749,7 +758,11 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     }
 
     if (!has_next) break;
-    if (nx.ua == 0 && nx.ub == 0) t += Gx;
+    if (nx.ua == 0 && nx.ub == 0) {
+      t += Gx;
+      tb = (int)nx.b;
+      tp = np_next;
+    }
     cur = nx;
     lds_sync();   // this epilogue's LDS reads are done before stage 3 is refilled
   }
@@ -788,33 +801,49 @@ int64_t grid_for(int64_t tiles) {
 
 }  // namespace
 
+// The kernel tracks a tile's sequence in 32 bits: batches beyond kMaxLaunchB sequences go out as
+// several launches over consecutive slices of the batch.
+constexpr int64_t kMaxLaunchB = int64_t(1) << 30;
+
 hipError_t launch_maxsim_bf16(const uint16_t* xp, int64_t B, int64_t N, int d, int S, float* scores,
                               hipStream_t stream) {
-  const MaxsimParams p = params(xp, 0, B, N, d, S, scores);
-  const dim3 grid((unsigned)grid_for(p.tiles));
-  switch (group_of(S)) {
-    case 4: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 4>), grid, dim3(512), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 2>), grid, dim3(512), 0, stream, p); break;
-    default: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 1>), grid, dim3(512), 0, stream, p); break;
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxLaunchB) {
+    MaxsimParams p = params(xp, 0, min(B - b0, kMaxLaunchB), N, d, S, scores);
+    p.x = xp + b0 * ((int64_t)p.n_s * p.nk * p.S * KH);
+    p.scores = scores + b0 * ((int64_t)p.n_out * p.n_out);
+    const dim3 grid((unsigned)grid_for(p.tiles));
+    switch (group_of(S)) {
+      case 4: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 4>), grid, dim3(512), 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 2>), grid, dim3(512), 0, stream, p); break;
+      default: hipLaunchKernelGGL((maxsim_bf16_kernel<false, false, 1>), grid, dim3(512), 0, stream, p); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_maxsim_rows_bf16(const uint16_t* x, int64_t B, int64_t N, int d, int64_t ld, int S, float* scores,
                                    hipStream_t stream) {
-  const MaxsimParams p = params(x, ld, B, N, d, S, scores);
-  const dim3 grid((unsigned)grid_for(p.tiles));
   const int g = group_of(S);
-  if (d % KH) {
-    if (g == 4) hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 4>), grid, dim3(512), 0, stream, p);
-    else if (g == 2) hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 2>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 1>), grid, dim3(512), 0, stream, p);
-  } else {
-    if (g == 4) hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 4>), grid, dim3(512), 0, stream, p);
-    else if (g == 2) hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 2>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 1>), grid, dim3(512), 0, stream, p);
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxLaunchB) {
+    MaxsimParams p = params(x, ld, min(B - b0, kMaxLaunchB), N, d, S, scores);
+    p.x = x + b0 * (N * ld);
+    p.scores = scores + b0 * ((int64_t)p.n_out * p.n_out);
+    const dim3 grid((unsigned)grid_for(p.tiles));
+    if (d % KH) {
+      if (g == 4) hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 4>), grid, dim3(512), 0, stream, p);
+      else if (g == 2) hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 2>), grid, dim3(512), 0, stream, p);
+      else hipLaunchKernelGGL((maxsim_bf16_kernel<true, true, 1>), grid, dim3(512), 0, stream, p);
+    } else {
+      if (g == 4) hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 4>), grid, dim3(512), 0, stream, p);
+      else if (g == 2) hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 2>), grid, dim3(512), 0, stream, p);
+      else hipLaunchKernelGGL((maxsim_bf16_kernel<true, false, 1>), grid, dim3(512), 0, stream, p);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace avey
