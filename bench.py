@@ -36,10 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("1bf9bd03542cd2fd", "long"): {"fetch_kib": 1198576.8, "fetch_scale": 1.99992,
-                                           "write_kib": 236.8, "write_scale": 1.0},
-            ("1bf9bd03542cd2fd", "extreme"): {"fetch_kib": 5431596.6, "fetch_scale": 1.99992,
-                                              "write_kib": 1131.3, "write_scale": 1.0},
+            ("9034c277b5184452", "long"): {"fetch_kib": 1182155.0, "fetch_scale": 1.99992,
+                                           "write_kib": 237.1, "write_scale": 1.0},
+            ("9034c277b5184452", "extreme"): {"fetch_kib": 5763103.1, "fetch_scale": 1.99992,
+                                              "write_kib": 1864.4, "write_scale": 1.0},
         },
     },
 }
