@@ -29,6 +29,12 @@ struct DynParams {
   uint16_t* out;
   int64_t N, ld_z, ld_out, tiles;
   int m_t, S, n_s, pgroups;
+  // S <= 256 kernel: splits full .. tiles - 1 (the last, partial wave of the grid) are each
+  // shared by fsplit workgroups, which all compute the split's G and take consecutive ranges of
+  // its phase-2 feature tiles; the fsplit workgroups of one split have ids fsplit NXCD apart
+  // (the same XCD), so that their repeated phase-1 reads meet in its L2. fsplit = 1: none.
+  int64_t full;
+  int fsplit;
   // S = 64 and 128 (ring kernel): a workgroup takes 256 / S consecutive splits (S above is then
   // 256 and n_s counts the groups) and mixes tokens p, q only when p >> gshift == q >> gshift;
   // otherwise gshift is 8 and seg == S.
@@ -123,19 +129,36 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
 
-  const int64_t split = xcd_remap(blockIdx.x, a.tiles);
+  const int nft_all = (a.m_t + FR - 1) / FR;     // phase-2 feature tiles of a split
+  int64_t split;
+  int ft0 = 0, nft = nft_all;                     // this workgroup's phase-2 feature tiles
+  if ((int64_t)blockIdx.x < a.full) {
+    split = xcd_remap(blockIdx.x, a.full);
+  } else {
+    // 32-bit arithmetic (the grid is below 2^32) on wave-uniform values, kept in scalar registers
+    const uint32_t j = blockIdx.x - (uint32_t)a.full, l = j / NXCD, f = (uint32_t)a.fsplit;
+    const uint32_t grp = (uint32_t)uniform((int)(l / f)), k = l - grp * f;
+    split = a.full + (int64_t)grp * NXCD + j % NXCD;
+    if (split >= a.tiles) return;                 // the grid's tail rounded up to whole XCD rounds
+    ft0 = uniform((int)(k * (uint32_t)nft_all / f));
+    nft = uniform((int)((k + 1) * (uint32_t)nft_all / f)) - ft0;
+  }
   const int64_t b = split / a.n_s;
   const int i = (int)(split % a.n_s);
   const int64_t base = (int64_t)i * a.S;
   const int valid_rows = (int)min((int64_t)a.S, a.N - base);
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z + b * a.N * a.ld_z, (uint32_t)(a.N * a.ld_z * 2));
+  // Phase 2 addresses features from this workgroup's first tile: its reads and stores go through
+  // descriptors whose base is moved by ft0 tiles, against m_loc features left.
+  const int m_loc = a.m_t - ft0 * FR;
+  const __amdgpu_buffer_rsrc_t zr2 =
+      make_rsrc(a.z + b * a.N * a.ld_z + ft0 * FR, (uint32_t)((a.N * a.ld_z - ft0 * FR) * 2));
   const int p = wave * 32 + (lane & 31);          // this lane's output token (in the workgroup's rows)
   const bool p_ok = p < valid_rows;
   const int pseg = p >> a.gshift;                 // p's split among the workgroup's (0 unless grouped)
   const float bv = layer_bias(a.epi, p - (pseg << a.gshift), p_ok);   // bias of p's position in its split
   const int nk1 = (a.m_t + KC - 1) / KC;          // phase-1 chunks of 64 features (last partial)
   const int nk1p = (nk1 + 3) / 4 * 4;             // padded with zero chunks to a multiple of 4
-  const int nft = (a.m_t + FR - 1) / FR;          // phase-2 feature tiles (two chunks each)
 
   // ---- copies: 4 per wave per chunk, zeros when !valid or out of range. The two phases have
   // separate copy routines, chosen at compile time at every call site: a run-time branch
@@ -163,8 +186,8 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     const int pp = ln & 15;
     const int pc = (pp >> 1) ^ (2 * (t & 3));
     const int f = ft * FR + pc * 16 + (pp & 1) * 8;
-    const bool ok = valid && c2 < 2 * nft && q < valid_rows && f < a.m_t;
-    dma16(zr, st + (wave * 16 + n * 4) * ZR, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
+    const bool ok = valid && c2 < 2 * nft && q < valid_rows && f < m_loc;
+    dma16(zr2, st + (wave * 16 + n * 4) * ZR, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
   };
 
   // ---- phase 1
@@ -346,7 +369,8 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   // first barrier (every wave is done reading the stage) it needs none. Every wave issues exactly
   // 8 stores per tile (lanes past the split or past m_t store out of range), which the next
   // tile's waits allow for: the stores drain under the MFMAs instead of holding up the next tile.
-  const __amdgpu_buffer_rsrc_t outr = make_rsrc(a.out + b * a.N * a.ld_out, (uint32_t)(a.N * a.ld_out * 2));
+  const __amdgpu_buffer_rsrc_t outr =
+      make_rsrc(a.out + b * a.N * a.ld_out + ft0 * FR, (uint32_t)((a.N * a.ld_out - ft0 * FR) * 2));
   // write: row p, piece c at wofs ^ (c << 4); read: row 32 w + 8 it + (lane >> 3), piece lane & 7,
   // at rofs ^ ((it & 1) << 6) + 1024 it (the row's swizzle is 4 (it & 1) + (lane >> 4))
   const uint32_t wofs = ((uint32_t)p * 128u + 8u * (uint32_t)(lane >> 5)) | ((uint32_t)((p >> 1) & 7) << 4);
@@ -374,7 +398,7 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
         }
       }
       const int f = ft * FR + rr * 64 + (lane & 7) * 8;
-      const bool fok = f < a.m_t;
+      const bool fok = f < m_loc;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const uint4 v = lds_read16(sst, (rofs ^ ((uint32_t)(it & 1) << 6)) + (uint32_t)it * 1024u);
@@ -692,6 +716,14 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
 
 }  // namespace ring
 
+int64_t device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
 }  // namespace
 
 hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int64_t ld_z, int S, float eps,
@@ -710,9 +742,22 @@ hipError_t launch_dyn_bf16(const uint16_t* z, int64_t B, int64_t N, int m_t, int
   p.n_s = (int)((N + p.S - 1) / p.S);
   p.tiles = B * p.n_s;
   p.pgroups = 1;
+  p.full = p.tiles;
+  p.fsplit = 1;
   if (p.S <= 256) {
-    if (epi.act != 0) hipLaunchKernelGGL(ring::dyn_ring_kernel<true>, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL(ring::dyn_ring_kernel<false>, dim3((unsigned)p.tiles), dim3(512), 0, stream, p);
+    // One workgroup per CU at a time. When the grid's last wave would leave half the CUs or
+    // more idle, its r splits are shared by f = min(CUs / r, feature tiles, 4) workgroups each.
+    const int64_t cus = device_cus();
+    const int64_t waves = (p.tiles + cus - 1) / cus, r = p.tiles - (waves - 1) * cus;
+    const int64_t f = min(min(cus / r, (int64_t)(m_t + ring::FR - 1) / ring::FR), (int64_t)4);
+    int64_t grid = p.tiles;
+    if (f >= 2) {
+      p.full = (waves - 1) * cus;
+      p.fsplit = (int)f;
+      grid = p.full + (r + NXCD - 1) / NXCD * NXCD * f;
+    }
+    if (epi.act != 0) hipLaunchKernelGGL(ring::dyn_ring_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL(ring::dyn_ring_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
   }
   p.pgroups = (S + 127) / 128;   // workgroups of 128 tokens p per split

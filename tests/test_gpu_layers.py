@@ -236,6 +236,68 @@ def test_dyn_norm_variants(gpu_ok, name, norm):
     say(f"{name}/{norm}: worst relative error {w:.2e}")
 
 
+# Grids whose last wave is partial: on a 256-CU device the splits (or groups) of that wave are
+# each shared by several workgroups, every one computing the split's G and writing its own
+# range of feature tiles, beside whole splits of the full wave in the same launch.
+WAVE_TAIL = {
+    # 300 splits (the last 100 tokens); m_t = 520: five feature tiles, the last one partial;
+    # 44 splits in the last wave, four workgroups each (tiles 0 | 1 | 2 | 3-4)
+    "tail_s256": Config("tail_s256", B=1, N=76644, d=64, S=256, k=2, m_t=520, m=600, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+    # S = 128: 290 groups of two splits (the last group a single 78-token split), m_t = 392
+    "tail_s128": Config("tail_s128", B=1, N=74190, d=64, S=128, k=2, m_t=392, m=456, dtype="bf16",
+                        x_dist="mixture", n_centroids=16),
+}
+
+
+@pytest.mark.parametrize("name", list(WAVE_TAIL))
+def test_dyn_wave_tail_every_split(gpu_ok, name):
+    """The dynamic core, and the dynamic layer with bias, ReLU and softmax weights, on grids with
+    a partial last wave: every split against the oracle."""
+    cfg = WAVE_TAIL[name]
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    _, bias = layer_params(inp)
+    say(f"{name}: dynamic core and layer B={cfg.B} N={cfg.N} S={cfg.S} m_t={cfg.m_t}, every split")
+    _, _, _, z_tail = upload(inp)
+    bd = torch.from_numpy(bias).to("cuda")
+    g_core = host_f64(A.avey_dyn_context(z_tail, cfg.S, cfg.eps))
+    g_lay = host_f64(A.avey_dyn_layer(z_tail, cfg.S, cfg.eps, bd, "relu", norm="softmax"))
+    torch.cuda.synchronize()
+    z64 = inp.z_tail_f64()
+    b64 = bias.astype(np.float64)
+    core = {(0, i): O.dyn_context_split(z64[0], cfg.S, cfg.eps, i) for i in range(cfg.n_s)}
+    w1 = check_layer(g_core, core, core, cfg, tol, "dynamic core")
+    pre = O.dyn_layer(z64, cfg.S, cfg.eps, b64, "identity", norm="softmax")
+    post = O.dyn_layer(z64, cfg.S, cfg.eps, b64, "relu", norm="softmax")
+    w2 = check_layer(g_lay, pre, post, cfg, tol, "dynamic layer/softmax")
+    say(f"{name}: {cfg.n_s} splits, worst {w1:.2e} (core), {w2:.2e} (layer)")
+
+
+def test_dyn_extreme_every_split(gpu_ok):
+    """The dynamic core on the 98304-token workload (384 splits of 256, m_t = 1536): a full wave
+    of whole splits and a last wave of shared ones, every split against the oracle."""
+    cfg = CONFIGS["extreme"]
+    tol = TOL[cfg.dtype]["out"]
+    inp = make_inputs(cfg)
+    say(f"extreme: dynamic core B={cfg.B} N={cfg.N} m_t={cfg.m_t}, every split")
+    _, _, _, z_tail = upload(inp)
+    g = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b in range(cfg.B):
+        zb = inp.z_tail_f64(b)
+        g_b = host_f64(g[b])
+        for i in range(cfg.n_s):
+            r = split_rows_of(cfg.N, cfg.S, i)
+            o = O.dyn_context_split(zb, cfg.S, cfg.eps, i)
+            err = float((np.linalg.norm(g_b[r] - o, axis=-1) / np.linalg.norm(o, axis=-1)).max())
+            assert err <= tol, f"extreme split {(b, i)}: {err:.3e}"
+            worst = max(worst, err)
+        del zb, g_b
+    say(f"extreme: {cfg.B * cfg.n_s} splits, worst {worst:.2e} (bar {tol})")
+
+
 @pytest.mark.parametrize("norm", ["softmax", "rms"])
 def test_dyn_norm_full_size_every_split(gpu_ok, norm):
     """Softmax and RMS normalisation on the 2 x 32768-token workload (m_t = 1536 at row stride
