@@ -240,9 +240,16 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   // row t >= N is read; with d % 32 != 0 (kTail) the pieces past d load zeros. Lane terms are
   // recomputed per copy (laundered through an empty asm so they are not hoisted into long-lived
   // registers).
-  auto src_off = [&](uint32_t pb, int lim, int r0, int sub, int pc) {
-    const int r = kRow ? min(r0 + sub, lim - 1) : r0 + sub;
-    return pb + (uint32_t)r * rowB + 16u * (uint32_t)pc;
+  auto src_off = [&](bool ok, uint32_t pb, int lim, int r0, int sub, int pc) {
+    uint32_t o;
+    if (kRow) {
+      const int r = max(min(min(r0 + sub, lim - 1), 255), -256);
+      o = pb + (uint32_t)(r * (int)(rowB & 0x3fffffu)) + 16u * (uint32_t)pc;
+    } else {
+      o = pb + (uint32_t)(r0 + sub) * rowB + 16u * (uint32_t)pc;
+    }
+    asm volatile("" : "+v"(o));
+    return ok ? o : OOB;
   };
   auto lane_terms = [&](int& sub, int& pc) {
     sub = lane >> 2;
@@ -263,8 +270,8 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     for (int n = 0; n < 2; ++n) {
       const int r0 = wave * 32 + n * 16;
       const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
-      dma16(xr, st + r0 * RB, ok ? src_off(pbA, limA, r0, sub, pc) : OOB, kb);
-      dma16(xr, st + T * RB + r0 * RB, ok ? src_off(pbB, limB, r0, sub, pc) : OOB, kb);
+      dma16(xr, st + r0 * RB, src_off(ok, pbA, limA, r0, sub, pc), kb);
+      dma16(xr, st + T * RB + r0 * RB, src_off(ok, pbB, limB, r0, sub, pc), kb);
     }
   };
 
@@ -313,12 +320,15 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     s_ssB[o + wn * 64 + wm * 32] = 0.f;
   }
   // One chunk from stage st whose k-step-0 fragments are already in ra0 / rb0; the 4 copies of
-  // chunk kc into dst go between the MFMA groups. With next != nullptr the next chunk's wait
-  // and barrier come before the last MFMA group, and its k-step-0 fragments are read under it.
+  // chunk kc into dst go between the MFMA groups. With a next stage the next chunk's wait and
+  // barrier come before the last MFMA group, and its k-step-0 fragments are read under it; the
+  // unit's last chunk passes nullptr, whose type tells the two apart at compile time (a run-time
+  // test of the stage pointer stays in the loop, the compiler not knowing it non-null).
   // FIRST: the unit's first chunk, whose k-step-0 MFMAs start the accumulators from zero (an
   // inline constant) instead of reading them, so that nothing has to clear them.
   const f32x16 zero16 = {};
-  auto compute_pipe = [&](auto FIRST, const uint8_t* st, int kc, uint8_t* dst, bool valid, const uint8_t* next) {
+  auto compute_pipe = [&](auto FIRST, const uint8_t* st, int kc, uint8_t* dst, bool valid, auto next) {
+    constexpr bool kHasNext = !std::is_same_v<decltype(next), std::nullptr_t>;
     int sub, pc;
     lane_terms(sub, pc);
     const bool ok = live(kc, pc, valid);
@@ -328,8 +338,8 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       // the descriptor is rebuilt from the first lane at each copy: carried across the loop it
       // is taken as per-lane, and every copy through it became a loop over distinct values
       const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
-      if (h == 0) dma16(xr, dst + r0 * RB, ok ? src_off(pbA, limA, r0, sub, pc) : OOB, kb);
-      else dma16(xr, dst + T * RB + r0 * RB, ok ? src_off(pbB, limB, r0, sub, pc) : OOB, kb);
+      if (h == 0) dma16(xr, dst + r0 * RB, src_off(ok, pbA, limA, r0, sub, pc), kb);
+      else dma16(xr, dst + T * RB + r0 * RB, src_off(ok, pbB, limB, r0, sub, pc), kb);
     };
     if (kRow) {   // before the MFMAs, which stay the fragments' last readers
       tA = sumsq8(ra0[0], tA);
@@ -365,7 +375,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
     copy(1, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if (next) {
+    if constexpr (kHasNext) {
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
       WAIT_KEEP(7);
       if (kRow) {
@@ -382,7 +392,9 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
-    if (kRow && next) fetch_hi(ra0, 0, next);
+    if constexpr (kHasNext) {
+      if (kRow) fetch_hi(ra0, 0, next);
+    }
     copy(1, 1);
     __builtin_amdgcn_sched_barrier(0);
   };
