@@ -164,6 +164,12 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   // separate copy routines, chosen at compile time at every call site: a run-time branch
   // between them would join control flow around the copies, after which the compiler drains
   // all copies before the next LDS read.
+  // A copy's offset is computed on every lane and then selected (OOB for the lanes that load
+  // zeros): under a branch around it, every copy split the K loop into another basic block.
+  auto sel_off = [](bool ok, uint32_t o) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(o));
+    return ok ? o : OOB;
+  };
   auto copy1 = [&](int c, uint8_t* st, bool valid, int n) __attribute__((always_inline)) {
     // rows 32 w + 8 n .. + 7 of chunk c, 128 bytes each; lane -> row (ln >> 3), position (ln & 7);
     // 16-byte pieces past m_t (the last chunk when m_t % 64 != 0) load zeros
@@ -172,7 +178,7 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     const int row = wave * 32 + n * 8 + (ln >> 3);
     const uint32_t pc = (uint32_t)((ln & 7) ^ (int)swz<SWZ_ROW>(row));
     const bool ok = valid && c < nk1 && row < valid_rows && 8 * (int)pc < a.m_t - c * KC;
-    dma16(zr, st + (wave * 32 + n * 8) * ROWB, ok ? (uint32_t)((base + row) * a.ld_z * 2) + 16u * pc : OOB,
+    dma16(zr, st + (wave * 32 + n * 8) * ROWB, sel_off(ok, (uint32_t)((base + row) * a.ld_z * 2) + 16u * pc),
           (uint32_t)c * KC * 2u);
   };
   auto copy2 = [&](int c2, uint8_t* st, bool valid, int n) __attribute__((always_inline)) {
@@ -187,7 +193,7 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     const int pc = (pp >> 1) ^ (2 * (t & 3));
     const int f = ft * FR + pc * 16 + (pp & 1) * 8;
     const bool ok = valid && c2 < 2 * nft && q < valid_rows && f < m_loc;
-    dma16(zr2, st + (wave * 16 + n * 4) * ZR, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
+    dma16(zr2, st + (wave * 16 + n * 4) * ZR, sel_off(ok, (uint32_t)(((base + q) * a.ld_z + f) * 2)), 0);
   };
 
   // ---- phase 1
@@ -220,8 +226,11 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     for (int qb = 4 * h; qb < 4 * h + 4; ++qb) ra[qb] = lds_read16(st, o + qb * 32 * ROWB);
   };
   // One chunk of MFMAs from stage st, whose first k-step is in ra / rb; issue(ks) issues the
-  // ks-th copy of a later chunk; next is the following chunk's stage (nullptr: none).
-  auto compute1 = [&](const uint8_t* st, auto&& issue, const uint8_t* next) __attribute__((always_inline)) {
+  // ks-th copy of a later chunk; next is the following chunk's stage, or nullptr for none: its
+  // type decides at compile time (a run-time test of the stage pointer, which the compiler cannot
+  // prove non-null, put a branch into every chunk).
+  auto compute1 = [&](const uint8_t* st, auto&& issue, auto next) __attribute__((always_inline)) {
+    constexpr bool kHasNext = !std::is_same_v<decltype(next), std::nullptr_t>;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       sq = sumsq8(rb, sq);
@@ -229,15 +238,18 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
       for (int qb = 0; qb < 4; ++qb) acc1[qb] = mfma32(as_bf16x8(ra[qb]), as_bf16x8(rb), acc1[qb]);
       if (ks < 3) {
         read1(st, ks + 1, 0);
-      } else if (next) {
+      } else if constexpr (kHasNext) {
         DYN_WAIT_KEEP(7);   // 3 of this chunk's copies and the 4 of the previous one may stay in flight
         read1(next, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int qb = 4; qb < 8; ++qb) acc1[qb] = mfma32(as_bf16x8(ra[qb]), as_bf16x8(rb), acc1[qb]);
-      if (ks < 3) read1(st, ks + 1, 1);
-      else if (next) read1(next, 0, 1);
+      if (ks < 3) {
+        read1(st, ks + 1, 1);
+      } else if constexpr (kHasNext) {
+        read1(next, 0, 1);
+      }
       rb = rbn;
       issue(ks);
       __builtin_amdgcn_sched_barrier(0);
@@ -337,9 +349,10 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   // following chunk's wait and barrier sit between the two MFMA halves of the last k-step, and
   // its first k-step is read there: 4 copies of the chunk after it and the 4 of this chunk may
   // stay in flight, and (after_epi) the 8 stores of the epilogue before this chunk.
-  auto compute2 = [&](const uint8_t* st, auto qh_tag, int cnext, uint8_t* dst, const uint8_t* next,
+  auto compute2 = [&](const uint8_t* st, auto qh_tag, int cnext, uint8_t* dst, auto next,
                       auto after_epi) __attribute__((always_inline)) {
     constexpr int qh = decltype(qh_tag)::value;
+    constexpr bool kHasNext = !std::is_same_v<decltype(next), std::nullptr_t>;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
@@ -350,9 +363,11 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
       if (ks < 7) read2(st, ks + 1);
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) acc2[fb] = mfma32(as_bf16x8(rz[fb]), as_bf16x8(gb), first ? zero16 : acc2[fb]);
-      if (ks == 7 && next) {
-        if constexpr (decltype(after_epi)::value) DYN_WAIT_KEEP(16); else DYN_WAIT_KEEP(8);
-        read2(next, 0);
+      if constexpr (kHasNext) {
+        if (ks == 7) {
+          if constexpr (decltype(after_epi)::value) DYN_WAIT_KEEP(16); else DYN_WAIT_KEEP(8);
+          read2(next, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -198,8 +198,11 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // inline constant) instead of reading them, so that nothing has to clear them.
   // late: the previous unit's 16 epilogue stores were issued after the copies of the chunk that
   // `next` waits for, and may stay in flight as well.
+  // next is nullptr for the unit's last chunk; its type decides at compile time (a run-time test
+  // of the stage pointer, which the compiler cannot prove non-null, put a branch into every chunk).
   auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
-                          const uint8_t* next, bool late) {
+                          auto next, bool late) {
+    constexpr bool kHasNext = !std::is_same_v<decltype(next), std::nullptr_t>;
     const bool ron = has_res && (c == nreg + 2 * wn || c == nreg + 2 * wn + 1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -223,7 +226,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
     copy(kc, dst, valid, 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (next) {
+    if constexpr (kHasNext) {
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
       if (late) WAIT_KEEP(23); else WAIT_KEEP(7);
       fetch(next, 0, ra0, rb0);
