@@ -169,8 +169,9 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     fa[ks] = (uint32_t)ra * RB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(ra)) << 4);
     fb[ks] = (uint32_t)rb * RB + ((((uint32_t)(2 * ks + (lane >> 5))) ^ sw4(rb)) << 4);
   }
-  // Fragment offset of slot s at k-step ks. The rotated offsets are rebuilt at each read (the
-  // base laundered through an empty asm): held, they would take 8 more long-lived registers.
+  // Fragment offset of slot s at k-step ks. kRow rebuilds the rotated target-block offsets at
+  // each read (the base laundered through an empty asm): held, they would take 8 more long-lived
+  // registers and spill. The 4 candidate-block offsets are held.
   auto offA = [&](int ks, int s_) {
     uint32_t o = fa[ks];
     if (kRow) asm volatile("" : "+v"(o));
@@ -178,7 +179,6 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   };
   auto offB = [&](int ks, int u_) {
     uint32_t o = fb[ks];
-    if (kRow) asm volatile("" : "+v"(o));
     return o + (uint32_t)blkB(u_) * 32 * RB;
   };
 
