@@ -36,10 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("9034c277b5184452", "long"): {"fetch_kib": 1182155.0, "fetch_scale": 1.99992,
-                                           "write_kib": 237.1, "write_scale": 1.0},
-            ("9034c277b5184452", "extreme"): {"fetch_kib": 5763103.1, "fetch_scale": 1.99992,
-                                              "write_kib": 1864.4, "write_scale": 1.0},
+            ("ad1d2f9733533f35", "long"): {"fetch_kib": 1182120.1, "fetch_scale": 1.99992,
+                                           "write_kib": 236.7, "write_scale": 1.0},
+            ("ad1d2f9733533f35", "extreme"): {"fetch_kib": 5224593.5, "fetch_scale": 1.99992,
+                                              "write_kib": 1592.6, "write_scale": 1.0},
         },
     },
 }
