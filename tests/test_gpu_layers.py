@@ -274,30 +274,6 @@ def test_dyn_wave_tail_every_split(gpu_ok, name):
     say(f"{name}: {cfg.n_s} splits, worst {w1:.2e} (core), {w2:.2e} (layer)")
 
 
-def test_dyn_extreme_every_split(gpu_ok):
-    """The dynamic core on the 98304-token workload (384 splits of 256, m_t = 1536): a full wave
-    of whole splits and a last wave of shared ones, every split against the oracle."""
-    cfg = CONFIGS["extreme"]
-    tol = TOL[cfg.dtype]["out"]
-    inp = make_inputs(cfg)
-    say(f"extreme: dynamic core B={cfg.B} N={cfg.N} m_t={cfg.m_t}, every split")
-    _, _, _, z_tail = upload(inp)
-    g = A.avey_dyn_context(z_tail, cfg.S, cfg.eps)
-    torch.cuda.synchronize()
-    worst = 0.0
-    for b in range(cfg.B):
-        zb = inp.z_tail_f64(b)
-        g_b = host_f64(g[b])
-        for i in range(cfg.n_s):
-            r = split_rows_of(cfg.N, cfg.S, i)
-            o = O.dyn_context_split(zb, cfg.S, cfg.eps, i)
-            err = float((np.linalg.norm(g_b[r] - o, axis=-1) / np.linalg.norm(o, axis=-1)).max())
-            assert err <= tol, f"extreme split {(b, i)}: {err:.3e}"
-            worst = max(worst, err)
-        del zb, g_b
-    say(f"extreme: {cfg.B * cfg.n_s} splits, worst {worst:.2e} (bar {tol})")
-
-
 @pytest.mark.parametrize("norm", ["softmax", "rms"])
 def test_dyn_norm_full_size_every_split(gpu_ok, norm):
     """Softmax and RMS normalisation on the 2 x 32768-token workload (m_t = 1536 at row stride
