@@ -62,7 +62,9 @@ struct GemmParams {
 template <int P>
 using Pos = std::integral_constant<int, P>;
 
-// kRelu2: the enricher's epilogue (bias, squared ReLU); otherwise the plain product.
+// kRelu2: the enricher (one A tensor, bias and squared ReLU in the epilogue); otherwise the
+// fuser (A in two tensors along K, then the residual). Fixing each one's operands at compile
+// time keeps the unused descriptors and their selects out of the K loop's scalar registers.
 template <bool kRelu2>
 __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
@@ -84,12 +86,13 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   lds_sync();   // the bias table is complete (its loads were waited for before the LDS writes)
 
   const int nreg = a.K / KH;                       // chunks of W x A
-  const int nk = nreg + (a.R ? TT / KH : 0);       // then the residual chunks
+  constexpr bool kRes = !kRelu2;                   // the fuser adds its residual
+  const int nk = nreg + (kRes ? TT / KH : 0);      // then the residual chunks
   const int nk4 = (nk + 3) / 4 * 4;                // padded with zero chunks to a multiple of 4
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.W, (uint32_t)((int64_t)a.K * a.ldw * 2));
   const __amdgpu_buffer_rsrc_t a1r = make_rsrc(a.A1, (uint32_t)(a.M * a.lda1 * 2));
-  const __amdgpu_buffer_rsrc_t a2r = make_rsrc(a.A2, a.A2 ? (uint32_t)(a.M * a.lda2 * 2) : 0u);
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R, a.R ? (uint32_t)(a.M * a.ldr * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t a2r = make_rsrc(kRes ? a.A2 : nullptr, kRes ? (uint32_t)(a.M * a.lda2 * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(kRes ? a.R : nullptr, kRes ? (uint32_t)(a.M * a.ldr * 2) : 0u);
   // the output; each wave's epilogue stores go through it, lanes out of range at OOB
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.C, (uint32_t)(a.M * a.ldc * 2));
 
@@ -109,7 +112,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   auto copy = [&](int kc, uint8_t* st, bool valid, int n) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const bool res = kc >= nreg;
+    const bool res = kRes && kc >= nreg;
     // Offsets are 32-bit (every operand is below 2^31 bytes); a lane out of range gets the high
     // bit, past the descriptor's range, so that no branch is needed.
     if (n < 2) {
@@ -127,7 +130,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
       const uint32_t tok = (uint32_t)c_t0 + (uint32_t)(r0 + (ln >> 2));
       const uint32_t piece = (uint32_t)((ln & 3) ^ (int)sw4(r0 + (ln >> 2)));
       const int k0 = kc * KH;
-      const bool first = k0 < a.k1;
+      const bool first = !kRes || k0 < a.k1;
       const uint32_t ld = first ? (uint32_t)a.lda1 : (uint32_t)a.lda2;
       const int kk = first ? k0 : k0 - a.k1;
       const bool ok = valid & !res & (tok < (uint32_t)a.M);
@@ -189,7 +192,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
         acc[mb][POS.value & 1] = mfma32(as_bf16x8(ra[mb]), as_bf16x8(idB[ks]), acc[mb][POS.value & 1]);
     }
   };
-  const bool has_res = a.R != nullptr;
+  constexpr bool has_res = kRes;
 
   // One chunk c from stage st at pipeline position POS (k-step-0 fragments already in ra0 /
   // rb0); the 4 copies of chunk kc of the copy unit into dst go between the MFMA groups.
