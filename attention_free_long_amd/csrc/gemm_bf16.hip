@@ -109,10 +109,10 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // (zeros in the residual chunks). Everything past M, F or K loads zeros. The source buffer is
   // selected per chunk without a branch (a control-flow join around a copy makes the compiler
   // drain every copy in flight).
-  auto copy = [&](int kc, uint8_t* st, bool valid, int n) {
+  auto copy = [&](int kc, uint8_t* st, bool valid, int n, bool may_res = true) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const bool res = kRes && kc >= nreg;
+    const bool res = kRes && may_res && kc >= nreg;
     // Offsets are 32-bit (every operand is below 2^31 bytes); a lane out of range gets the high
     // bit, past the descriptor's range, so that no branch is needed.
     if (n < 2) {
@@ -203,31 +203,34 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // `next` waits for, and may stay in flight as well.
   // next is nullptr for the unit's last chunk; its type decides at compile time (a run-time test
   // of the stage pointer, which the compiler cannot prove non-null, put a branch into every chunk).
+  // RES (compile time): chunk c, or the chunk kc being copied, may be one of the residual
+  // chunks; off in the main loop's groups that lie before them, so that neither the identity
+  // MFMAs nor the copy's choice of source put a branch into those chunks.
   auto compute_pipe = [&](auto FIRST, auto POS, const uint8_t* st, int c, int kc, uint8_t* dst, bool valid,
-                          auto next, bool late) {
+                          auto next, bool late, auto RES) {
     constexpr bool kHasNext = !std::is_same_v<decltype(next), std::nullptr_t>;
-    const bool ron = has_res && (c == nreg + 2 * wn || c == nreg + 2 * wn + 1);
+    const bool ron = RES.value && has_res && (c == nreg + 2 * wn || c == nreg + 2 * wn + 1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
             mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
     fetch(st, 1, ra1, rb1);
-    copy(kc, dst, valid, 0);
+    copy(kc, dst, valid, 0, RES.value);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] =
             mfma32(as_bf16x8(ra0[mb]), as_bf16x8(rb0[nb]), FIRST.value ? zero16 : acc[mb][nb]);
-    copy(kc, dst, valid, 1);
+    copy(kc, dst, valid, 1, RES.value);
     __builtin_amdgcn_sched_barrier(0);
     res_mfma(POS, ron, ra0, 0);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
-    copy(kc, dst, valid, 2);
+    copy(kc, dst, valid, 2, RES.value);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kHasNext) {
       // 3 of this chunk's copies and the 4 of the previous one may stay in flight
@@ -238,7 +241,7 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
     for (int mb = 2; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(as_bf16x8(ra1[mb]), as_bf16x8(rb1[nb]), acc[mb][nb]);
-    copy(kc, dst, valid, 3);
+    copy(kc, dst, valid, 3, RES.value);
     __builtin_amdgcn_sched_barrier(0);
     res_mfma(POS, ron, ra1, 1);
   };
@@ -274,27 +277,39 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
     if (late) WAIT_KEEP(24); else WAIT_KEEP(8);
     first_unit = false;
     fetch(st0, 0, ra0, rb0);
+    const std::integral_constant<bool, true> kMayRes;
+    const std::integral_constant<bool, false> kNoRes;
     if (nk4 > 4) {
-      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1, late);
-      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2, late);
-      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3, false);
-      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0, false);
-      for (int kc = 4; kc + 4 < nk4; kc += 4) {
-        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, false);
-        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2, false);
-        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3, false);
-        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0, false);
+      compute_pipe(kFirst, Pos<0>{}, st0, 0, 3, st3, 3 < nk, st1, late, kMayRes);
+      compute_pipe(kNext, Pos<1>{}, st1, 1, 4, st0, 4 < nk, st2, late, kMayRes);
+      compute_pipe(kNext, Pos<2>{}, st2, 2, 5, st1, 5 < nk, st3, false, kMayRes);
+      compute_pipe(kNext, Pos<3>{}, st3, 3, 6, st2, 6 < nk, st0, false, kMayRes);
+      int kc = 4;
+      // groups whose chunks and copies (3 chunks ahead) all lie before the residual
+      for (; kc + 4 < nk4 && (!kRes || kc + 6 < nreg); kc += 4) {
+        compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, false, kNoRes);
+        compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2, false, kNoRes);
+        compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3, false, kNoRes);
+        compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0, false, kNoRes);
+      }
+      if constexpr (kRes) {
+        for (; kc + 4 < nk4; kc += 4) {
+          compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, false, kMayRes);
+          compute_pipe(kNext, Pos<1>{}, st1, kc + 1, kc + 4, st0, kc + 4 < nk, st2, false, kMayRes);
+          compute_pipe(kNext, Pos<2>{}, st2, kc + 2, kc + 5, st1, kc + 5 < nk, st3, false, kMayRes);
+          compute_pipe(kNext, Pos<3>{}, st3, kc + 3, kc + 6, st2, kc + 6 < nk, st0, false, kMayRes);
+        }
       }
     }
     {
       // last four chunks; the next unit's first three are copied meanwhile
       const int kc = nk4 - 4;
       const bool late4 = late && nk4 == 4;
-      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, late4);
+      compute_pipe(kNext, Pos<0>{}, st0, kc, kc + 3, st3, kc + 3 < nk, st1, late4, kMayRes);
       if (has_next) set_copy_unit(t + Gx);
-      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2, late4);
-      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3, false);
-      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr, false);
+      compute_pipe(kNext, Pos<1>{}, st1, kc + 1, 0, st0, has_next, st2, late4, kMayRes);
+      compute_pipe(kNext, Pos<2>{}, st2, kc + 2, 1, st1, has_next && 1 < nk, st3, false, kMayRes);
+      compute_pipe(kNext, Pos<3>{}, st3, kc + 3, 2, st2, has_next && 2 < nk, nullptr, false, kMayRes);
     }
 
     // ---- epilogue through stage 3: wave w uses bytes 4096 w .. +4095, a [32 tokens][64
