@@ -99,10 +99,32 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // ---- copy side: the unit whose chunks are being copied
   int64_t c_t0 = 0;
   int c_f0 = 0;
+  // Enricher: each lane's copy offsets for the copy unit, less the chunk's K term, with bit 31
+  // set where the lane is out of range (past F for W, past M for A); the K term rides in the
+  // scalar offset, so that a copy costs no vector arithmetic. Copy n = 0, 1: W row
+  // 4 w + 2 n + (lane >> 5) at the lane's feature; n = 2, 3: A row 32 w + 16 (n - 2) + (lane >> 2).
+  uint32_t c_off[4] = {0u, 0u, 0u, 0u};
   auto set_copy_unit = [&](int64_t tl) {
     const int64_t L = xs + tl;
     c_f0 = (int)(L % a.f_tiles) * TF;
     c_t0 = (L / a.f_tiles) * TT;
+    if constexpr (kRelu2) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int tr = wave * 4 + n * 2 + (lane >> 5);
+        const int p = lane & 31;
+        const int fl = ((p >> 1) ^ (2 * (tr & 3))) * 16 + (p & 1) * 8;
+        c_off[n] = ((uint32_t)tr * (uint32_t)a.ldw + (uint32_t)(c_f0 + fl)) * 2u |
+                   ((uint32_t)!(fl < a.F - c_f0) << 31);
+      }
+#pragma unroll
+      for (int n = 2; n < 4; ++n) {
+        const int r0 = wave * 32 + (n - 2) * 16;
+        const uint32_t tok = (uint32_t)c_t0 + (uint32_t)(r0 + (lane >> 2));
+        const uint32_t piece = (uint32_t)((lane & 3) ^ (int)sw4(r0 + (lane >> 2)));
+        c_off[n] = (tok * (uint32_t)a.lda1 * 2u + 16u * piece) | ((uint32_t)!(tok < (uint32_t)a.M) << 31);
+      }
+    }
   };
   // Copy n of chunk kc into stage st: n = 0, 1 are W rows 4 w + 2 n, + 1 (1 KiB; in the
   // residual chunks the unit's token rows of R), n = 2, 3 are A rows 32 w + 16 (n - 2) .. + 15
@@ -110,6 +132,15 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // selected per chunk without a branch (a control-flow join around a copy makes the compiler
   // drain every copy in flight).
   auto copy = [&](int kc, uint8_t* st, bool valid, int n, bool may_res = true) {
+    if constexpr (kRelu2) {
+      // an invalid chunk takes scalar offset 0, so that bit 31 alone puts it out of range
+      const uint32_t vbit = valid ? 0u : 0x80000000u;
+      if (n < 2)
+        dma16(wr, st + (wave * 4 + n * 2) * XB, c_off[n] | vbit, valid ? (uint32_t)(kc * KH) * (uint32_t)a.ldw * 2u : 0u);
+      else
+        dma16(a1r, st + XS + (wave * 32 + (n - 2) * 16) * PB, c_off[n] | vbit, valid ? (uint32_t)(kc * KH) * 2u : 0u);
+      return;
+    }
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const bool res = kRes && may_res && kc >= nreg;
