@@ -104,26 +104,27 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // scalar offset, so that a copy costs no vector arithmetic. Copy n = 0, 1: W row
   // 4 w + 2 n + (lane >> 5) at the lane's feature; n = 2, 3: A row 32 w + 16 (n - 2) + (lane >> 2).
   uint32_t c_off[4] = {0u, 0u, 0u, 0u};
+  uint32_t c_off2[2] = {0u, 0u};   // fuser: the A rows in its second A tensor
   auto set_copy_unit = [&](int64_t tl) {
     const int64_t L = xs + tl;
     c_f0 = (int)(L % a.f_tiles) * TF;
     c_t0 = (L / a.f_tiles) * TT;
-    if constexpr (kRelu2) {
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int tr = wave * 4 + n * 2 + (lane >> 5);
-        const int p = lane & 31;
-        const int fl = ((p >> 1) ^ (2 * (tr & 3))) * 16 + (p & 1) * 8;
-        c_off[n] = ((uint32_t)tr * (uint32_t)a.ldw + (uint32_t)(c_f0 + fl)) * 2u |
-                   ((uint32_t)!(fl < a.F - c_f0) << 31);
-      }
+    for (int n = 0; n < 2; ++n) {
+      const int tr = wave * 4 + n * 2 + (lane >> 5);
+      const int p = lane & 31;
+      const int fl = ((p >> 1) ^ (2 * (tr & 3))) * 16 + (p & 1) * 8;
+      c_off[n] = ((uint32_t)tr * (uint32_t)a.ldw + (uint32_t)(c_f0 + fl)) * 2u |
+                 ((uint32_t)!(fl < a.F - c_f0) << 31);
+    }
 #pragma unroll
-      for (int n = 2; n < 4; ++n) {
-        const int r0 = wave * 32 + (n - 2) * 16;
-        const uint32_t tok = (uint32_t)c_t0 + (uint32_t)(r0 + (lane >> 2));
-        const uint32_t piece = (uint32_t)((lane & 3) ^ (int)sw4(r0 + (lane >> 2)));
-        c_off[n] = (tok * (uint32_t)a.lda1 * 2u + 16u * piece) | ((uint32_t)!(tok < (uint32_t)a.M) << 31);
-      }
+    for (int n = 2; n < 4; ++n) {
+      const int r0 = wave * 32 + (n - 2) * 16;
+      const uint32_t tok = (uint32_t)c_t0 + (uint32_t)(r0 + (lane >> 2));
+      const uint32_t piece = (uint32_t)((lane & 3) ^ (int)sw4(r0 + (lane >> 2)));
+      const uint32_t oob = (uint32_t)!(tok < (uint32_t)a.M) << 31;
+      c_off[n] = (tok * (uint32_t)a.lda1 * 2u + 16u * piece) | oob;
+      if constexpr (!kRelu2) c_off2[n - 2] = (tok * (uint32_t)a.lda2 * 2u + 16u * piece) | oob;
     }
   };
   // Copy n of chunk kc into stage st: n = 0, 1 are W rows 4 w + 2 n, + 1 (1 KiB; in the
@@ -132,13 +133,28 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // selected per chunk without a branch (a control-flow join around a copy makes the compiler
   // drain every copy in flight).
   auto copy = [&](int kc, uint8_t* st, bool valid, int n, bool may_res = true) {
-    if constexpr (kRelu2) {
-      // an invalid chunk takes scalar offset 0, so that bit 31 alone puts it out of range
-      const uint32_t vbit = valid ? 0u : 0x80000000u;
-      if (n < 2)
-        dma16(wr, st + (wave * 4 + n * 2) * XB, c_off[n] | vbit, valid ? (uint32_t)(kc * KH) * (uint32_t)a.ldw * 2u : 0u);
-      else
-        dma16(a1r, st + XS + (wave * 32 + (n - 2) * 16) * PB, c_off[n] | vbit, valid ? (uint32_t)(kc * KH) * 2u : 0u);
+    // Held offsets: an invalid chunk takes scalar offset 0, so that bit 31 alone puts it out of
+    // range. W copies that may be residual ones (the unit's rows of R; may_res is a constant at
+    // every call) take the general path below, whose choice of source is a select: a branch
+    // around a copy makes the compiler drain every copy in flight.
+    const bool res_chunk = kRes && may_res && kc >= nreg;
+    if (n < 2 && !(kRes && may_res)) {
+      dma16(wr, st + (wave * 4 + n * 2) * XB, c_off[n] | (valid ? 0u : 0x80000000u),
+            valid ? (uint32_t)(kc * KH) * (uint32_t)a.ldw * 2u : 0u);
+      return;
+    }
+    if (n >= 2) {
+      const int k0 = kc * KH;
+      const bool first = !kRes || k0 < a.k1;
+      const bool live = valid && !res_chunk;   // the residual chunks' A rows load zeros
+      uint32_t vo = c_off[n];
+      if constexpr (kRes) {
+        uint32_t v2 = c_off2[n - 2];
+        asm volatile("" : "+v"(v2));   // a select, not a branch on the uniform `first`
+        vo = first ? vo : v2;
+      }
+      dma16(first ? a1r : a2r, st + XS + (wave * 32 + (n - 2) * 16) * PB, vo | (live ? 0u : 0x80000000u),
+            live ? (uint32_t)(first ? k0 : k0 - a.k1) * 2u : 0u);
       return;
     }
     int ln = lane;
@@ -207,20 +223,23 @@ __global__ void __launch_bounds__(512, 1) gemm_unit_kernel(GemmParams a) {
   // (l & 31) - 16 ks - 8 (l >> 5) when that lies in 0..7. Token block nb of this wave sits in
   // chunk nreg + 2 wn + nb; nreg is even (K % 64 == 0), so that chunk is at an odd pipeline
   // position exactly when nb = 1.
-  uint4 idB[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int j = (lane & 31) - 16 * ks - 8 * (lane >> 5);
+  // The fragment is built where it is used (from a laundered lane index), so that it does not
+  // hold 8 registers across the main loop.
+  auto id_frag = [&](int ks) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int j = (ln & 31) - 16 * ks - 8 * (ln >> 5);
     uint32_t wv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wv[q] = (j >> 1) == q ? ((j & 1) ? 0x3F800000u : 0x00003F80u) : 0u;
-    idB[ks] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
+    return make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  };
   auto res_mfma = [&](auto POS, bool on, const uint4 (&ra)[4], int ks) {
     if (on) {
+      const uint4 id = id_frag(ks);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        acc[mb][POS.value & 1] = mfma32(as_bf16x8(ra[mb]), as_bf16x8(idB[ks]), acc[mb][POS.value & 1]);
+        acc[mb][POS.value & 1] = mfma32(as_bf16x8(ra[mb]), as_bf16x8(id), acc[mb][POS.value & 1]);
     }
   };
   constexpr bool has_res = kRes;
