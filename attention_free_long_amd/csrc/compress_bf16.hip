@@ -433,12 +433,31 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   // lane r: first token of block r of the copy unit, and its first column of P (the launcher
   // ensures k + 1 <= 64)
   int vtok = 0, vcol = 0;
+  // Each lane's copy offsets for the copy unit, less the chunk's terms (which go in the copies'
+  // scalar offsets), with bit 31 set where the lane is out of range whatever the chunk: X row
+  // 4 w + 2 n + (lane >> 5) at the lane's feature (n = 0, 1), P row 32 w + 16 (n - 2) +
+  // (lane >> 2) (n = 2, 3). A copy then costs at most a compare and a select.
+  uint32_t c_off[4] = {0u, 0u, 0u, 0u};
   auto set_copy_unit = [&](const UnitPos& u, int bf) {
     xr = make_rsrc(a.x + u.b * a.N * a.ld_x, (uint32_t)(a.N * a.ld_x * 2));
     c_su = u.su;
     c_fb = u.f_base;
     vtok = lane <= a.k ? s_tok0[bf][lane] : 0;
     vcol = lane <= a.k ? s_col0[bf][lane] : 0;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int tr = wave * 4 + n * 2 + (lane >> 5);
+      const int p = lane & 31;
+      const int fl = ((p >> 1) ^ (2 * (tr & 3))) * 16 + (p & 1) * 8;
+      c_off[n] = ((uint32_t)tr * (uint32_t)a.ld_x + (uint32_t)(c_fb + fl)) * 2u | ((uint32_t)!(fl < a.d - c_fb) << 31);
+    }
+#pragma unroll
+    for (int n = 2; n < 4; ++n) {
+      const int row = wave * 32 + (n - 2) * 16 + (lane >> 2);
+      const int s = c_su * TU + row;
+      const uint32_t piece = (uint32_t)((lane & 3) ^ (int)sw4(row));
+      c_off[n] = ((uint32_t)s * (uint32_t)KP * 2u + 16u * piece) | ((uint32_t)!(s < a.S) << 31);
+    }
   };
   // Chunk c covers block (c / cpb + 1) mod (k + 1): blocks 1..k, then block 0.
   auto chunk_block = [&](int c, int& r, int& j) {
@@ -459,26 +478,23 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   // d and rows past S load zeros:
   // their offset gets the high bit, past the descriptor's range (a sequence and P are < 2^31
   // bytes), so that the offsets are plain 32-bit arithmetic without a branch.
+  // The chunk's terms go in the scalar offset, zero for a chunk out of range, so that bit 31 of a
+  // lane's offset alone keeps it out of range (the sums stay below 2^32: every offset inside a
+  // sequence or P is below 2^31).
   auto copy = [&](uint8_t* st, bool valid, int n, int3 src) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
     if (n < 2) {
-      const int tr = wave * 4 + n * 2 + (ln >> 5);
-      const int p = ln & 31;
-      const int c = (p >> 1) ^ (2 * (tr & 3));
-      const int fl = c * 16 + (p & 1) * 8;                 // feature within the tile
-      const uint32_t tok = (uint32_t)(src.x + tr);         // an empty block's tokens wrap above N
-      const bool ok = valid & (tok < (uint32_t)a.N) & (tr < src.z) & (fl < a.d - c_fb);
-      const uint32_t off = (tok * (uint32_t)a.ld_x + (uint32_t)(c_fb + fl)) * 2u;
-      dma16(xr, st + (wave * 4 + n * 2) * XB, off | ((uint32_t)!ok << 31), 0);
+      // X rows src.x + 4 w + 2 n + (lane >> 5): in range while below N and below the block's
+      // src.z rows; an empty block's first token is negative and takes the whole chunk out
+      const int n_tok = (int)a.N;   // below 2^30 (host checks): 32-bit compares stay scalar
+      const bool cok = valid && src.x >= 0 && src.x < n_tok;
+      const int bound = cok ? min(src.z, n_tok - src.x) - (wave * 4 + n * 2) : 0;
+      int lh = lane >> 5;
+      asm volatile("" : "+v"(lh));
+      const uint32_t vo = lh < bound ? c_off[n] : OOB;
+      dma16(xr, st + (wave * 4 + n * 2) * XB, vo, cok ? (uint32_t)src.x * (uint32_t)a.ld_x * 2u : 0u);
     } else {
       const int r0 = wave * 32 + (n - 2) * 16;
-      const int row = r0 + (ln >> 2);
-      const int s = c_su * TU + row;
-      const uint32_t piece = (uint32_t)((ln & 3) ^ (int)sw4(row));
-      const bool ok = valid & (s < a.S);
-      dma16(pr, st + XS + r0 * PB, ((uint32_t)s * (uint32_t)KP * 2u + 16u * piece) | ((uint32_t)!ok << 31),
-            (uint32_t)src.y * 2u);
+      dma16(pr, st + XS + r0 * PB, c_off[n] | (valid ? 0u : OOB), valid ? (uint32_t)src.y * 2u : 0u);
     }
   };
   auto dma = [&](int kc, uint8_t* st, bool valid) {
@@ -538,24 +554,27 @@ __global__ void __launch_bounds__(512, 1) compress_unit_kernel(CompressParams a)
   // (l & 31) - 16 ks - 8 (l >> 5) when that lies in 0..7. Token block nb of this wave sits in
   // chunk k cpb + 8 su + 2 wn + nb; block 0 starts on an even chunk (cpb is even), so that chunk
   // is at an odd pipeline position exactly when nb = 1.
-  uint4 idB[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int j = (lane & 31) - 16 * ks - 8 * (lane >> 5);
+  // The fragment is built where it is used (from a laundered lane index), so that it does not
+  // hold 8 registers across the K loop.
+  auto id_frag = [&](int ks) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int j = (ln & 31) - 16 * ks - 8 * (ln >> 5);
     uint32_t wv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wv[q] = (j >> 1) == q ? ((j & 1) ? 0x3F800000u : 0x00003F80u) : 0u;
-    idB[ks] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
+    return make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  };
   auto res_chunk = [&](int nb) {
     const int jt = cur_su * 8 + 2 * wn + nb;
     return jt < cpb ? a.k * cpb + jt : -1;
   };
   auto res_mfma = [&](auto POS, bool on, const uint4 (&ra)[4], int ks) {
     if (on) {
+      const uint4 id = id_frag(ks);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        acc[mb][POS.value & 1] = mfma32(as_bf16x8(ra[mb]), as_bf16x8(idB[ks]), acc[mb][POS.value & 1]);
+        acc[mb][POS.value & 1] = mfma32(as_bf16x8(ra[mb]), as_bf16x8(id), acc[mb][POS.value & 1]);
     }
   };
 
