@@ -219,9 +219,9 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
   uint32_t pbA = 0, pbB = 0;
   const uint32_t rowB = kRow ? (uint32_t)(a.ld * 2) : (uint32_t)RB;
   const uint32_t chunkB = kRow ? (uint32_t)RB : (uint32_t)a.S * RB;
-  // kRow with d % 32 == 0: each lane's copy offsets of the copy unit (row clamped to the block's
-  // last valid row, piece, block base), held, so that a copy costs one select; with kTail a
-  // lane's pieces past d also depend on the chunk, and the offsets are built per copy.
+  // Each lane's copy offsets of the copy unit (block base, row, piece; kRow: the row clamped to
+  // the block's last valid row), held, so that a copy costs one select; with kTail a lane's
+  // pieces past d also depend on the chunk, and the offsets are built per copy.
   uint32_t hoA[2] = {0u, 0u}, hoB[2] = {0u, 0u};
   auto set_unit = [&](const Unit& u) {
     const int64_t seq = kRow ? a.N * a.ld : (int64_t)a.n_s * a.nk * a.S * KH;
@@ -243,6 +243,13 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     } else {
       pbA = (uint32_t)((int64_t)u.i * a.nk * a.S * RB + u.ua * T * RB);
       pbB = (uint32_t)((int64_t)u.j * a.nk * a.S * RB + u.ub * T * RB);
+      const int sub = lane >> 2, pc = (lane & 3) ^ ((sub >> 2) & 3);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const uint32_t lo = (uint32_t)(wave * 32 + n * 16 + sub) * RB + 16u * (uint32_t)pc;
+        hoA[n] = pbA + lo;
+        hoB[n] = pbB + lo;
+      }
     }
   };
   // Lane l of a copy lands at LDS row r0 + (l >> 2), position l & 3, so it fetches the logical
@@ -282,7 +289,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
     for (int n = 0; n < 2; ++n) {
       const int r0 = wave * 32 + n * 16;
       const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
-      if (kRow && !kTail) {
+      if (!kTail) {
         dma16(xr, st + r0 * RB, ok ? hoA[n] : OOB, kb);
         dma16(xr, st + T * RB + r0 * RB, ok ? hoB[n] : OOB, kb);
       } else {
@@ -355,7 +362,7 @@ __global__ void __launch_bounds__(512, 1) maxsim_bf16_kernel(MaxsimParams a) {
       // the descriptor is rebuilt from the first lane at each copy: carried across the loop it
       // is taken as per-lane, and every copy through it became a loop over distinct values
       const __amdgpu_buffer_rsrc_t xr = make_rsrc_uniform(xbase, xbytes);
-      if (kRow && !kTail) {
+      if (!kTail) {
         uint32_t o = h == 0 ? hoA[ks] : hoB[ks];
         asm volatile("" : "+v"(o));   // a select, not a branch
         if (h == 0) dma16(xr, dst + r0 * RB, ok ? o : OOB, kb);
