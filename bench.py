@@ -36,10 +36,10 @@ TRAFFIC = {
     "maxsim": {
         "sources": ("maxsim_bf16.hip", "avey_common.h", "../build.py"),
         "measured": {
-            ("ad1d2f9733533f35", "long"): {"fetch_kib": 1182120.1, "fetch_scale": 1.99992,
-                                           "write_kib": 236.7, "write_scale": 1.0},
-            ("ad1d2f9733533f35", "extreme"): {"fetch_kib": 5224593.5, "fetch_scale": 1.99992,
-                                              "write_kib": 1592.6, "write_scale": 1.0},
+            ("4c61ddd2265b4d10", "long"): {"fetch_kib": 1188920.5, "fetch_scale": 1.99992,
+                                           "write_kib": 236.8, "write_scale": 1.0},
+            ("4c61ddd2265b4d10", "extreme"): {"fetch_kib": 5086366.6, "fetch_scale": 1.99992,
+                                              "write_kib": 1142.5, "write_scale": 1.0},
         },
     },
 }
