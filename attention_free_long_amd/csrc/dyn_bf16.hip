@@ -120,6 +120,13 @@ __device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* base, uint32_t off)
 
 #define DYN_WAIT_KEEP(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+// A copy's offset is computed on every lane and then selected (OOB for the lanes that load
+// zeros): under a branch around it, every copy split the K loop into another basic block.
+__device__ __forceinline__ uint32_t sel_off(bool ok, uint32_t o) {
+  asm volatile("" : "+v"(o));
+  return ok ? o : OOB;
+}
+
 template <bool kRelu>
 __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
@@ -164,12 +171,6 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
   // separate copy routines, chosen at compile time at every call site: a run-time branch
   // between them would join control flow around the copies, after which the compiler drains
   // all copies before the next LDS read.
-  // A copy's offset is computed on every lane and then selected (OOB for the lanes that load
-  // zeros): under a branch around it, every copy split the K loop into another basic block.
-  auto sel_off = [](bool ok, uint32_t o) __attribute__((always_inline)) {
-    asm volatile("" : "+v"(o));
-    return ok ? o : OOB;
-  };
   auto copy1 = [&](int c, uint8_t* st, bool valid, int n) __attribute__((always_inline)) {
     // rows 32 w + 8 n .. + 7 of chunk c, 128 bytes each; lane -> row (ln >> 3), position (ln & 7);
     // 16-byte pieces past m_t (the last chunk when m_t % 64 != 0) load zeros
@@ -618,8 +619,8 @@ __global__ void __launch_bounds__(256, 1) dyn512_kernel(DynParams a) {
     const int pp = ln & 31;
     const int pc = (pp >> 1) ^ (2 * (t & 3));
     const int f = ft * FT + pc * 16 + (pp & 1) * 8;
-    const bool ok = c2 < total && q < nvalid && f < a.m_t;
-    dma16(zr, st + (wave * 16 + n * 2) * ZB, ok ? (uint32_t)(((base + q) * a.ld_z + f) * 2) : OOB, 0);
+    const bool ok = (c2 < total) & (q < nvalid) & (f < a.m_t);   // no short-circuit: no branch
+    dma16(zr, st + (wave * 16 + n * 2) * ZB, sel_off(ok, (uint32_t)(((base + q) * a.ld_z + f) * 2)), 0);
   };
   uint32_t offZ2[8];
   {
