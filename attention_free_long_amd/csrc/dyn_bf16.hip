@@ -187,7 +187,11 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
     // t holds the row's 32-byte piece s ^ 2 (t & 3)
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int ft = c2 >> 1, qh = c2 & 1;
+    // Phase 2 walks the workgroup's feature tiles from the last one down: phase 1 read the
+    // split's last features most recently, so the first tiles' copies can still meet them in
+    // the L2. Logical tile c2 >> 1 is feature tile nft - 1 - (c2 >> 1) (the epilogue maps it the
+    // same way).
+    const int ft = nft - 1 - (c2 >> 1), qh = c2 & 1;
     const int t = wave * 16 + n * 4 + (ln >> 4);
     const int q = qh * 128 + t;
     const int pp = ln & 15;
@@ -413,7 +417,7 @@ __global__ void __launch_bounds__(512, 1) dyn_ring_kernel(DynParams a) {
           *reinterpret_cast<uint2*>(sst + (wofs ^ ((uint32_t)(4 * fh + g) << 4))) = make_uint2(lo, hi);
         }
       }
-      const int f = ft * FR + rr * 64 + (lane & 7) * 8;
+      const int f = (nft - 1 - ft) * FR + rr * 64 + (lane & 7) * 8;
       const bool fok = f < m_loc;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
